@@ -1,0 +1,428 @@
+"""Pins for the CPU oracle: closed forms, special cases that reduce to library
+routines, exhaustive format tables and brute force on tiny inputs.
+
+Each test names the property of the pages (or of the mathematics) it fixes.
+None of them re-types an oracle formula: each computes the expected value
+another way.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import csa_synth as syn
+from oracle import csa_oracle as O
+
+
+# ---------------------------------------------------------------- compression
+
+@pytest.mark.parametrize("seed", range(5))
+def test_csa_one_hot_gates_select_tokens(seed):
+    """One-hot gates reduce the gated merge to picking a single token, exactly."""
+    g = np.random.default_rng(seed)
+    T, d, m = 32, 8, 4
+    c_a, c_b = g.standard_normal((T, d)), g.standard_normal((T, d))
+    z_a = np.full((T, d), -1e4)
+    z_b = np.full((T, d), -1e4)
+    N = T // m
+    expect = np.zeros((N, d))
+    for j in range(N):
+        for c in range(d):
+            # candidates: A tokens m*j..m*j+m-1, B tokens m*j-m..m*j-1 (j>0)
+            cands = [("a", t) for t in range(m * j, m * j + m)]
+            if j > 0:
+                cands += [("b", t) for t in range(m * j - m, m * j)]
+            src, t = cands[g.integers(len(cands))]
+            (z_a if src == "a" else z_b)[t, c] = 0.0
+            expect[j, c] = (c_a if src == "a" else c_b)[t, c]
+    got = O.csa_compress(c_a, c_b, z_a, z_b, m)
+    assert np.array_equal(got, expect)
+
+
+def test_csa_joint_softmax_and_overlap_closed_form():
+    """Constant gates per stream: A logits 0, B logits log 3 -> joint-softmax weights
+    1/16 (A) and 3/16 (B) for j > 0, and 1/4 (A only) for j = 0."""
+    g = np.random.default_rng(7)
+    T, d = 40, 5
+    c_a, c_b = g.standard_normal((T, d)), g.standard_normal((T, d))
+    z_a = np.zeros((T, d))
+    z_b = np.full((T, d), np.log(3.0))
+    got = O.csa_compress(c_a, c_b, z_a, z_b, 4)
+    blocks_a = c_a.reshape(T // 4, 4, d).sum(axis=1)
+    blocks_b = c_b.reshape(T // 4, 4, d).sum(axis=1)
+    expect = np.empty_like(got)
+    expect[0] = blocks_a[0] / 4.0
+    expect[1:] = (blocks_a[1:] + 3.0 * blocks_b[:-1]) / 16.0
+    np.testing.assert_allclose(got, expect, rtol=1e-13, atol=1e-14)
+
+
+def test_csa_trailing_partial_block_dropped():
+    T, d = 4 * 5 + 3, 4
+    x = np.ones((T, d))
+    assert O.csa_compress(x, x, x, x, 4).shape == (5, d)
+    assert O.hca_compress(np.ones((128 * 3 + 127, d)), np.zeros((128 * 3 + 127, d))).shape == (3, d)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_gate_weights_sum_to_one(seed):
+    """C = 1 gives E = 1 for any gate logits (softmax weights sum to 1)."""
+    g = np.random.default_rng(seed)
+    T, d = 64, 16
+    ones = np.ones((T, d))
+    z1, z2 = 3 * g.standard_normal((T, d)), 3 * g.standard_normal((T, d))
+    np.testing.assert_allclose(O.csa_compress(ones, ones, z1, z2, 4), 1.0, rtol=0, atol=4e-15)
+    np.testing.assert_allclose(O.hca_compress(np.ones((256, d)), 3 * g.standard_normal((256, d)), 128),
+                               1.0, rtol=0, atol=4e-15)
+
+
+def test_hca_one_hot_and_ratio_one_identity():
+    g = np.random.default_rng(3)
+    T, d, m = 512, 8, 128
+    c = g.standard_normal((T, d))
+    z = np.full((T, d), -1e4)
+    pick = g.integers(0, m, size=(T // m, d))
+    for j in range(T // m):
+        for ch in range(d):
+            z[m * j + pick[j, ch], ch] = 0.0
+    expect = np.array([[c[m * j + pick[j, ch], ch] for ch in range(d)] for j in range(T // m)])
+    assert np.array_equal(O.hca_compress(c, z, m), expect)
+    assert np.array_equal(O.hca_compress(c, g.standard_normal((T, d)), 1), c)
+
+
+def test_hca_uniform_gates_mean():
+    g = np.random.default_rng(4)
+    c = g.standard_normal((384, 6))
+    np.testing.assert_allclose(O.hca_compress(c, np.zeros_like(c), 128),
+                               c.reshape(3, 128, 6).mean(axis=1), rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- number formats
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.e4m3_decode(codes)
+    finite = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[finite], ref[finite])
+    assert O.e4m3_decode(0x7E) == 448.0 and O.e4m3_decode(0x01) == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_rne():
+    g = np.random.default_rng(11)
+    v = np.concatenate([
+        g.uniform(-448, 448, 200000), g.uniform(-1, 1, 100000) * 2.0 ** -5,
+        g.standard_normal(100000) * 30,
+    ]).astype(np.float32)
+    # all exact midpoints between adjacent finite codes (ties to even)
+    vals = O.e4m3_decode(np.arange(0, 0x7F))
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids, vals.astype(np.float32)])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_encode(v)
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_saturates_and_roundtrips():
+    assert O.e4m3_encode(np.float32(1e6)) == 0x7E
+    assert O.e4m3_encode(np.float32(-460.0)) == 0xFE
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(O.e4m3_encode(O.e4m3_decode(codes).astype(np.float32)), codes)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fp8_rows_scale_and_error_bound(seed):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((64, 128)) * g.uniform(0.01, 100, (64, 1))).astype(np.float32)
+    x[3] = 0.0
+    codes, scale = O.quant_fp8_rows(x)
+    assert scale[3] == 1.0 and np.all(codes[3] == 0)
+    amax = np.abs(x).max(axis=1)
+    rows = [r for r in range(64) if r != 3]
+    assert np.array_equal(scale[rows], (amax[rows] / np.float32(448)).astype(np.float32))
+    # the row maximum lands on +-448
+    am = np.abs(x).argmax(axis=1)
+    assert all((codes[r, am[r]] & 0x7F) == 0x7E for r in rows)
+    deq = O.dequant_fp8_rows(codes, scale)
+    # relative error of a normal e4m3 value is at most 2^-4; subnormals: half a step of 2^-9
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None])
+    assert np.all(err <= bound * (1 + 1e-6))
+
+
+def _e2m1_brute(v):
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    out = []
+    for x in np.asarray(v, dtype=np.float64):
+        a = min(abs(x), 6.0)
+        dist = np.abs(grid - a)
+        best = np.flatnonzero(dist == dist.min())
+        mag = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        out.append(mag | (8 if np.signbit(x) else 0))
+    return np.array(out, dtype=np.uint8)
+
+
+def test_e2m1_encode_brute_force():
+    v = np.concatenate([np.arange(-80, 81) / 8.0, np.arange(-600, 601) / 97.0, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.0]])
+    v = v.astype(np.float32)
+    assert np.array_equal(O.e2m1_encode(v), _e2m1_brute(v))
+    assert list(O.e2m1_decode(np.arange(8))) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_mxfp4_scales_and_bound(seed):
+    g = np.random.default_rng(seed)
+    x = (g.standard_normal((16, 128)) * g.uniform(1e-3, 1e3, (16, 1))).astype(np.float32)
+    x[2, 32:64] = 0.0
+    packed, sc = O.quant_mxfp4_rows(x)
+    assert packed.shape == (16, 64) and sc.shape == (16, 4)
+    blocks = np.abs(x).reshape(16, 4, 32).max(axis=-1)
+    E = sc.astype(np.int64) - 127
+    nz = blocks > 0
+    # amax / 2^E lies in [4, 8): the block maximum uses the top binade of e2m1
+    r = blocks[nz] / np.exp2(E[nz])
+    assert np.all((r >= 4) & (r < 8))
+    assert E[2, 1] == 0
+    deq = O.dequant_mxfp4_rows(packed, sc)
+    # error bound: half a step of the binade (step 2^(E-1) at the top, 2^(E)... ) or saturation at 6*2^E
+    step = np.repeat(np.exp2(E), 32, axis=1)
+    err = np.abs(deq - x)
+    assert np.all(err <= np.maximum(0.25 * step * np.maximum(np.abs(x) / step, 1.0), 2.0 * step) + 1e-30)
+    # pack order: element 2i in the low nibble
+    lo = O.e2m1_decode(packed[0, 0] & 0xF) * np.exp2(E[0, 0])
+    assert lo == deq[0, 0]
+
+
+def test_fp4_to_fp8_dequant_is_lossless():
+    """FP4 -> FP8 dequantisation is lossless [cf-1 §4.4]: every e2m1 value times a
+    power-of-two scale in e4m3's range is exactly an e4m3 value."""
+    for code in range(16):
+        v = O.e2m1_decode(code)
+        for e in range(-8, 7):
+            x = np.float32(v * 2.0 ** e)
+            assert O.e4m3_decode(O.e4m3_encode(x)) == x
+
+
+# ---------------------------------------------------------------- indexer
+
+def test_visibility_brute_force():
+    for ratio in (1, 4, 128):
+        N = 50
+        for p in range(0, 60 * ratio, max(1, ratio // 3)):
+            brute = sum(1 for j in range(N) if ratio * j + ratio - 1 <= p)
+            assert O.visible_entries(p, ratio, N) == brute
+
+
+def test_indexer_single_head_is_relu_dot():
+    g = np.random.default_rng(5)
+    q = g.standard_normal((6, 1, 16))
+    k = g.standard_normal((10, 16))
+    s = O.indexer_scores(q, np.ones((6, 1)), k, np.arange(100, 106) * 0 + 39, 4)
+    for t in range(6):
+        for j in range(10):
+            assert s[t, j] == pytest.approx(max(0.0, float(np.dot(q[t, 0], k[j]))), rel=1e-14, abs=1e-14)
+
+
+def test_indexer_linear_in_weights_and_causal_mask():
+    g = np.random.default_rng(6)
+    q = g.standard_normal((8, 4, 16))
+    k = g.standard_normal((12, 16))
+    pos = np.array([0, 2, 3, 7, 11, 30, 47, 100])
+    w1, w2 = g.uniform(size=(8, 4)), g.uniform(size=(8, 4))
+    s1 = O.indexer_scores(q, w1, k, pos, 4)
+    s2 = O.indexer_scores(q, w2, k, pos, 4)
+    s12 = O.indexer_scores(q, w1 + w2, k, pos, 4)
+    vis = np.isfinite(s12)
+    np.testing.assert_allclose(s12[vis], (s1 + s2)[vis], rtol=1e-13)
+    for t, p in enumerate(pos):
+        n = min(12, (p + 1) // 4)
+        assert vis[t].sum() == n and vis[t, :n].all()
+    # negative weight with a one-hot head picks -ReLU
+    w = np.zeros((8, 4)); w[:, 2] = -1.0
+    s = O.indexer_scores(q, w, k, pos, 4)
+    t = 7
+    np.testing.assert_allclose(s[t], -np.maximum(q[t, 2] @ k.T, 0), rtol=1e-14)
+
+
+def test_indexer_exact_grid_is_order_independent():
+    """Integer queries/keys in [-4,4] and weights on {0,1/8,..,1}: float32 scores in
+    any summation order equal the float64 scores exactly."""
+    d = syn.csa_decode(99, B=1, N=512, H=8, H_I=64, d_I=128, key_grid="int")
+    s64 = O.indexer_scores(d["q_i"][0][None], d["w"][0][None], d["k_i"][0], [4 * 512], 4)[0]
+    q32 = d["q_i"][0].astype(np.float32)
+    k32 = d["k_i"][0].astype(np.float32)
+    logits = (k32[:, ::-1] @ q32[:, ::-1].T).astype(np.float32)   # reversed d order
+    s32 = (np.maximum(logits, 0) * d["w"][0][None, :]).astype(np.float32)[:, ::-1].sum(axis=1, dtype=np.float32)
+    assert np.array_equal(s32.astype(np.float64), s64)
+
+
+def _topk_brute(s, n, k):
+    """Repeated arg-max: pick the largest remaining score, lowest index on ties."""
+    s = list(s[:n])
+    chosen = []
+    for _ in range(min(k, n)):
+        best = None
+        for j in range(n):
+            if j in chosen:
+                continue
+            if best is None or s[j] > s[best]:
+                best = j
+        chosen.append(best)
+    return sorted(chosen)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_topk_brute_force_with_ties(seed):
+    g = np.random.default_rng(seed)
+    n_rows, N, k = 6, 40, 7
+    scores = g.integers(-3, 4, size=(n_rows, N)).astype(np.float64)   # many ties
+    scores[0, ::2] = -0.0
+    scores[0, 1::2] = 0.0
+    n_vis = np.array([0, 3, 7, 8, 25, 40])
+    got = O.topk_select(scores, n_vis, k)
+    for t in range(n_rows):
+        want = _topk_brute(scores[t], n_vis[t], k)
+        assert list(got[t, :len(want)]) == want
+        assert np.all(got[t, len(want):] == -1)
+
+
+def test_topk_signed_zero_is_a_tie():
+    s = np.array([[0.0, -0.0, -0.0, 0.0]])
+    assert list(O.topk_select(s, [4], 2)[0]) == [0, 1]
+    s = np.array([[-0.0, 0.0, -1.0, 0.0]])
+    assert list(O.topk_select(s, [4], 2)[0]) == [0, 1]
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_ones_values_closed_form():
+    """V = 1 gives o = 1 - e^sink / (e^sink + sum e^l); with sink -> -inf, o = 1."""
+    g = np.random.default_rng(8)
+    H, d, n = 4, 16, 9
+    q = g.standard_normal((H, d))
+    keys = np.ones((n, d))
+    sink = g.standard_normal(H)
+    o, lse = O.attend(q, keys, sink)
+    l = q @ keys.T
+    expect = 1 - np.exp(sink) / (np.exp(sink) + np.exp(l).sum(axis=1))
+    np.testing.assert_allclose(o, np.repeat(expect[:, None], d, axis=1), rtol=1e-13)
+    np.testing.assert_allclose(lse, logsumexp(np.concatenate([sink[:, None], l], axis=1), axis=1), rtol=1e-14)
+    o2, _ = O.attend(q, keys, np.full(H, -np.inf))
+    np.testing.assert_allclose(o2, 1.0, rtol=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_ratio_one_full_selection_is_causal_attention_with_sink(seed):
+    """Ratio 1 with full selection and no window is causal softmax attention with a
+    sink; checked against torch's SDPA (float64, CPU) with the sink as an extra
+    zero-valued key carrying the per-head logit as an additive bias."""
+    g = np.random.default_rng(seed)
+    T, H, d = 24, 4, 16
+    q = g.standard_normal((T, H, d)) / 4
+    x = g.standard_normal((T, d))
+    sink = g.standard_normal(H)
+    kv = O.hca_compress(x, g.standard_normal((T, d)), 1)
+    idx = np.tile(np.arange(T), (T, 1))
+    idx = np.where(idx <= np.arange(T)[:, None], idx, -1)
+    o, lse = O.sparse_attn(q, kv, idx, x, 0, sink, np.arange(T), window=0)
+    o_d, _ = O.dense_attn(q, kv, x, 0, sink, np.arange(T), ratio=1, window=0)
+    np.testing.assert_allclose(o_d, o, rtol=1e-14, atol=1e-15)
+    # SDPA: keys = [zero key for the sink, x_0..x_{T-1}], values = [0, x]
+    K = torch.from_numpy(np.concatenate([np.zeros((1, d)), x]))[None, None].expand(1, H, T + 1, d)
+    V = K.clone(); V[:, :, 0] = 0
+    Q = torch.from_numpy(q.transpose(1, 0, 2))[None]
+    mask = torch.full((T, T + 1), float("-inf"), dtype=torch.float64)
+    for t in range(T):
+        mask[t, 1:t + 2] = 0.0
+    bias = mask[None].repeat(H, 1, 1)
+    bias[:, :, 0] = torch.from_numpy(sink)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=bias[None], scale=1.0)
+    np.testing.assert_allclose(o, ref[0].numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+    # and with the sink at -inf it is plain causal attention
+    o3, _ = O.sparse_attn(q, kv, idx, x, 0, np.full(H, -np.inf), np.arange(T), window=0)
+    Kx = torch.from_numpy(x)[None, None].expand(1, H, T, d)
+    ref3 = torch.nn.functional.scaled_dot_product_attention(Q, Kx, Kx, is_causal=True, scale=1.0)
+    np.testing.assert_allclose(o3, ref3[0].numpy().transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+
+
+def test_window_rows_reading():
+    assert list(O.window_rows(5, 128, 0, 10)) == [0, 1, 2, 3, 4, 5]
+    assert list(O.window_rows(300, 128, 0, 301)) == list(range(173, 301))
+    assert list(O.window_rows(300, 128, 200, 101)) == list(range(200, 301))
+    assert len(O.window_rows(300, 0, 0, 301)) == 0
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_full_selection_reduces_csa_to_dense(seed):
+    """k >= n(p) turns CSA's sparse attention into dense attention over compressed entries."""
+    g = np.random.default_rng(seed)
+    T, H, d = 64, 4, 16
+    kv = g.standard_normal((T // 4, d))
+    x = g.standard_normal((T, d))
+    q = g.standard_normal((T, H, d)) / 4
+    sink = g.standard_normal(H)
+    pos = np.arange(T)
+    scores = g.standard_normal((T, T // 4))
+    idx = O.topk_select(scores, O.visible_entries(pos, 4, T // 4), k=T)
+    o1, l1 = O.sparse_attn(q, kv, idx, x, 0, sink, pos, 8)
+    o2, l2 = O.dense_attn(q, kv, x, 0, sink, pos, 4, 8)
+    np.testing.assert_allclose(o1, o2, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14)
+
+
+def _layer_by_masks(inp, k, ratio, window):
+    """Second formulation of the CSA layer: full score matrix, a full sort per row,
+    and one masked softmax over [sink | all entries | all raw tokens]."""
+    inp = {key: np.asarray(v, dtype=np.float64) for key, v in inp.items()}
+    T, d = inp["c_a"].shape
+    N = T // ratio
+    # compression as a mask-weighted sum over all tokens
+    def compress(ca, cb, za, zb):
+        E = np.zeros((N, ca.shape[1]))
+        for j in range(N):
+            tok = np.arange(T)
+            ma = (tok // ratio) == j
+            mb = ((tok // ratio) == j - 1) if j > 0 else np.zeros(T, bool)
+            logit = np.where(ma[:, None], za, np.where(mb[:, None], zb, -np.inf))
+            val = np.where(ma[:, None], ca, np.where(mb[:, None], cb, 0.0))
+            wgt = np.exp(logit - logit.max(axis=0))
+            E[j] = (wgt * val).sum(axis=0) / wgt.sum(axis=0)
+        return E
+    kv = compress(inp["c_a"], inp["c_b"], inp["z_a"], inp["z_b"])
+    ki = compress(inp["ci_a"], inp["ci_b"], inp["zi_a"], inp["zi_b"])
+    q_i, w = inp["q_i"].astype(np.float64), inp["w"].astype(np.float64)
+    full = np.einsum("thd,nd->thn", q_i, ki)
+    S = np.einsum("th,thn->tn", w, np.maximum(full, 0))
+    vis = (ratio * np.arange(N)[None, :] + ratio - 1) <= np.arange(T)[:, None]
+    sel = np.zeros((T, N), bool)
+    for t in range(T):
+        cand = np.flatnonzero(vis[t])
+        order = sorted(cand, key=lambda j: (-S[t, j], j))
+        sel[t, order[:k]] = True
+    win = (np.arange(T)[None, :] <= np.arange(T)[:, None]) & (np.arange(T)[None, :] > np.arange(T)[:, None] - window)
+    keys = np.concatenate([kv, inp["c_a"]], axis=0)          # [N + T, d]
+    mask = np.concatenate([sel, win], axis=1)                 # [T, N + T]
+    q = inp["q"].astype(np.float64)
+    logits = np.einsum("thd,kd->thk", q, keys)
+    logits = np.where(mask[:, None, :], logits, -np.inf)
+    sink = np.broadcast_to(inp["sink"][None, :, None], (T, q.shape[1], 1))
+    allz = np.concatenate([sink, logits], axis=2)
+    p = np.exp(allz - allz.max(axis=2, keepdims=True))
+    p = p / p.sum(axis=2, keepdims=True)
+    o = np.einsum("thk,kd->thd", p[:, :, 1:], keys)
+    return o, sel
+
+
+@pytest.mark.parametrize("seed", range(100))
+def test_layer_brute_force_T16(seed):
+    """Whole CSA layer at T = 16: the gather formulation equals the mask formulation."""
+    inp = syn.csa_prefill(500 + seed, T=16, H=2, H_I=3, d_I=8, bf16=False, d=8)
+    for k, W in ((2, 4), (1, 1), (4, 128)):
+        got = O.csa_layer(inp, k=k, ratio=4, window=W)
+        o_ref, sel_ref = _layer_by_masks(inp, k, 4, W)
+        np.testing.assert_allclose(got["o"], o_ref, rtol=1e-12, atol=1e-13)
+        sel = np.zeros_like(sel_ref)
+        for t in range(16):
+            ii = got["idx"][t]
+            sel[t, ii[ii >= 0]] = True
+        assert np.array_equal(sel, sel_ref)
