@@ -1,0 +1,224 @@
+/*
+ * csa_hip.h — C ABI of the CSA/HCA hybrid attention forward for MI355X (gfx950).
+ *
+ * The method is DeepSeek-V4's attention layer as the public write-ups describe
+ * it: a gated, overlapped 4:1 KV compressor feeding a low-precision lightning
+ * indexer that picks the top-k compressed entries per query (CSA), a 128:1
+ * compressor with dense attention over all entries (HCA), and in both a
+ * 128-token uncompressed sliding window and a learnable attention sink.
+ * Sources, by page address and section:
+ *   cf-1.com write-up (www.cf-1.com/news/5231315): §2.4 top-k 512/1024,
+ *     §3.1 CSA, §3.2 HCA, §3.3 window branch and sink, §3.4 low-rank FP4
+ *     indexer, §4.3 deterministic kernels, §4.4 FP4 QK path, FP4->FP8 lossless.
+ *   yfxerp.com write-up "DeepSeek-V4 原理拆解" (www.yfxerp.com/news/211352):
+ *     §1 module overview, §3 config skeleton (kv_compress_ratio 4,
+ *     top_k_blocks 1024, indexer_rank 64, sliding_window 128,
+ *     compress_ratio 128, attention_sink).
+ *
+ * Conventions (all entry points):
+ *  - Every tensor pointer is a DEVICE pointer, allocated, owned and freed by
+ *    the caller. Tensors are dense, row-major, with the shapes given below.
+ *  - The library never allocates device memory in these calls. Scratch space
+ *    is the caller's `ws` buffer, sized by the matching *_workspace_size().
+ *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *    asynchronously; the caller synchronises before reading results.
+ *  - Arguments are validated on the host before anything is launched. On
+ *    failure the call returns a non-zero csa_status, launches nothing, and
+ *    csa_last_error() holds a description (thread-local). A failed kernel
+ *    launch returns CSA_ERR_HIP. There are no slow fallbacks: an unsupported
+ *    combination returns CSA_ERR_UNSUPPORTED.
+ *  - Positions are absolute token positions. q_pos unifies prefill (0..T-1),
+ *    decode (one position L per sequence) and chunked prefill (L-C..L-1).
+ *  - Entry visibility is causal: with compression ratio m, the query at
+ *    position p sees entries j < n(p) = min(N, floor((p+1)/m)).
+ *  - Results are deterministic: the same inputs give bit-identical outputs.
+ *  - Calls are not thread-safe with respect to csa_kernel_timer_*.
+ */
+#ifndef CSA_HIP_H
+#define CSA_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  CSA_ERR_SHAPE = 2,       /* sizes are negative, inconsistent or out of range */
+  CSA_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, width, head count) */
+  CSA_ERR_WORKSPACE = 4,   /* ws is NULL or smaller than *_workspace_size() */
+  CSA_ERR_HIP = 5          /* the HIP runtime reported an error */
+} csa_status;
+
+typedef enum {
+  CSA_F32 = 0,       /* IEEE float32 */
+  CSA_BF16 = 1,      /* bfloat16 (stored as 16-bit words) */
+  CSA_FP8_E4M3 = 2,  /* OCP e4m3 (max 448), one float32 scale per row */
+  CSA_FP4_E2M1 = 3   /* OCP e2m1, two per byte (element 2i in the low nibble),
+                        one E8M0 scale byte per 32 consecutive elements */
+} csa_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* csa_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* csa_last_error(void);
+/* Library version string. */
+const char* csa_version(void);
+
+/*
+ * csa_quantize_rows — quantise `rows` vectors of `width` elements.
+ * Low-precision indexer keys and queries (cf-1.com write-up §3.4: the indexer
+ * QK runs in FP4; §4.4: FP4->FP8 dequantisation is lossless).
+ *   x        [rows, width] of in_t (CSA_F32 or CSA_BF16)
+ *   out      CSA_FP8_E4M3: uint8 [rows, width]; scale: float32 [rows],
+ *              scale = amax/448 in float32 (1 for an all-zero row),
+ *              code = e4m3(x / scale), IEEE float32 division, round to
+ *              nearest even, saturating at 448.
+ *            CSA_FP4_E2M1: uint8 [rows, width/2]; scale: uint8 [rows, width/32]
+ *              holding E+127 with E = floor(log2(block amax)) - 2 (0 for an
+ *              all-zero block), code = e2m1(x * 2^-E), round to nearest even,
+ *              saturating at 6.
+ *   width    multiple of 32 (fp4) or any positive value (fp8), <= 4096.
+ * The sign bit of a code is the sign of the input (tiny negatives give -0).
+ */
+csa_status csa_quantize_rows(const void* x, csa_dtype in_t, int64_t rows, int32_t width,
+                             void* out, csa_dtype out_t, void* scale, void* stream);
+
+/*
+ * csa_compress — CSA compressor: overlapped, gated, two-stream, ratio:1
+ * (cf-1.com write-up §3.1; yfxerp.com write-up §3 kv_compress_ratio 4).
+ * Entry j, channel c:  E[j,c] = sum_t w_t * C_t[c], with one softmax per
+ * channel over the joint list of gate logits of stream A at tokens
+ * [ratio*j, ratio*j+ratio) and stream B at tokens [ratio*j-ratio, ratio*j)
+ * (B omitted for j = 0). N = floor(T/ratio); a trailing partial block is
+ * not compressed.
+ *   c_a, c_b, z_a, z_b  [B, T, width] of in_t (CSA_F32 or CSA_BF16)
+ *   out       [B, N, width] of out_t: CSA_F32, CSA_BF16, or a quantised
+ *             indexer-key format (CSA_FP8_E4M3 / CSA_FP4_E2M1, quantised per
+ *             entry row exactly as csa_quantize_rows does, from the float32
+ *             value of E) with out_scale as csa_quantize_rows' `scale`
+ *             ([B, N] float32 or [B, N, width/32] uint8). out_scale must be
+ *             NULL for CSA_F32/CSA_BF16.
+ *   width     64 or 128;  ratio 1..128.
+ */
+csa_status csa_compress(const void* c_a, const void* c_b, const void* z_a, const void* z_b,
+                        csa_dtype in_t, int64_t B, int64_t T, int32_t width, int32_t ratio,
+                        void* out, csa_dtype out_t, void* out_scale, void* stream);
+
+/*
+ * hca_compress — HCA compressor: non-overlapped, gated, single stream,
+ * ratio:1 (cf-1.com write-up §3.2; yfxerp.com write-up §3 compress_ratio 128).
+ * E[j,c] = sum_{i<ratio} softmax_i(Z[ratio*j+i, c]) * C[ratio*j+i, c].
+ * Ratio 1 is the identity.
+ *   c, z   [B, T, width] of in_t (CSA_F32 or CSA_BF16)
+ *   out    [B, floor(T/ratio), width] of out_t (CSA_F32 or CSA_BF16)
+ *   width  64 or 128;  ratio 1..4096.
+ */
+csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B, int64_t T,
+                        int32_t width, int32_t ratio, void* out, csa_dtype out_t, void* stream);
+
+/*
+ * indexer_topk — lightning-indexer scores and per-query top-k selection
+ * (cf-1.com write-up §3.1: each query picks its top-k compressed entries
+ * through the lightning indexer; §2.4: k = 512 or 1024; §3.4: low-rank,
+ * low-precision indexer; yfxerp.com write-up §3 top_k_blocks, indexer_rank).
+ * Score of entry s for the query at position p (s < n(p)):
+ *     I(p,s) = sum_h w(p,h) * max(0, q(p,h) . k(s))
+ * with q and k dequantised (code * scale). Scores are accumulated in float32.
+ * Selection: the min(k, n(p)) largest scores under the total order
+ * (score descending, index ascending); -0 equals +0.
+ *   q_idx    [B, Tq, H_I, d_I] of qk_t (fp4: [B, Tq, H_I, d_I/2] bytes)
+ *   q_scale  fp8: float32 [B, Tq, H_I]; fp4: uint8 [B, Tq, H_I, d_I/32];
+ *            must be NULL for CSA_F32 / CSA_BF16
+ *   w        float32 [B, Tq, H_I], any sign
+ *   k_idx    [B, N, d_I] of qk_t;  k_scale: fp8 float32 [B, N], fp4 uint8
+ *            [B, N, d_I/32], NULL otherwise
+ *   q_pos    int32 [B, Tq], >= 0
+ *   idx_out  int32 [B, Tq, k]: selected entries in ascending order, then -1
+ *   score_out  NULL, or float32 [B, Tq, N]: the scores (entries >= n(p)
+ *            are left untouched)
+ *   H_I 1..64; d_I 64 or 128; k 1..2048; ratio >= 1; N < 2^30.
+ * Scores must be finite (NaN selection order is undefined).
+ */
+size_t indexer_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I,
+                                   int32_t k, csa_dtype qk_t);
+csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w,
+                        const void* k_idx, const void* k_scale, csa_dtype qk_t,
+                        const int32_t* q_pos, int64_t B, int64_t Tq, int64_t N,
+                        int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
+                        int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * sparse_attn_fwd — CSA core attention over the selected compressed entries,
+ * the uncompressed window and the sink (cf-1.com write-up §3.1, §3.3;
+ * yfxerp.com write-up §3 sliding_window 128, attention_sink).
+ * For the query at position p and head h, with keys (= values, one shared KV
+ * head for all query heads) K = {kv[s] : s in idx[p], 0 <= s < N} joined with
+ * the window rows {x_win[t - win_start] : max(0, p-window+1) <= t <= p,
+ * win_start <= t < win_start + T_win}:
+ *     l_i = scale * q_h . K_i,
+ *     o_h = sum_i e^{l_i} K_i / (e^{sink_h} + sum_i e^{l_i}),
+ *     lse_h = log(e^{sink_h} + sum_i e^{l_i}).
+ * Entries of idx outside [0, N) (e.g. -1 padding) are skipped.
+ *   q      [B, Tq, H, d] of t (CSA_F32 or CSA_BF16)
+ *   kv     [B, N, d] of t;   idx int32 [B, Tq, k]
+ *   x_win  [B, T_win, d] of t;  win_start int32 [B] (position of row 0)
+ *   sink   float32 [H], or NULL for no sink
+ *   q_pos  int32 [B, Tq];  out [B, Tq, H, d] of t;  lse NULL or float32 [B, Tq, H]
+ *   d == 128; H a multiple of 16, <= 256; 1 <= k <= 4096; window >= 0.
+ * Accumulation is float32; a query with no keys and no sink gives o = 0.
+ */
+size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, int32_t k,
+                                  int32_t window);
+csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
+                           const int32_t* win_start, const float* sink, const int32_t* q_pos,
+                           csa_dtype t, int64_t B, int64_t Tq, int64_t N, int64_t T_win,
+                           int32_t H, int32_t d, int32_t k, int32_t window, float scale,
+                           void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dense_compressed_attn_fwd — HCA core attention: every visible compressed
+ * entry (j < n(p), dense, no selection), plus the window and the sink
+ * (cf-1.com write-up §3.2, §3.3). Same formula and layouts as
+ * sparse_attn_fwd with idx = 0..n(p)-1.
+ *   ratio >= 1 defines n(p).
+ */
+size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t d,
+                                 int32_t window);
+csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* x_win,
+                                     const int32_t* win_start, const float* sink,
+                                     const int32_t* q_pos, csa_dtype t, int64_t B, int64_t Tq,
+                                     int64_t N, int64_t T_win, int32_t H, int32_t d,
+                                     int32_t ratio, int32_t window, float scale, void* out,
+                                     float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timer (measurement support). csa_kernel_timer_start() arms the
+ * library to record a pair of hipEvents around each of the next
+ * `max_launches` launches of kernel `kernel_id` (a csa_kernel_id), on the
+ * stream the kernel is launched on. csa_kernel_timer_read() waits for the
+ * last recorded event, writes up to `capacity` durations in milliseconds and
+ * returns how many launches were recorded (negative on error); it disarms the
+ * timer. Not for use under stream capture.
+ */
+typedef enum {
+  CSA_KID_COMPRESS = 1,
+  CSA_KID_HCA_COMPRESS = 2,
+  CSA_KID_QUANTIZE = 3,
+  CSA_KID_INDEX_SCORE = 4,
+  CSA_KID_TOPK = 5,
+  CSA_KID_SPARSE_ATTN = 6,
+  CSA_KID_DENSE_ATTN = 7,
+  CSA_KID_ATTN_MERGE = 8
+} csa_kernel_id;
+csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches);
+int32_t csa_kernel_timer_read(float* ms_out, int32_t capacity);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_HIP_H */

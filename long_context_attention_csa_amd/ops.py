@@ -1,0 +1,179 @@
+"""Python binding of the C ABI: same names, argument marshalling only.
+
+Each function takes torch tensors that already live on the GPU, allocates the
+outputs (and workspace, unless one is passed in) with torch, and calls the
+library on torch's current stream. Every step of the computation runs in the
+HIP kernels of libcsa_hip.so; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import (CSA_BF16, CSA_F32, CSA_FP4_E2M1, CSA_FP8_E4M3, KID, check, lib)
+
+FMT = {"f32": CSA_F32, "bf16": CSA_BF16, "fp8": CSA_FP8_E4M3, "fp4": CSA_FP4_E2M1}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _float_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _torch_dtype(fmt: int):
+    return {CSA_F32: torch.float32, CSA_BF16: torch.bfloat16}[fmt]
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() < nbytes:
+        raise ValueError(f"workspace too small: {ws.numel()} < {nbytes}")
+    return ws, ws.numel()
+
+
+def _quant_out(shape_rows, width, fmt, device):
+    if fmt == CSA_FP8_E4M3:
+        return (torch.empty(*shape_rows, width, dtype=torch.uint8, device=device),
+                torch.empty(*shape_rows, dtype=torch.float32, device=device))
+    return (torch.empty(*shape_rows, width // 2, dtype=torch.uint8, device=device),
+            torch.empty(*shape_rows, width // 32, dtype=torch.uint8, device=device))
+
+
+def csa_quantize_rows(x: torch.Tensor, out_fmt: str):
+    """Quantise the last axis of x to "fp8" (per-row float32 scale) or "fp4" (E8M0 per 32)."""
+    _contig(x)
+    fmt = FMT[out_fmt]
+    width = x.shape[-1]
+    rows = x.numel() // width if width else 0
+    out, scale = _quant_out(tuple(x.shape[:-1]), width, fmt, x.device)
+    check("csa_quantize_rows", lib().csa_quantize_rows(_ptr(x), _float_dtype(x), rows, width, _ptr(out), fmt,
+                                                       _ptr(scale), _stream()))
+    return out, scale
+
+
+def csa_compress(c_a, c_b, z_a, z_b, ratio: int = 4, out_fmt: str | None = None):
+    """CSA compressor. Inputs [B, T, width]; returns E [B, T//ratio, width] (and the
+    scale tensor when out_fmt is "fp8"/"fp4")."""
+    _contig(c_a, c_b, z_a, z_b)
+    in_t = _float_dtype(c_a)
+    B, T, width = c_a.shape
+    N = T // ratio
+    fmt = FMT[out_fmt] if out_fmt else in_t
+    if fmt in (CSA_F32, CSA_BF16):
+        out, scale = torch.empty(B, N, width, dtype=_torch_dtype(fmt), device=c_a.device), None
+    else:
+        out, scale = _quant_out((B, N), width, fmt, c_a.device)
+    check("csa_compress", lib().csa_compress(_ptr(c_a), _ptr(c_b), _ptr(z_a), _ptr(z_b), in_t, B, T, width, ratio,
+                                             _ptr(out), fmt, _ptr(scale), _stream()))
+    return out if scale is None else (out, scale)
+
+
+def hca_compress(c, z, ratio: int = 128, out_fmt: str | None = None):
+    """HCA compressor. Inputs [B, T, width]; returns [B, T//ratio, width]."""
+    _contig(c, z)
+    in_t = _float_dtype(c)
+    B, T, width = c.shape
+    fmt = FMT[out_fmt] if out_fmt else in_t
+    out = torch.empty(B, T // ratio, width, dtype=_torch_dtype(fmt), device=c.device)
+    check("hca_compress", lib().hca_compress(_ptr(c), _ptr(z), in_t, B, T, width, ratio, _ptr(out), fmt, _stream()))
+    return out
+
+
+def indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt: str) -> int:
+    return int(lib().indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, FMT[fmt]))
+
+
+def indexer_topk(q_idx, q_scale, w, k_idx, k_scale, fmt: str, q_pos, ratio: int, k: int, d_I: int,
+                 want_scores: bool = False, ws=None, idx_out=None):
+    """Indexer scores and top-k. q_idx [B, Tq, H_I, d_I(/2 for fp4)], w [B, Tq, H_I] float32,
+    k_idx [B, N, d_I(/2)], q_pos int32 [B, Tq]. Returns idx int32 [B, Tq, k]
+    (and the float32 scores [B, Tq, N] when want_scores)."""
+    _contig(q_idx, q_scale, w, k_idx, k_scale, q_pos)
+    f = FMT[fmt]
+    B, Tq, H_I = q_idx.shape[:3]
+    N = k_idx.shape[1]
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty(B, Tq, k, dtype=torch.int32, device=dev)
+    scores = torch.empty(B, Tq, N, dtype=torch.float32, device=dev) if want_scores else None
+    ws, nbytes = _workspace(indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt), dev, ws)
+    check("indexer_topk", lib().indexer_topk(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), f,
+                                             _ptr(q_pos), B, Tq, N, H_I, d_I, ratio, k, _ptr(idx_out), _ptr(scores),
+                                             _ptr(ws), nbytes, _stream()))
+    return (idx_out, scores) if want_scores else idx_out
+
+
+def sparse_attn_workspace_size(B, Tq, H, d, k, window) -> int:
+    return int(lib().sparse_attn_workspace_size(B, Tq, H, d, k, window))
+
+
+def sparse_attn_fwd(q, kv, idx, x_win, win_start, sink, q_pos, window: int = 128, scale: float = 1.0,
+                    want_lse: bool = False, ws=None, out=None):
+    """CSA core attention. q [B, Tq, H, d], kv [B, N, d], idx int32 [B, Tq, k],
+    x_win [B, T_win, d], win_start int32 [B], sink float32 [H] or None, q_pos int32 [B, Tq]."""
+    _contig(q, kv, idx, x_win, win_start, sink, q_pos)
+    t = _float_dtype(q)
+    B, Tq, H, d = q.shape
+    N, T_win, k = kv.shape[1], x_win.shape[1], idx.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device=q.device) if want_lse else None
+    ws, nbytes = _workspace(sparse_attn_workspace_size(B, Tq, H, d, k, window), q.device, ws)
+    check("sparse_attn_fwd", lib().sparse_attn_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(x_win), _ptr(win_start),
+                                                   _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H, d, k, window,
+                                                   scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
+    return (out, lse) if want_lse else out
+
+
+def dense_attn_workspace_size(B, Tq, N, H, d, window) -> int:
+    return int(lib().dense_attn_workspace_size(B, Tq, N, H, d, window))
+
+
+def dense_compressed_attn_fwd(q, kv, x_win, win_start, sink, q_pos, ratio: int = 128, window: int = 128,
+                              scale: float = 1.0, want_lse: bool = False, ws=None, out=None):
+    """HCA core attention over all visible entries plus window and sink."""
+    _contig(q, kv, x_win, win_start, sink, q_pos)
+    t = _float_dtype(q)
+    B, Tq, H, d = q.shape
+    N, T_win = kv.shape[1], x_win.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device=q.device) if want_lse else None
+    ws, nbytes = _workspace(dense_attn_workspace_size(B, Tq, N, H, d, window), q.device, ws)
+    check("dense_compressed_attn_fwd", lib().dense_compressed_attn_fwd(
+        _ptr(q), _ptr(kv), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H, d, ratio,
+        window, scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
+    return (out, lse) if want_lse else out
+
+
+def kernel_timer_start(kernel: str, max_launches: int) -> None:
+    check("csa_kernel_timer_start", lib().csa_kernel_timer_start(KID[kernel], max_launches))
+
+
+def kernel_timer_read(capacity: int = 4096) -> list[float]:
+    buf = (ctypes.c_float * capacity)()
+    n = lib().csa_kernel_timer_read(buf, capacity)
+    if n < 0:
+        raise RuntimeError("csa_kernel_timer_read failed")
+    return [buf[i] for i in range(min(n, capacity))]

@@ -1,0 +1,111 @@
+"""C-ABI contract on the host: the library loads, exports every declared
+symbol, and rejects bad arguments with the documented status before any launch
+(these calls make no HIP call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_csa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa_hip.h")
+
+OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
+P = ctypes.c_void_p(0x1000)   # a non-NULL pointer that is never dereferenced (validation fails first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), set(names) ^ set(_lib.SIGNATURES)
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    assert lib.csa_status_string(0) == b"CSA_OK"
+    assert lib.csa_status_string(4) == b"CSA_ERR_WORKSPACE"
+    assert b"gfx950" in lib.csa_version()
+
+
+def _err(lib):
+    return lib.csa_last_error().decode()
+
+
+def test_compress_validation():
+    lib = _lib.lib()
+    assert lib.csa_compress(P, P, P, P, 1, 1, 64, 96, 4, P, 1, None, None) == UNSUP      # width
+    assert "width" in _err(lib)
+    assert lib.csa_compress(P, P, P, P, 2, 1, 64, 128, 4, P, 1, None, None) == UNSUP     # fp8 input
+    assert lib.csa_compress(P, P, P, P, 1, 1, 64, 128, 0, P, 1, None, None) == SHAPE     # ratio 0
+    assert lib.csa_compress(P, P, P, P, 1, -1, 64, 128, 4, P, 1, None, None) == SHAPE    # B < 0
+    assert lib.csa_compress(None, P, P, P, 1, 1, 64, 128, 4, P, 1, None, None) == NULL
+    assert lib.csa_compress(P, P, P, P, 1, 1, 64, 128, 4, P, 2, None, None) == NULL      # fp8 without scale
+    assert lib.csa_compress(P, P, P, P, 1, 1, 64, 128, 4, P, 1, P, None) == SHAPE        # scale for bf16 out
+    assert lib.csa_compress(None, None, None, None, 1, 1, 3, 128, 4, None, 1, None, None) == OK  # nothing to do
+    assert lib.hca_compress(P, P, 1, 1, 256, 128, 0, P, 1, None) == SHAPE
+    assert lib.hca_compress(P, P, 1, 1, 256, 128, 128, P, 2, None) == UNSUP
+    assert lib.csa_quantize_rows(P, 1, 4, 48, P, 3, P, None) == SHAPE                   # fp4 width % 32
+    assert lib.csa_quantize_rows(P, 1, 4, 64, P, 1, P, None) == UNSUP
+
+
+def test_indexer_validation():
+    lib = _lib.lib()
+    args = lambda **kw: dict(dict(q=P, qs=P, w=P, k=P, ks=P, fmt=2, pos=P, B=1, Tq=1, N=64, H=64, d=128, ratio=4,
+                                  kk=16, out=P, so=None, ws=P, wsb=1 << 40), **kw)
+    call = lambda a: lib.indexer_topk(a["q"], a["qs"], a["w"], a["k"], a["ks"], a["fmt"], a["pos"], a["B"], a["Tq"],
+                                      a["N"], a["H"], a["d"], a["ratio"], a["kk"], a["out"], a["so"], a["ws"],
+                                      a["wsb"], None)
+    assert call(args(kk=0)) == SHAPE
+    assert call(args(kk=2049)) == SHAPE
+    assert call(args(H=65)) == UNSUP
+    assert call(args(d=96)) == UNSUP
+    assert call(args(qs=None)) == NULL
+    assert call(args(fmt=0)) == SHAPE              # scales given for float operands
+    assert call(args(fmt=7)) == UNSUP
+    assert call(args(ws=None)) == WS
+    need = lib.indexer_topk_workspace_size(1, 1, 64, 64, 128, 16, 2)
+    assert need > 0 and call(args(wsb=need - 1)) == WS
+    assert call(args(B=0)) == OK
+
+
+def test_attention_validation():
+    lib = _lib.lib()
+    f = lib.sparse_attn_fwd
+    base = [P, P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 64, 128, 1.0, P, None, P, 1 << 40, None]
+    def call(**kw):
+        a = list(base)
+        pos = {"t": 7, "H": 12, "d": 13, "k": 14, "window": 15, "q": 0, "ws": 19, "wsb": 20, "idx": 2}
+        for k_, v in kw.items():
+            a[pos[k_]] = v
+        return f(*a)
+    assert call(d=64) == UNSUP
+    assert call(H=24) == UNSUP
+    assert call(t=2) == UNSUP
+    assert call(k=0) == SHAPE
+    assert call(window=-1) == SHAPE
+    assert call(q=None) == NULL
+    assert call(idx=None) == NULL
+    g = lib.dense_compressed_attn_fwd
+    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 0, 128, 1.0, P, None, P, 1 << 40, None) == SHAPE
+    # decode shapes need a split workspace
+    need = lib.dense_attn_workspace_size(1, 1, 8192, 128, 128, 128)
+    assert need > 0
+    assert g(P, P, P, P, None, P, 1, 1, 1, 8192, 128, 128, 128, 128, 128, 1.0, P, None, None, 0, None) == WS
+
+
+def test_timer_validation():
+    lib = _lib.lib()
+    assert lib.csa_kernel_timer_start(0, 4) == SHAPE
+    assert lib.csa_kernel_timer_start(4, 0) == SHAPE

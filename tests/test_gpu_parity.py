@@ -1,0 +1,363 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded
+inputs, at sizes that span several tiles and a ragged tail, plus edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import csa_synth as syn
+import long_context_attention_csa_amd as C
+from oracle import csa_oracle as O
+from tests.gpu_common import (assert_close, certified_index_mismatches, dev, host, recall)
+
+pytestmark = pytest.mark.gpu
+BF = torch.bfloat16
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------- quantisation
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("in_dtype", [torch.float32, torch.bfloat16])
+def test_quantize_rows_bit_exact(fmt, in_dtype):
+    g = np.random.default_rng(1)
+    x = (g.standard_normal((1031, 128)) * np.exp(g.uniform(-8, 8, (1031, 1)))).astype(np.float32)
+    x[5] = 0.0
+    x[6, :64] = 0.0
+    x[7] = 1e-38
+    x[8, 3] = -1e-30
+    if in_dtype == torch.bfloat16:
+        x = syn.round_bf16(x)
+    _print("quantize", fmt, in_dtype)
+    codes, scale = C.csa_quantize_rows(dev(x, in_dtype), fmt)
+    torch.cuda.synchronize()
+    if fmt == "fp8":
+        rc, rs = O.quant_fp8_rows(x)
+    else:
+        rc, rs = O.quant_mxfp4_rows(x)
+    assert np.array_equal(host(codes), rc)
+    assert np.array_equal(host(scale), rs)
+
+
+# ---------------------------------------------------------------- compression
+
+@pytest.mark.parametrize("width", [128, 64])
+@pytest.mark.parametrize("ratio", [4, 1, 8])
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_csa_compress(width, ratio, kind):
+    T = 4 * 37 * 8 + 3 if ratio != 1 else 301
+    inp = syn.csa_prefill(7, T=T, H=16, H_I=4, d_I=width, bf16=(kind == "bf16"), d=width)
+    dt = torch.float32 if kind == "f32" else BF
+    B = 2
+    stack = lambda a: np.stack([a, a[::-1].copy()])
+    ca, cb, za, zb = (stack(inp[n]) for n in ("c_a", "c_b", "z_a", "z_b"))
+    _print("csa_compress", width, ratio, kind)
+    out = C.csa_compress(dev(ca, dt), dev(cb, dt), dev(za, dt), dev(zb, dt), ratio)
+    got = host(out)
+    for b in range(B):
+        want = O.csa_compress(ca[b], cb[b], za[b], zb[b], ratio)
+        assert_close(got[b], want, kind, f"csa_compress b={b}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_csa_compress_quantized_epilogue(fmt):
+    """Fused quantisation of the compressed indexer keys. The GPU decides codes
+    from its own float32 E; a code may differ from the oracle's (float64 E
+    rounded to float32) only by one step, and only rarely."""
+    T = 4 * 1000
+    inp = syn.csa_prefill(8, T=T, H=16, H_I=4, d_I=128, bf16=True)
+    _print("csa_compress quant", fmt)
+    codes, scale = C.csa_compress(*(dev(inp[n][None], BF) for n in ("ci_a", "ci_b", "zi_a", "zi_b")), 4, out_fmt=fmt)
+    E = O.csa_compress(inp["ci_a"], inp["ci_b"], inp["zi_a"], inp["zi_b"], 4).astype(np.float32)
+    if fmt == "fp8":
+        rc, rs = O.quant_fp8_rows(E)
+        deq_g = O.dequant_fp8_rows(host(codes)[0], host(scale)[0])
+        deq_o = O.dequant_fp8_rows(rc, rs)
+        step = np.abs(deq_o) * 2.0 ** -3 + rs[:, None] * 2.0 ** -9
+    else:
+        rc, rs = O.quant_mxfp4_rows(E)
+        deq_g = O.dequant_mxfp4_rows(host(codes)[0], host(scale)[0])
+        deq_o = O.dequant_mxfp4_rows(rc, rs)
+        step = np.repeat(np.exp2(rs.astype(np.float64) - 127.0), 32, axis=1) * 2.0
+    mism = np.mean(host(codes)[0] != rc)
+    assert mism < 2e-3, mism
+    assert np.all(np.abs(deq_g - deq_o) <= step * (1 + 1e-9))
+
+
+@pytest.mark.parametrize("ratio", [128, 1, 32])
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_hca_compress(ratio, kind):
+    T = 128 * 19 + 77 if ratio != 1 else 257
+    inp = syn.hca_prefill(9, T=T, H=16, bf16=(kind == "bf16"))
+    dt = torch.float32 if kind == "f32" else BF
+    _print("hca_compress", ratio, kind)
+    out = C.hca_compress(dev(inp["c"][None], dt), dev(inp["z"][None], dt), ratio)
+    want = O.hca_compress(inp["c"], inp["z"], ratio)
+    if ratio == 1 and kind == "f32":
+        assert np.array_equal(host(out)[0], inp["c"])
+    assert_close(host(out)[0], want, kind, "hca_compress")
+
+
+# ---------------------------------------------------------------- indexer
+
+def _grid_operands(fmt, q_i, k_i):
+    """Exact-grid operands: codes of the integer / e2m1-grid values with unit scales."""
+    if fmt == "fp8":
+        qc = O.e4m3_encode(q_i)
+        kc = O.e4m3_encode(k_i)
+        qs = np.ones(q_i.shape[:-1], np.float32)
+        ks = np.ones(k_i.shape[:-1], np.float32)
+        return dev(qc, torch.uint8), dev(qs), dev(kc, torch.uint8), dev(ks)
+    if fmt == "fp4":
+        pk = lambda v: (O.e2m1_encode(v)[..., 0::2] | (O.e2m1_encode(v)[..., 1::2] << 4)).astype(np.uint8)
+        qs = np.full(q_i.shape[:-1] + (q_i.shape[-1] // 32,), 127, np.uint8)
+        ks = np.full(k_i.shape[:-1] + (k_i.shape[-1] // 32,), 127, np.uint8)
+        return dev(pk(q_i), torch.uint8), dev(qs, torch.uint8), dev(pk(k_i), torch.uint8), dev(ks, torch.uint8)
+    dt = torch.float32 if fmt == "f32" else BF
+    return dev(q_i, dt), None, dev(k_i, dt), None
+
+
+def _oracle_topk(q_i, w, k_i, q_pos, ratio, k):
+    """Per-batch oracle scores (float64) and top-k. q_i [B, Tq, H, d], k_i [B, N, d]."""
+    B, Tq = q_i.shape[:2]
+    N = k_i.shape[1]
+    scores = np.stack([O.indexer_scores(q_i[b], w[b], k_i[b], q_pos[b], ratio) for b in range(B)])
+    idx = np.stack([O.topk_select(scores[b], O.visible_entries(q_pos[b], ratio, N), k) for b in range(B)])
+    return scores, idx
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "f32", "bf16"])
+def test_indexer_exact_grid_decode(fmt):
+    """Integer (fp4: e2m1-grid) operands make every score exact in float32, so the
+    indices must match the oracle bit for bit; ties abound (lower index wins)."""
+    B, N, d_I, k = 3, 5003, 128, 256
+    d = syn.csa_decode(21, B=B, N=N, H=16, H_I=64, d_I=d_I, key_grid=("fp4" if fmt == "fp4" else "int"))
+    q_i = d["q_i"][:, None]               # [B, 1, H_I, d_I]
+    q_pos = np.array([[4 * N + 2], [4 * 3000 + 1], [4 * 100]], np.int32)
+    _print("indexer grid decode", fmt)
+    qc, qs, kc, ks = _grid_operands(fmt, q_i, d["k_i"])
+    idx = C.indexer_topk(qc, qs, dev(d["w"][:, None]), kc, ks, fmt, dev(q_pos, torch.int32), 4, k, d_I)
+    _, want = _oracle_topk(q_i, d["w"][:, None], d["k_i"], q_pos, 4, k)
+    assert np.array_equal(host(idx), want)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "f32"])
+@pytest.mark.parametrize("d_I,H_I", [(128, 64), (64, 4), (64, 19)])
+def test_indexer_exact_grid_prefill(fmt, d_I, H_I):
+    T, k = 1203, 64
+    N = T // 4
+    g = np.random.default_rng(5)
+    if fmt == "fp4":
+        q_i, k_i = syn.fp4_grid(31, (1, T, H_I, d_I)), syn.fp4_grid(32, (1, N, d_I))
+    else:
+        q_i, k_i = syn.integers(31, (1, T, H_I, d_I), -4, 4), syn.integers(32, (1, N, d_I), -4, 4)
+    w = syn.grid_weights(33, (1, T, H_I))
+    q_pos = np.arange(T, dtype=np.int32)[None]
+    _print("indexer grid prefill", fmt, d_I, H_I)
+    qc, qs, kc, ks = _grid_operands(fmt, q_i, k_i)
+    idx, sc = C.indexer_topk(qc, qs, dev(w), kc, ks, fmt, dev(q_pos, torch.int32), 4, k, d_I, want_scores=True)
+    scores, want = _oracle_topk(q_i, w, k_i, q_pos, 4, k)
+    got_s = host(sc)[0]
+    vis = np.isfinite(scores[0])
+    assert np.array_equal(got_s[vis], scores[0][vis])
+    assert np.array_equal(host(idx), want)
+
+
+def test_indexer_normal_f32_scores_and_selection():
+    """N(0,1) float32 operands: GPU scores match the oracle to float32 accuracy,
+    the oracle's selection over the GPU's own scores equals the GPU's indices
+    exactly, and any difference from the float64 selection is a certified tie."""
+    B, Tq, N, H_I, d_I, k = 2, 5, 20000, 64, 128, 1024
+    d = syn.csa_decode(22, B=B, N=N, H=16, H_I=H_I, d_I=d_I)
+    q_i = np.repeat(d["q_i"][:, None], Tq, axis=1) * np.linspace(0.5, 1.5, Tq)[None, :, None, None].astype(np.float32)
+    q_i = q_i.astype(np.float32)
+    w = np.repeat(d["w"][:, None], Tq, axis=1)
+    q_pos = np.array([[4 * N - 1, 4 * N + 9, 4 * 7000, 4 * 300 + 2, 4 * 257 - 1]] * B, np.int32)
+    _print("indexer normal f32")
+    idx, sc = C.indexer_topk(dev(q_i), None, dev(w), dev(d["k_i"]), None, "f32", dev(q_pos, torch.int32), 4, k,
+                             d_I, want_scores=True)
+    got_idx, got_s = host(idx), host(sc)
+    scores, want = _oracle_topk(q_i, w, d["k_i"], q_pos, 4, k)
+    for b in range(B):
+        n_vis = O.visible_entries(q_pos[b], 4, N)
+        for t in range(Tq):
+            n = n_vis[t]
+            np.testing.assert_allclose(got_s[b, t, :n], scores[b, t, :n], rtol=2e-5, atol=1e-3)
+        # selection on the GPU's own scores is bit-exact
+        assert np.array_equal(got_idx[b], O.topk_select(got_s[b].astype(np.float64), n_vis, k))
+        nbad = certified_index_mismatches(got_idx[b], want[b], scores[b], n_vis, k)
+        assert nbad <= 1
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_indexer_quantized_recall(fmt):
+    """Quantised operands (quantised by the oracle's quantiser): the kernel's picks
+    agree with the oracle on the same operands (recall >= 0.99 per query)."""
+    B, N, H_I, d_I, k = 4, 30000, 64, 128, 1024
+    d = syn.csa_decode(23, B=B, N=N, H=16, H_I=H_I, d_I=d_I)
+    q_i = d["q_i"][:, None]
+    q_pos = np.full((B, 1), 4 * N, np.int32)
+    quant, dequant = ((O.quant_fp8_rows, O.dequant_fp8_rows) if fmt == "fp8"
+                      else (O.quant_mxfp4_rows, O.dequant_mxfp4_rows))
+    qc, qs = quant(q_i)
+    kc, ks = quant(d["k_i"])
+    _print("indexer quant recall", fmt)
+    idx = C.indexer_topk(dev(qc, torch.uint8), dev(qs, torch.uint8 if fmt == "fp4" else torch.float32),
+                         dev(d["w"][:, None]), dev(kc, torch.uint8), dev(ks, torch.uint8 if fmt == "fp4" else torch.float32),
+                         fmt, dev(q_pos, torch.int32), 4, k, d_I)
+    _, want = _oracle_topk(dequant(qc, qs), d["w"][:, None], dequant(kc, ks), q_pos, 4, k)
+    rec = recall(host(idx), want)
+    _print(fmt, "recall vs oracle on same operands", rec)
+    assert rec.min() >= 0.99
+
+
+def test_indexer_heavy_ties_overflow_path():
+    """All scores equal: the candidate bucket holds every entry (more than the
+    in-LDS list), so the row-scan fallback runs; lowest indices must win."""
+    N, k = 20000, 100
+    q_i = np.zeros((1, 2, 4, 64), np.float32)
+    k_i = np.ones((1, N, 64), np.float32)
+    w = np.ones((1, 2, 4), np.float32)
+    q_pos = np.array([[4 * N, 4 * 5000 + 3]], np.int32)
+    idx = C.indexer_topk(dev(q_i), None, dev(w), dev(k_i), None, "f32", dev(q_pos, torch.int32), 4, k, 64)
+    got = host(idx)[0]
+    assert np.array_equal(got[0], np.arange(k)) and np.array_equal(got[1], np.arange(k))
+
+
+def test_indexer_small_n_and_padding():
+    N, k = 50, 64
+    d = syn.csa_decode(24, B=1, N=N, H=16, H_I=8, d_I=64)
+    q_pos = np.array([[0, 3, 4 * 20 + 1, 4 * 50 + 100]], np.int32)
+    q_i = np.repeat(d["q_i"][:, None], 4, axis=1)
+    w = np.repeat(d["w"][:, None], 4, axis=1)
+    idx = C.indexer_topk(dev(q_i), None, dev(w), dev(d["k_i"]), None, "f32", dev(q_pos, torch.int32), 4, k, 64)
+    got = host(idx)[0]
+    for t, n in enumerate([0, 1, 20, 50]):
+        assert np.array_equal(got[t, :n], np.arange(n)) and np.all(got[t, n:] == -1)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_case(seed, B, Tq, N, H, T_win, kind, q_pos, win_start):
+    g = np.random.default_rng(seed)
+    bf = kind == "bf16"
+    q = syn.normal(seed * 10 + 1, (B, Tq, H, 128), scale=1 / np.sqrt(128), bf16=bf)
+    kv = syn.normal(seed * 10 + 2, (B, N, 128), bf16=bf)
+    xw = syn.normal(seed * 10 + 3, (B, T_win, 128), bf16=bf)
+    sink = syn.normal(seed * 10 + 4, (H,))
+    return q, kv, xw, sink
+
+
+@pytest.mark.parametrize("kind,H,Tq,B,k", [("f32", 16, 700, 1, 64), ("bf16", 64, 300, 2, 512),
+                                           ("bf16", 128, 1, 3, 1024), ("f32", 32, 1, 2, 300)])
+def test_sparse_attn(kind, H, Tq, B, k):
+    N = 5000
+    T_win = 128 + Tq - 1 if Tq > 1 else 128
+    q_pos = np.stack([np.arange(4 * N - Tq, 4 * N) + b for b in range(B)]).astype(np.int32)
+    win_start = (q_pos[:, 0] - 127).astype(np.int32)
+    q, kv, xw, sink = _attn_case(3, B, Tq, N, H, T_win, kind, q_pos, win_start)
+    g = np.random.default_rng(4)
+    idx = np.stack([[np.sort(g.choice(N, size=k, replace=False)) for _ in range(Tq)] for _ in range(B)]).astype(np.int32)
+    idx[:, ::3, -k // 5:] = -1             # padded rows
+    dt = torch.float32 if kind == "f32" else BF
+    _print("sparse_attn", kind, H, Tq, B, k)
+    out, lse = C.sparse_attn_fwd(dev(q, dt), dev(kv, dt), dev(idx, torch.int32), dev(xw, dt),
+                                 dev(win_start, torch.int32), dev(sink), dev(q_pos, torch.int32), 128, 1.0,
+                                 want_lse=True)
+    got, got_lse = host(out), host(lse)
+    for b in range(B):
+        o, l = O.sparse_attn(q[b], kv[b], idx[b], xw[b], int(win_start[b]), sink, q_pos[b], 128)
+        assert_close(got[b], o, kind, f"sparse_attn b={b}")
+        np.testing.assert_allclose(got_lse[b], l, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("kind,H,T,ratio", [("f32", 16, 1000, 4), ("bf16", 64, 2000, 128), ("bf16", 16, 777, 16)])
+def test_dense_attn_prefill(kind, H, T, ratio):
+    N = T // ratio
+    q_pos = np.arange(T, dtype=np.int32)[None]
+    q, kv, xw, sink = _attn_case(5, 1, T, N, H, T, kind, q_pos, np.zeros(1, np.int32))
+    dt = torch.float32 if kind == "f32" else BF
+    _print("dense prefill", kind, H, T, ratio)
+    out = C.dense_compressed_attn_fwd(dev(q, dt), dev(kv, dt), dev(xw, dt), dev(np.zeros(1, np.int32), torch.int32),
+                                      dev(sink), dev(q_pos, torch.int32), ratio, 128)
+    o, _ = O.dense_attn(q[0], kv[0], xw[0], 0, sink, q_pos[0], ratio, 128)
+    assert_close(host(out)[0], o, kind, "dense prefill")
+
+
+@pytest.mark.parametrize("kind,B,N,H", [("bf16", 2, 3000, 128), ("f32", 3, 700, 16)])
+def test_dense_attn_decode(kind, B, N, H):
+    L = 128 * N + 50
+    q_pos = np.full((B, 1), L, np.int32)
+    win_start = np.full(B, L - 127, np.int32)
+    q, kv, xw, sink = _attn_case(6, B, 1, N, H, 128, kind, q_pos, win_start)
+    dt = torch.float32 if kind == "f32" else BF
+    _print("dense decode", kind, B, N, H)
+    out = C.dense_compressed_attn_fwd(dev(q, dt), dev(kv, dt), dev(xw, dt), dev(win_start, torch.int32), dev(sink),
+                                      dev(q_pos, torch.int32), 128, 128)
+    for b in range(B):
+        o, _ = O.dense_attn(q[b], kv[b], xw[b], int(win_start[b]), sink, q_pos[b], 128, 128)
+        assert_close(host(out)[b], o, kind, f"dense decode b={b}")
+
+
+def test_attention_edge_cases():
+    """window 0, no sink, a window that starts inside the supplied rows, and a
+    query with no keys and no sink (output 0)."""
+    H, N = 16, 40
+    q_pos = np.array([[0, 3, 200, 500]], np.int32)
+    q, kv, xw, sink = _attn_case(7, 1, 4, N, H, 60, "f32", q_pos, None)
+    win_start = np.array([170], np.int32)   # rows 170..229
+    idx = np.full((1, 4, 8), -1, np.int32)
+    idx[0, 2, :5] = [0, 3, 9, 30, 39]
+    idx[0, 3, :3] = [1, 2, 3]
+    for window, use_sink in ((0, False), (128, False), (5, True), (0, True)):
+        out = C.sparse_attn_fwd(dev(q), dev(kv), dev(idx, torch.int32), dev(xw), dev(win_start, torch.int32),
+                                dev(sink) if use_sink else None, dev(q_pos, torch.int32), window, 1.0)
+        o, _ = O.sparse_attn(q[0], kv[0], idx[0], xw[0], 170, sink if use_sink else np.full(H, -np.inf), q_pos[0],
+                             window)
+        o = np.nan_to_num(o, nan=0.0)      # no keys and no sink: defined as 0
+        assert_close(host(out)[0], o, "f32", f"edge window={window} sink={use_sink}")
+
+
+# ---------------------------------------------------------------- whole layer (fp32, T = 4096)
+
+def test_csa_layer_fp32_T4096():
+    """The small CSA prefill workload end to end: compress (KV and indexer
+    streams) -> indexer top-k (k = 64) -> sparse attention, float32."""
+    T, H, H_I, d_I, k = 4096, 16, 4, 64, 64
+    inp = syn.csa_prefill(1, T=T, H=H, H_I=H_I, d_I=d_I, bf16=False)
+    d = lambda n: dev(inp[n][None])
+    _print("csa layer fp32")
+    kv = C.csa_compress(d("c_a"), d("c_b"), d("z_a"), d("z_b"), 4)
+    ki = C.csa_compress(d("ci_a"), d("ci_b"), d("zi_a"), d("zi_b"), 4)
+    q_pos = torch.arange(T, dtype=torch.int32, device="cuda")[None]
+    idx, sc = C.indexer_topk(dev(inp["q_i"][None]), None, dev(inp["w"][None]), ki, None, "f32", q_pos, 4, k, d_I,
+                             want_scores=True)
+    out = C.sparse_attn_fwd(dev(inp["q"][None]), kv, idx, d("c_a"), torch.zeros(1, dtype=torch.int32, device="cuda"),
+                            dev(inp["sink"]), q_pos, 128, 1.0)
+    ref = O.csa_layer(inp, k=k)
+    assert_close(host(kv)[0], ref["kv"], "f32", "kv")
+    got_idx = host(idx)[0]
+    n_vis = O.visible_entries(np.arange(T), 4, T // 4)
+    nbad = certified_index_mismatches(got_idx, ref["idx"], ref["scores"], n_vis, k)
+    assert nbad <= 8
+    # attention on the GPU's own indices
+    o, _ = O.sparse_attn(inp["q"], ref["kv"], got_idx, inp["c_a"], 0, inp["sink"], np.arange(T), 128)
+    assert_close(host(out)[0], o, "f32", "layer output")
+
+
+def test_determinism():
+    d = syn.csa_decode(25, B=2, N=8000, H=128, H_I=64, d_I=128)
+    qc, qs = O.quant_fp8_rows(d["q_i"][:, None])
+    kc, ks = O.quant_fp8_rows(d["k_i"])
+    q_pos = dev(np.full((2, 1), 4 * 8000, np.int32), torch.int32)
+    args = (dev(qc, torch.uint8), dev(qs), dev(d["w"][:, None]), dev(kc, torch.uint8), dev(ks), "fp8", q_pos, 4, 1024,
+            128)
+    i1 = C.indexer_topk(*args)
+    i2 = C.indexer_topk(*args)
+    ws = torch.tensor([4 * 8000 - 127] * 2, dtype=torch.int32, device="cuda")
+    a = (dev(d["q"][:, None], BF), dev(d["kv"], BF), i1, dev(d["x_win"], BF), ws, dev(d["sink"]), q_pos)
+    o1 = C.sparse_attn_fwd(*a)
+    o2 = C.sparse_attn_fwd(*a)
+    assert torch.equal(i1, i2) and torch.equal(o1, o2)
