@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA/HCA attention forward on one MI355X.
+
+Headline workload (the metric's "1M-ctx decode"): one decode step of an
+alternating CSA + HCA layer pair at a 1,048,576-token context, batch 8:
+  CSA: indexer over 262,144 compressed entries with fp4 (e2m1, 1x32 E8M0)
+       keys, 64 indexer heads x 128, top-k 1024, then sparse attention over
+       the 1024 selected entries + the 128-token window + sink, 128 heads;
+  HCA: dense attention over 8,192 compressed entries + window + sink.
+A step = indexer_topk + sparse_attn_fwd + dense_compressed_attn_fwd on
+caches already resident in HBM, replayed as a HIP graph. Four independent
+copies of the caches are rotated so the 256 MB Infinity Cache cannot serve a
+step from the previous one. ``value`` = queries/s = B / step time.
+
+Also reported: the step's algorithmic HBM bytes / step time, the dominant
+kernel's roofline fraction (timed with HIP events on its own stream by the
+library's kernel timer), the CPU oracle timed on a bounded sample, and extra
+workloads (CSA decode at 262k context; prefill TFLOP/s) under "extras".
+
+Usage: python bench.py [--steps K] [--warmup W] [--extras decode4,prefill2,prefill3|none]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
+METRIC = "CSA/HCA attn queries/sec + achieved HBM TB/s at 1M-ctx decode; prefill TFLOP/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- decode workloads
+
+def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies, wid):
+    """Build the caches (copies of them) and one-step closures for a decode workload."""
+    dev = "cuda"
+    N = L // 4
+    NH = L // 128
+    bf = torch.bfloat16
+    s = 1000 * wid
+    st = {"B": B, "L": L, "N": N, "NH": NH, "H": H, "H_I": H_I, "d_I": d_I, "k": k, "fmt": fmt}
+    # keys: generate once in float32 on the device, quantise with the library
+    ki32 = syn.normal_device(s + 2, (B, N, d_I), dev)
+    codes, scales = C.csa_quantize_rows(ki32, fmt)
+    st["ki_host_rows"] = ki32[: min(B, 8)].cpu()       # for the CPU baseline sample
+    del ki32
+    kv = syn.normal_device(s + 1, (B, N, 128), dev, bf)
+    st["kv_host"] = kv[: min(B, 8)].float().cpu()
+    st["codes"], st["scales"], st["kv"] = [codes], [scales], [kv]
+    for _ in range(copies - 1):
+        st["codes"].append(codes.clone())
+        st["scales"].append(scales.clone())
+        st["kv"].append(kv.clone())
+    st["x_win"] = syn.normal_device(s + 3, (B, 128, 128), dev, bf)
+    st["q"] = syn.normal_device(s + 4, (B, 1, H, 128), dev, bf, scale=1 / np.sqrt(128))
+    qi32 = syn.normal_device(s + 5, (B, 1, H_I, d_I), dev)
+    st["qi32"] = qi32
+    st["qi"], st["qs"] = C.csa_quantize_rows(qi32, fmt)
+    st["w"] = syn.uniform_device(s + 6, (B, 1, H_I), dev)
+    st["sink"] = syn.normal_device(s + 7, (H,), dev)
+    st["q_pos"] = torch.full((B, 1), L, dtype=torch.int32, device=dev)
+    st["win_start"] = torch.full((B,), L - 127, dtype=torch.int32, device=dev)
+    st["idx"] = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
+    st["out"] = torch.empty(B, 1, H, 128, dtype=bf, device=dev)
+    st["ws_idx"] = torch.empty(C.indexer_topk_workspace_size(B, 1, N, H_I, d_I, k, fmt), dtype=torch.uint8, device=dev)
+    st["ws_sp"] = torch.empty(max(1, C.sparse_attn_workspace_size(B, 1, H, 128, k, 128)), dtype=torch.uint8, device=dev)
+    bytes_idx = B * N * (d_I // 2 + d_I // 32 if fmt == "fp4" else d_I + 4) + B * H_I * (d_I + 8)
+    bytes_sp = B * (k + 128) * 256 + 2 * B * H * 256 + B * k * 4
+    st["bytes_index_score"] = bytes_idx
+    st["bytes"] = bytes_idx + bytes_sp
+    if hca:
+        kvh = syn.normal_device(s + 11, (B, NH, 128), dev, bf)
+        st["kvh_host"] = kvh[: min(B, 8)].float().cpu()
+        st["kvh"] = [kvh] + [kvh.clone() for _ in range(copies - 1)]
+        st["xh"] = syn.normal_device(s + 12, (B, 128, 128), dev, bf)
+        st["qh"] = syn.normal_device(s + 13, (B, 1, H, 128), dev, bf, scale=1 / np.sqrt(128))
+        st["sinkh"] = syn.normal_device(s + 14, (H,), dev)
+        st["outh"] = torch.empty(B, 1, H, 128, dtype=bf, device=dev)
+        st["ws_dn"] = torch.empty(max(1, C.dense_attn_workspace_size(B, 1, NH, H, 128, 128)), dtype=torch.uint8,
+                                  device=dev)
+        st["bytes"] += B * (NH + 128) * 256 + 2 * B * H * 256
+
+    def step(c):
+        C.indexer_topk(st["qi"], st["qs"], st["w"], st["codes"][c], st["scales"][c], fmt, st["q_pos"], 4, k, d_I,
+                       ws=st["ws_idx"], idx_out=st["idx"])
+        C.sparse_attn_fwd(st["q"], st["kv"][c], st["idx"], st["x_win"], st["win_start"], st["sink"], st["q_pos"],
+                          128, 1.0, ws=st["ws_sp"], out=st["out"])
+        if hca:
+            C.dense_compressed_attn_fwd(st["qh"], st["kvh"][c], st["xh"], st["win_start"], st["sinkh"],
+                                        st["q_pos"], 128, 128, 1.0, ws=st["ws_dn"], out=st["outh"])
+    st["step"] = step
+    st["name"] = name
+    st["hca"] = hca
+    return st
+
+
+def time_graphs(torch, st, copies, steps, warmup, use_graph=True):
+    """Capture one graph per cache copy; replay round-robin. Returns ms/step."""
+    step = st["step"]
+    for c in range(copies):
+        step(c)
+    torch.cuda.synchronize()
+    if use_graph:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in range(copies):
+                step(c)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        run = lambda i: graphs[i % copies].replay()
+    else:
+        run = lambda i: step(i % copies)
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def kernel_times(torch, C, st, copies, steps, kernel):
+    """Average duration of one library kernel over `steps` eager steps (HIP events
+    recorded by the library on the stream the kernel runs on)."""
+    C.kernel_timer_start(kernel, steps)
+    for i in range(steps):
+        st["step"](i % copies)
+    torch.cuda.synchronize()
+    t = C.kernel_timer_read(steps)
+    return float(np.mean(t)) if t else None
+
+
+def cpu_baseline_decode(O, st, seconds):
+    """The oracle on the host: whole decode step for as many sequences as fit in
+    about `seconds` of CPU time (at least one), inputs prepared outside the timer."""
+    import torch
+    B, N, NH, k, fmt = st["B"], st["N"], st["NH"], st["k"], st["fmt"]
+    L = st["L"]
+    quant, deq = ((O.quant_mxfp4_rows, O.dequant_mxfp4_rows) if fmt == "fp4" else (O.quant_fp8_rows, O.dequant_fp8_rows))
+    qi = st["qi32"].cpu().numpy()
+    w = st["w"].cpu().numpy()
+    q = st["q"].float().cpu().numpy()
+    xw = st["x_win"].float().cpu().numpy()
+    sink = st["sink"].cpu().numpy()
+    if st["hca"]:
+        qh = st["qh"].float().cpu().numpy()
+        xh = st["xh"].float().cpu().numpy()
+        sinkh = st["sinkh"].cpu().numpy()
+    done, spent = 0, 0.0
+    nsample = st["ki_host_rows"].shape[0]
+    for b in range(nsample):
+        kd = deq(*quant(st["ki_host_rows"][b].numpy()))
+        qd = deq(*quant(qi[b]))
+        kvb = st["kv_host"][b].numpy()
+        kvh = st["kvh_host"][b].numpy() if st["hca"] else None
+        t0 = time.perf_counter()
+        s = O.indexer_scores(qd, w[b], kd, [L], 4)
+        idx = O.topk_select(s, O.visible_entries([L], 4, N), k)
+        O.sparse_attn(q[b], kvb, idx, xw[b], L - 127, sink, [L], 128)
+        if st["hca"]:
+            O.dense_attn(qh[b], kvh, xh[b], L - 127, sinkh, [L], 128, 128)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= seconds:
+            break
+    return done, spent
+
+
+def run_decode(torch, C, syn, O, args, which):
+    if which == "pair1m":
+        st = decode_workload(torch, C, syn, "csa_hca_decode_pair_1m_ctx", B=8, L=1 << 20, H=128, H_I=64, d_I=128,
+                             k=1024, fmt="fp4", hca=True, copies=args.copies, wid=5)
+    else:
+        st = decode_workload(torch, C, syn, "csa_decode_262k_ctx", B=32, L=1 << 18, H=128, H_I=64, d_I=128,
+                             k=1024, fmt="fp8", hca=False, copies=args.copies, wid=4)
+    torch.cuda.synchronize()
+    log(f"[bench] {st['name']}: setup done")
+    ms, wall = time_graphs(torch, st, args.copies, args.steps, args.warmup, use_graph=not args.eager)
+    log(f"[bench] {st['name']}: {ms * 1e3:.1f} us/step (graph), wall {wall * 1e3:.1f} us/step")
+    kt = {}
+    for kname in ("index_score", "topk", "sparse_attn", "attn_merge", "dense_attn"):
+        if kname == "dense_attn" and not st["hca"]:
+            continue
+        kt[kname] = kernel_times(torch, C, st, args.copies, args.steps, kname)
+    log(f"[bench] {st['name']}: kernel us {({k_: (None if v is None else round(v * 1e3, 1)) for k_, v in kt.items()})}")
+    return st, ms, wall, kt
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
+    ap.add_argument("--extras", default="decode4", help="comma list of decode4,prefill2,prefill3 or 'none'")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
+              "this build. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import csa_synth as syn
+    import long_context_attention_csa_amd as C
+    from oracle import csa_oracle as O   # CPU-baseline leg only
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    st, ms, wall, kt = run_decode(torch, C, syn, O, args, "pair1m")
+    B = st["B"]
+    qps = B / (ms * 1e-3)
+    dom = kt["index_score"]
+    achieved = st["bytes_index_score"] / (dom * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16+fp4",
+        "data": "synthetic",
+        "config": {"workload": st["name"], "batch": B, "context": st["L"], "csa_entries": st["N"],
+                   "hca_entries": st["NH"], "heads": st["H"], "head_dim": 128, "index_heads": st["H_I"],
+                   "index_dim": st["d_I"], "index_keys": "fp4 e2m1 + E8M0 per 32", "top_k": st["k"],
+                   "window": 128, "kv": "bf16", "cache_copies": args.copies,
+                   "timing": "eager" if args.eager else "hip graph replay"},
+        "hbm_tb_s": round(st["bytes"] / (ms * 1e-3) / 1e12, 3),
+        "step_bytes": st["bytes"],
+        "wall_ms_per_step": round(wall, 5),
+        "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in kt.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_index_score (fp4 keys)", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": st["bytes_index_score"]},
+    }
+    if not args.no_cpu_baseline:
+        done, spent = cpu_baseline_decode(O, st, args.cpu_seconds)
+        result["cpu_baseline"] = {"value": round(done / spent, 3), "unit": "queries/s",
+                                  "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                                  "sample": f"{done} of {B} sequences of one decode step (whole CSA+HCA pair, "
+                                            f"float64 NumPy), {spent:.1f} s"}
+    extras = {}
+    wanted = [] if args.extras == "none" else [x for x in args.extras.split(",") if x]
+    del st
+    torch.cuda.empty_cache()
+    if "decode4" in wanted:
+        st4, ms4, wall4, kt4 = run_decode(torch, C, syn, O, args, "decode4")
+        extras["csa_decode_262k_ctx"] = {
+            "batch": st4["B"], "queries_per_s": round(st4["B"] / (ms4 * 1e-3), 1), "ms_per_step": round(ms4, 5),
+            "hbm_tb_s": round(st4["bytes"] / (ms4 * 1e-3) / 1e12, 3),
+            "index_score_gb_s": round(st4["bytes_index_score"] / (kt4["index_score"] * 1e-3) / 1e9, 1),
+            "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in kt4.items()}}
+        del st4
+        torch.cuda.empty_cache()
+    if extras:
+        result["extras"] = extras
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -152,3 +152,26 @@ def hca_decode(wid: int, B: int, N: int, H: int, T_win: int = 128, d: int = 128)
         "q": normal(s + 13, (B, H, d), scale=1.0 / np.sqrt(d), bf16=True),
         "sink": normal(s + 14, (H,)),
     }
+
+
+# ---------------------------------------------------------------------------
+# Device-side generation for the benchmark's large tensors (hundreds of MB):
+# torch's seeded Philox generator on the GPU. Both the HIP path and the
+# oracle's timed sample read the same tensors (the oracle gets host copies).
+# ---------------------------------------------------------------------------
+
+def normal_device(seed: int, shape, device, dtype=None, scale: float = 1.0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x if dtype is None else x.to(dtype)
+
+
+def uniform_device(seed: int, shape, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.rand(*shape, generator=g, device=device, dtype=torch.float32)

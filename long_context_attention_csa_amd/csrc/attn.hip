@@ -32,12 +32,19 @@ constexpr int kD = 128;            // head dim
 template <typename T> struct AttnTypes;
 template <> struct AttnTypes<uint16_t> {
   static constexpr int KP = kD + 8;     // row pitch of the row-major tile (elements)
-  static constexpr int VP = kKT + 4;    // row pitch of the transposed tile
 };
 template <> struct AttnTypes<float> {
   static constexpr int KP = kD + 4;
-  static constexpr int VP = kKT + 4;
 };
+
+// Position of key `key` of value-row d in the transposed tile. Groups of 4
+// consecutive keys stay together; the group index is XOR-swizzled by a
+// function of d so that both the packed 4-key stores of the gather and the
+// 4-key fragment loads of the P*V product spread over all LDS banks.
+__device__ __forceinline__ int vt_pos(int d, int key) {
+  const int h = (d & 15) ^ ((d >> 3) & 15);
+  return d * kKT + (key ^ (4 * h));
+}
 
 // 8 consecutive K-elements of one lane's MFMA operand.
 template <typename T> struct Frag;
@@ -46,14 +53,14 @@ template <> struct Frag<uint16_t> {
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const i32x4*>(p); }
   __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<i32x4*>(p) = v; }
   __device__ __forceinline__ void zero() { v = i32x4{0, 0, 0, 0}; }
-  __device__ __forceinline__ uint16_t elem(int j) const {
+  __device__ __forceinline__ uint32_t elem(int j) const {
     const uint32_t w = (uint32_t)v[j >> 1];
-    return (uint16_t)((j & 1) ? (w >> 16) : (w & 0xffffu));
+    return (j & 1) ? (w >> 16) : (w & 0xffffu);
   }
-  // keys {0..3} from p, {4..7} from p + 16
-  __device__ __forceinline__ void load_split(const uint16_t* p) {
+  // keys {0..3} from p, {4..7} from q
+  __device__ __forceinline__ void load_split(const uint16_t* p, const uint16_t* q) {
     const uint2 a = *reinterpret_cast<const uint2*>(p);
-    const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+    const uint2 b = *reinterpret_cast<const uint2*>(q);
     v = i32x4{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
   }
 };
@@ -73,12 +80,20 @@ template <> struct Frag<float> {
     for (int j = 0; j < 8; ++j) v[j] = 0.f;
   }
   __device__ __forceinline__ float elem(int j) const { return v[j]; }
-  __device__ __forceinline__ void load_split(const float* p) {
+  __device__ __forceinline__ void load_split(const float* p, const float* q) {
     const float4 a = *reinterpret_cast<const float4*>(p);
-    const float4 b = *reinterpret_cast<const float4*>(p + 16);
+    const float4 b = *reinterpret_cast<const float4*>(q);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
 };
+
+// Store element e of four consecutive key rows (f[0..3]) as 4 packed keys.
+__device__ __forceinline__ void store_vt4(uint16_t* p, const Frag<uint16_t>* f, int e) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(f[0].elem(e) | (f[1].elem(e) << 16), f[2].elem(e) | (f[3].elem(e) << 16));
+}
+__device__ __forceinline__ void store_vt4(float* p, const Frag<float>* f, int e) {
+  *reinterpret_cast<float4*>(p) = make_float4(f[0].elem(e), f[1].elem(e), f[2].elem(e), f[3].elem(e));
+}
 
 // acc += A(16 x 32) * B(32 x 16) with the 8 K-elements per lane of each fragment.
 __device__ __forceinline__ f32x4 mma8(const Frag<uint16_t>& a, const Frag<uint16_t>& b, f32x4 acc) {
@@ -91,17 +106,22 @@ __device__ __forceinline__ f32x4 mma8(const Frag<float>& a, const Frag<float>& b
   return acc;
 }
 
-template <typename T, bool SPARSE, int NW>
+// One block: one query row, NW waves x HPW blocks of 16 heads, one key split.
+template <typename T, bool SPARSE, int NW, int HPW>
 __global__ __launch_bounds__(NW * 64) void k_attn(
     const T* __restrict__ q, const T* __restrict__ kv, const int32_t* __restrict__ idx, const T* __restrict__ x_win,
     const int32_t* __restrict__ win_start, const float* __restrict__ sink, const int32_t* __restrict__ q_pos,
     int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale, int S,
     T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int KP = AttnTypes<T>::KP, VP = AttnTypes<T>::VP;
+  constexpr int KP = AttnTypes<T>::KP;
   constexpr int NT = NW * 64;
+  constexpr int PAIRS = 256 / NT;            // (4-row quad, 16-byte column) pairs per thread per tile
+  constexpr int TPS = (sizeof(T) == 2 ? 2 : 1) * (NT >= 128 ? 1 : 1);   // tiles per super-tile
+  constexpr int SUPER = TPS * kKT;
   __shared__ __align__(16) T Kt[kKT * KP];
-  __shared__ __align__(16) T Vt[kD * VP];
+  __shared__ __align__(16) T Vt[kD * kKT];
   __shared__ int valid[kKT];
+  __shared__ int sidx[SUPER];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, col = lane & 15;
@@ -122,176 +142,252 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
   const int64_t kbeg = (int64_t)sp * chunk;
   const int64_t kend = (kbeg + chunk) < nk ? (kbeg + chunk) : nk;
 
-  const int head = hg * (NW * 16) + wv * 16 + col;
-  // Q^T fragments (B operand of S^T): lane holds q[head, 32ks + 8g .. +8].
-  Frag<T> qf[kD / 32];
-  {
-    const T* qrow = q + (r * H + head) * kD;
+  // heads of this lane: h0 + 16 * hb + col
+  const int h0 = hg * (NW * 16 * HPW) + wv * 16 * HPW;
+  Frag<T> qf[HPW][kD / 32];
 #pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) qf[ks].load(qrow + 32 * ks + 8 * g);
+  for (int hb = 0; hb < HPW; ++hb) {
+    const T* qrow = q + (r * H + h0 + 16 * hb + col) * kD;
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) qf[hb][ks].load(qrow + 32 * ks + 8 * g);
   }
   const bool has_sink = (sink != nullptr) && sp == 0;
-  float m = has_sink ? sink[head] : -INFINITY;
-  float lsum = (has_sink && g == 0) ? 1.f : 0.f;
-  f32x4 O[kD / 16];
+  float m[HPW], lsum[HPW];
+  f32x4 O[HPW][kD / 16];
 #pragma unroll
-  for (int db = 0; db < kD / 16; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t t0 = kbeg; t0 < kend; t0 += kKT) {
-    const int nt = (int)((kend - t0) < kKT ? (kend - t0) : kKT);
-    // ---- gather: 64 rows x 16 pieces of 8 elements
-    for (int c = tid; c < kKT * (kD / 8); c += NT) {
-      const int kr = c >> 4, cc = c & 15;
-      const int64_t i = t0 + kr;
-      const T* src = nullptr;
-      if (kr < nt) {
-        if (i < n_sel) {
-          const int64_t e = SPARSE ? (int64_t)idx[r * k + i] : i;
-          if (e >= 0 && e < N) src = kv + (b * N + e) * kD;
-        } else {
-          src = x_win + (b * T_win + (lo + (i - n_sel) - w0)) * kD;
-        }
-      }
-      Frag<T> v;
-      if (src) v.load(src + 8 * cc);
-      else v.zero();
-      v.store(&Kt[kr * KP + 8 * cc]);
+  for (int hb = 0; hb < HPW; ++hb) {
+    m[hb] = has_sink ? sink[h0 + 16 * hb + col] : -INFINITY;
+    lsum[hb] = (has_sink && g == 0) ? 1.f : 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(8 * cc + j) * VP + kr] = v.elem(j);
-      if (cc == 0) valid[kr] = src != nullptr;
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T for 4 blocks of 16 keys
-    float s[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const T* krow = &Kt[(16 * kb + col) * KP + 8 * g];
-#pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        Frag<T> a;
-        a.load(krow + 32 * ks);
-        acc = mma8(a, qf[ks], acc);
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int key = 16 * kb + 4 * g + rr;
-        s[kb][rr] = (key < nt && valid[key]) ? acc[rr] * scale : -INFINITY;
-      }
-    }
-    // ---- online softmax (per head = per column)
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) tmax = fmaxf(tmax, s[kb][rr]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(m, tmax);
-    const bool live = mnew != -INFINITY;
-    const float alpha = live ? __expf(m - mnew) : 1.f;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float pv = live ? __expf(s[kb][rr] - mnew) : 0.f;
-        s[kb][rr] = pv;
-        psum += pv;
-      }
-    lsum = fmaf(lsum, alpha, psum);
-    m = mnew;
-#pragma unroll
-    for (int db = 0; db < kD / 16; ++db) O[db] *= alpha;
-
-    // ---- O^T += V^T P^T, two groups of 32 keys. K-slot t of lane group g is
-    // key 4g+t (t < 4) or 16+4g+(t-4) (t >= 4) of the group.
-#pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      Frag<T> pf;
-      if constexpr (sizeof(T) == 2) {
-        pf.v[0] = (int)pack_bf16x2(s[2 * grp][0], s[2 * grp][1]);
-        pf.v[1] = (int)pack_bf16x2(s[2 * grp][2], s[2 * grp][3]);
-        pf.v[2] = (int)pack_bf16x2(s[2 * grp + 1][0], s[2 * grp + 1][1]);
-        pf.v[3] = (int)pack_bf16x2(s[2 * grp + 1][2], s[2 * grp + 1][3]);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pf.v[t] = s[2 * grp + (t >> 2)][t & 3];
-      }
-#pragma unroll
-      for (int db = 0; db < kD / 16; ++db) {
-        Frag<T> va;
-        va.load_split(&Vt[(16 * db + col) * VP + 32 * grp + 4 * g]);
-        O[db] = mma8(va, pf, O[db]);
-      }
-    }
-    __syncthreads();
+    for (int db = 0; db < kD / 16; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
-  if (S == 1) {
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    T* orow = out + (r * H + head) * kD;
-#pragma unroll
-    for (int db = 0; db < kD / 16; ++db) {
-      const float v[4] = {O[db][0] * inv, O[db][1] * inv, O[db][2] * inv, O[db][3] * inv};
-      Elem<T>::store4(orow + 16 * db + 4 * g, v);
+  // Keys are walked in super-tiles: every gather of a super-tile is issued
+  // before its first tile is computed (one round of memory latency per
+  // super-tile). A thread gathers, per tile, PAIRS quads of 4 consecutive key
+  // rows at one 16-byte column, so it can store V^T as packed 4-key groups.
+  for (int64_t s0 = kbeg; s0 < kend; s0 += SUPER) {
+    const int ns = (int)((kend - s0) < SUPER ? (kend - s0) : SUPER);
+    if (SPARSE) {
+      for (int i = tid; i < SUPER; i += NT) {
+        const int64_t ki = s0 + i;
+        sidx[i] = (i < ns && ki < n_sel) ? idx[r * k + ki] : -1;
+      }
+      __syncthreads();
     }
-    if (lse && g == 0) lse[r * H + head] = lsum > 0.f ? m + __logf(lsum) : -INFINITY;
-  } else {
-    const int64_t pi = (r * H + head) * S + sp;
-    float* po = part_o + pi * kD;
+    Frag<T> buf[TPS][PAIRS][4];
+    bool okb[TPS][PAIRS][4];
 #pragma unroll
-    for (int db = 0; db < kD / 16; ++db)
-      *reinterpret_cast<float4*>(po + 16 * db + 4 * g) = make_float4(O[db][0], O[db][1], O[db][2], O[db][3]);
-    if (g == 0) {
-      part_ml[2 * pi] = m;
-      part_ml[2 * pi + 1] = lsum;
+    for (int tt = 0; tt < TPS; ++tt)
+#pragma unroll
+      for (int pp = 0; pp < PAIRS; ++pp) {
+        const int pr = tid + pp * NT;
+        const int mq = pr >> 4, cc = pr & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kr = tt * kKT + 4 * mq + i;        // key within the super-tile
+          const int64_t ki = s0 + kr;
+          const T* src = nullptr;
+          if (kr < ns) {
+            if (ki < n_sel) {
+              const int64_t e = SPARSE ? (int64_t)sidx[kr] : ki;
+              if (e >= 0 && e < N) src = kv + (b * N + e) * kD;
+            } else {
+              src = x_win + (b * T_win + (lo + (ki - n_sel) - w0)) * kD;
+            }
+          }
+          okb[tt][pp][i] = src != nullptr;
+          if (src) buf[tt][pp][i].load(src + 8 * cc);
+          else buf[tt][pp][i].zero();
+        }
+      }
+#pragma unroll
+    for (int tt = 0; tt < TPS; ++tt) {
+      if (tt * kKT >= ns) break;
+      const int nt = (ns - tt * kKT) < kKT ? (ns - tt * kKT) : kKT;
+#pragma unroll
+      for (int pp = 0; pp < PAIRS; ++pp) {
+        const int pr = tid + pp * NT;
+        const int mq = pr >> 4, cc = pr & 15;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf[tt][pp][i].store(&Kt[(4 * mq + i) * KP + 8 * cc]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) store_vt4(&Vt[vt_pos(8 * cc + e, 4 * mq)], buf[tt][pp], e);
+        if (cc == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) valid[4 * mq + i] = okb[tt][pp][i];
+        }
+      }
+      __syncthreads();
+
+      // ---- S^T = K Q^T for 4 blocks of 16 keys; each K fragment feeds HPW head blocks
+      float s[HPW][4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4 acc[HPW];
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const T* krow = &Kt[(16 * kb + col) * KP + 8 * g];
+#pragma unroll
+        for (int ks = 0; ks < kD / 32; ++ks) {
+          Frag<T> a;
+          a.load(krow + 32 * ks);
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) acc[hb] = mma8(a, qf[hb][ks], acc[hb]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int key = 16 * kb + 4 * g + rr;
+          const bool ok = key < nt && valid[key];
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = ok ? acc[hb][rr] * scale : -INFINITY;
+        }
+      }
+      // ---- online softmax (per head = per column)
+#pragma unroll
+      for (int hb = 0; hb < HPW; ++hb) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) tmax = fmaxf(tmax, s[hb][kb][rr]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mnew = fmaxf(m[hb], tmax);
+        const bool live = mnew != -INFINITY;
+        const float alpha = live ? __expf(m[hb] - mnew) : 1.f;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float pv = live ? __expf(s[hb][kb][rr] - mnew) : 0.f;
+            s[hb][kb][rr] = pv;
+            psum += pv;
+          }
+        lsum[hb] = fmaf(lsum[hb], alpha, psum);
+        m[hb] = mnew;
+#pragma unroll
+        for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
+      }
+
+      // ---- O^T += V^T P^T, two groups of 32 keys. K-slot t of lane group g is
+      // key 4g+t (t < 4) or 16+4g+(t-4) (t >= 4) of the group.
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp) {
+        Frag<T> pf[HPW];
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+          if constexpr (sizeof(T) == 2) {
+            pf[hb].v[0] = (int)pack_bf16x2(s[hb][2 * grp][0], s[hb][2 * grp][1]);
+            pf[hb].v[1] = (int)pack_bf16x2(s[hb][2 * grp][2], s[hb][2 * grp][3]);
+            pf[hb].v[2] = (int)pack_bf16x2(s[hb][2 * grp + 1][0], s[hb][2 * grp + 1][1]);
+            pf[hb].v[3] = (int)pack_bf16x2(s[hb][2 * grp + 1][2], s[hb][2 * grp + 1][3]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) pf[hb].v[t] = s[hb][2 * grp + (t >> 2)][t & 3];
+          }
+        }
+#pragma unroll
+        for (int db = 0; db < kD / 16; ++db) {
+          const int d = 16 * db + col;
+          Frag<T> va;
+          va.load_split(&Vt[vt_pos(d, 32 * grp + 4 * g)], &Vt[vt_pos(d, 32 * grp + 16 + 4 * g)]);
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) O[hb][db] = mma8(va, pf[hb], O[hb][db]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) {
+    float l = lsum[hb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int head = h0 + 16 * hb + col;
+    if (S == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      T* orow = out + (r * H + head) * kD;
+#pragma unroll
+      for (int db = 0; db < kD / 16; ++db) {
+        const float v[4] = {O[hb][db][0] * inv, O[hb][db][1] * inv, O[hb][db][2] * inv, O[hb][db][3] * inv};
+        Elem<T>::store4(orow + 16 * db + 4 * g, v);
+      }
+      if (lse && g == 0) lse[r * H + head] = l > 0.f ? m[hb] + __logf(l) : -INFINITY;
+    } else {
+      const int64_t pi = (r * H + head) * S + sp;
+      float* po = part_o + pi * kD;
+#pragma unroll
+      for (int db = 0; db < kD / 16; ++db)
+        *reinterpret_cast<float4*>(po + 16 * db + 4 * g) = make_float4(O[hb][db][0], O[hb][db][1], O[hb][db][2], O[hb][db][3]);
+      if (g == 0) {
+        part_ml[2 * pi] = m[hb];
+        part_ml[2 * pi + 1] = l;
+      }
     }
   }
 }
 
 // Merge of S partial results per (row, head), in split order. 256 threads =
-// 2 (row, head) pairs x 128 channels.
+// 8 (row, head) pairs x 32 lanes x 4 channels; loads are unrolled so the S
+// partials of a pair are in flight together.
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                                                     int64_t RH, int S, T* __restrict__ out, float* __restrict__ lse) {
-  const int64_t rh = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
-  const int d = threadIdx.x & 127;
+  const int64_t rh = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int d0 = (threadIdx.x & 31) * 4;
   if (rh >= RH) return;
+  const float* ml = part_ml + 2 * rh * S;
   float mx = -INFINITY;
-  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, part_ml[2 * (rh * S + sp)]);
-  float l = 0.f, o = 0.f;
+#pragma unroll 8
+  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, ml[2 * sp]);
+  float l = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
   if (mx != -INFINITY) {
+#pragma unroll 8
     for (int sp = 0; sp < S; ++sp) {
-      const float f = __expf(part_ml[2 * (rh * S + sp)] - mx);
-      l = fmaf(part_ml[2 * (rh * S + sp) + 1], f, l);
-      o = fmaf(part_o[(rh * S + sp) * kD + d], f, o);
+      const float f = __expf(ml[2 * sp] - mx);
+      l = fmaf(ml[2 * sp + 1], f, l);
+      const float4 v = *reinterpret_cast<const float4*>(part_o + (rh * S + sp) * kD + d0);
+      o[0] = fmaf(v.x, f, o[0]); o[1] = fmaf(v.y, f, o[1]); o[2] = fmaf(v.z, f, o[2]); o[3] = fmaf(v.w, f, o[3]);
     }
   }
-  const float v = l > 0.f ? o / l : 0.f;
-  if constexpr (sizeof(T) == 4) out[rh * kD + d] = v;
-  else out[rh * kD + d] = f32_to_bf16(v);
-  if (lse && d == 0) lse[rh] = l > 0.f ? mx + __logf(l) : -INFINITY;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  Elem<T>::store4(out + rh * kD + d0, v);
+  if (lse && d0 == 0) lse[rh] = l > 0.f ? mx + __logf(l) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ host side
 
-static int pick_nw(int H) {
+// Waves per block and 16-head blocks per wave: 2 head blocks per wave when
+// possible (each LDS fragment then feeds two MFMAs), up to 4 waves.
+struct AttnShape { int nw, hpw; };
+static AttnShape pick_shape(int H) {
   const int hb = H / 16;
-  return (hb % 4 == 0) ? 4 : (hb % 2 == 0 ? 2 : 1);
+  const int hpw = (hb % 2 == 0) ? 2 : 1;
+  const int waves = hb / hpw;
+  const int nw = (waves % 4 == 0) ? 4 : (waves % 2 == 0 ? 2 : 1);
+  return {nw, hpw};
 }
 
+// Key splits per (row, head group): a fixed function of the shapes, so the
+// merge order (and the result) never depends on timing. Enough splits that a
+// split holds at most one bf16 super-tile of keys (one round of gathers), and
+// more while the grid is small, down to 128 keys per split.
 int attn_splits(int64_t rows, int H, int64_t nk_max) {
-  const int nw = pick_nw(H);
-  const int64_t base = rows * (H / (16 * nw));
+  const AttnShape sh = pick_shape(H);
+  const int64_t base = rows * (H / (16 * sh.nw * sh.hpw));
   if (base >= 256) return 1;
-  int64_t s = cdiv(512, base);
+  const int64_t super_keys = 128;   // bf16 super-tile size
+  int64_t s = cdiv(nk_max, super_keys);
+  const int64_t fill = cdiv(256, base);
   const int64_t by_keys = nk_max / 128 > 1 ? nk_max / 128 : 1;
-  if (s > by_keys) s = by_keys;
-  if (s > 64) s = 64;
+  const int64_t more = fill < by_keys ? fill : by_keys;
+  if (s < more) s = more;
+  if (s > 128) s = 128;
   return (int)(s < 1 ? 1 : s);
 }
 
@@ -301,24 +397,34 @@ size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max) {
   return (size_t)rows * H * S * (kD + 2) * 4;
 }
 
-template <typename T, bool SPARSE, int NW>
+template <typename T, bool SPARSE, int NW, int HPW>
 static void launch_attn_t(dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                           const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                           int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
                           int S, void* out, float* lse, float* po, float* pml) {
-  k_attn<T, SPARSE, NW><<<grid, NW * 64, 0, st>>>((const T*)q, (const T*)kv, idx, (const T*)x_win, win_start, sink,
-                                                  q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, (T*)out, lse,
-                                                  po, pml);
+  k_attn<T, SPARSE, NW, HPW><<<grid, NW * 64, 0, st>>>((const T*)q, (const T*)kv, idx, (const T*)x_win, win_start,
+                                                       sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S,
+                                                       (T*)out, lse, po, pml);
 }
 
 template <typename T, bool SPARSE>
-static void launch_attn_nw(int nw, dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
+static void launch_attn_sh(AttnShape sh, dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                            const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                            int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
                            int S, void* out, float* lse, float* po, float* pml) {
-  if (nw == 4) launch_attn_t<T, SPARSE, 4>(grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
-  else if (nw == 2) launch_attn_t<T, SPARSE, 2>(grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
-  else launch_attn_t<T, SPARSE, 1>(grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
+#define CSA_ATTN_CASE(NW_, HPW_)                                                                               \
+  if (sh.nw == NW_ && sh.hpw == HPW_) {                                                                        \
+    launch_attn_t<T, SPARSE, NW_, HPW_>(grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, \
+                                        k, window, ratio, scale, S, out, lse, po, pml);                        \
+    return;                                                                                                    \
+  }
+  CSA_ATTN_CASE(4, 2)
+  CSA_ATTN_CASE(2, 2)
+  CSA_ATTN_CASE(1, 2)
+  CSA_ATTN_CASE(4, 1)
+  CSA_ATTN_CASE(2, 1)
+  CSA_ATTN_CASE(1, 1)
+#undef CSA_ATTN_CASE
 }
 
 hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void* kv, const int32_t* idx,
@@ -327,27 +433,27 @@ hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void*
                             float scale, void* out, float* lse, void* ws, int64_t nk_max, hipStream_t st) {
   const int64_t rows = B * Tq;
   if (rows == 0) return hipSuccess;
-  const int nw = pick_nw(H);
+  const AttnShape sh = pick_shape(H);
   const int S = attn_splits(rows, H, nk_max);
   float* po = reinterpret_cast<float*>(ws);
   float* pml = po ? po + (size_t)rows * H * S * kD : nullptr;
-  const dim3 grid((unsigned)rows, (unsigned)((H / (16 * nw)) * S));
+  const dim3 grid((unsigned)rows, (unsigned)((H / (16 * sh.nw * sh.hpw)) * S));
   const int kid = sparse ? CSA_KID_SPARSE_ATTN : CSA_KID_DENSE_ATTN;
   timer_before(kid, st);
   if (t == CSA_BF16) {
-    if (sparse) launch_attn_nw<uint16_t, true>(nw, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
-    else launch_attn_nw<uint16_t, false>(nw, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
+    if (sparse) launch_attn_sh<uint16_t, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
+    else launch_attn_sh<uint16_t, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
   } else {
-    if (sparse) launch_attn_nw<float, true>(nw, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
-    else launch_attn_nw<float, false>(nw, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
+    if (sparse) launch_attn_sh<float, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
+    else launch_attn_sh<float, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
   }
   hipError_t e = hipGetLastError();
   timer_after(kid, st);
   if (e != hipSuccess || S == 1) return e;
   const int64_t RH = rows * H;
   timer_before(CSA_KID_ATTN_MERGE, st);
-  if (t == CSA_BF16) k_attn_merge<uint16_t><<<dim3((unsigned)cdiv(RH, 2)), 256, 0, st>>>(po, pml, RH, S, (uint16_t*)out, lse);
-  else k_attn_merge<float><<<dim3((unsigned)cdiv(RH, 2)), 256, 0, st>>>(po, pml, RH, S, (float*)out, lse);
+  if (t == CSA_BF16) k_attn_merge<uint16_t><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(po, pml, RH, S, (uint16_t*)out, lse);
+  else k_attn_merge<float><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(po, pml, RH, S, (float*)out, lse);
   e = hipGetLastError();
   timer_after(CSA_KID_ATTN_MERGE, st);
   return e;

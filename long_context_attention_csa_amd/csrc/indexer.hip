@@ -22,12 +22,19 @@
 // lanes of one load cover 16 whole key rows, i.e. the scan is one coalesced
 // stream. Up to 4 consecutive queries of one sequence share each key load.
 //
-// Select stage (k_topk_rows). One block per query row: a 13-bit histogram of
-// the order-preserving score keys locates the bucket holding the k-th largest
-// score; rows above it are taken, the bucket's members are resolved by a radix
-// select on 64-bit (score key, inverted index) composites, which realises the
-// total order "score descending, index ascending" exactly; the chosen indices
-// are sorted ascending with a bitonic network. Deterministic by construction.
+// Select stage (k_topk_select, one block per query row). The score kernel
+// also writes the maximum of every group of 16 consecutive entries. The k-th
+// largest group maximum tau is a lower bound of the k-th largest score (at
+// least k groups hold an entry >= tau), so the top-k lies among the entries
+// >= tau, which are read only from groups whose maximum is >= tau. On random
+// scores that is about k candidates out of n. They are resolved exactly by a
+// radix select on 64-bit (order-preserving score key, inverted index)
+// composites, which realises the total order "score descending, index
+// ascending"; each chosen index is written at its rank among the chosen.
+// Rows with few groups per selected entry, and candidate sets too large for
+// LDS (heavy ties), take the full-row path: a 13-bit histogram over all
+// scores, then the same exact radix select on the boundary bucket.
+// Deterministic by construction (atomics only build sets, never orders).
 #include "common.hpp"
 
 namespace csa {
@@ -35,8 +42,10 @@ namespace csa {
 constexpr int kTopkThreads = 512;
 constexpr int kHistBits = 13;
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kCandCap = kHistBins / 2;   // u64 candidates aliased onto the histogram
+constexpr int kCandCap = 8192;            // candidates held in LDS
 constexpr int kMaxK = 2048;
+constexpr int kGroup = 16;                // entries per group maximum
+constexpr int kGroupFactor = 4;           // group path when groups >= 4k
 
 // ------------------------------------------------------------------ operand loads
 // Per-format A/B operand of one 16x16 MFMA tile, for one lane:
@@ -57,15 +66,14 @@ template <int DI> struct Operand<CSA_FP8_E4M3, DI> {
 };
 
 template <int DI> struct Operand<CSA_FP4_E2M1, DI> {
-  i32x8 v;
+  i32x4 v;      // 32 e2m1 values; the MFMA reads only the low 4 dwords of its operand
   int scale;
   __device__ __forceinline__ void load(const uint8_t* row, const uint8_t* srow, int g) {
     if (DI == 128 || g < 2) {
-      const i32x4 a = *reinterpret_cast<const i32x4*>(row + 16 * g);
-      v = i32x8{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+      v = *reinterpret_cast<const i32x4*>(row + 16 * g);
       scale = srow[g];
     } else {
-      v = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      v = i32x4{0, 0, 0, 0};
       scale = 127;
     }
   }
@@ -99,7 +107,9 @@ __device__ __forceinline__ f32x4 mma_tile(const Operand<FMT, DI>& a, const Opera
   if constexpr (FMT == CSA_FP8_E4M3) {
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, acc, 0, 0, 0, 127, 0, 127);
   } else if constexpr (FMT == CSA_FP4_E2M1) {
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a.v, b.v, acc, 4, 4, 0, a.scale, 0, b.scale);
+    const i32x8 av = {a.v[0], a.v[1], a.v[2], a.v[3], 0, 0, 0, 0};
+    const i32x8 bv = {b.v[0], b.v[1], b.v[2], b.v[3], 0, 0, 0, 0};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, a.scale, 0, b.scale);
   } else if constexpr (FMT == CSA_BF16) {
 #pragma unroll
     for (int ks = 0; ks < DI / 32; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[ks], b.v[ks], acc, 0, 0, 0);
@@ -121,16 +131,34 @@ template <int FMT, int DI> __host__ __device__ constexpr int row_units() {
   return FMT == CSA_FP4_E2M1 ? DI / 2 : DI;
 }
 
+// ------------------------------------------------------------------ lane reductions
+// Sum of the four lanes l, l^16, l^32, l^48 (VALU permlane swaps: each swap
+// returns both halves, whose sum pairs every lane with its partner).
+__device__ __forceinline__ float sum_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+// Maximum over the 16 lanes of a row (DPP row rotations).
+__device__ __forceinline__ float max_row16(float v) {
+  v = fmaxf(v, __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x128, 0xf, 0xf, false)));
+  v = fmaxf(v, __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x124, 0xf, 0xf, false)));
+  v = fmaxf(v, __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x122, 0xf, 0xf, false)));
+  v = fmaxf(v, __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x121, 0xf, 0xf, false)));
+  return v;
+}
+
 // ------------------------------------------------------------------ score kernel
 // grid.x: entry chunk (chunk_entries entries each), grid.y: query group
 // (QB consecutive queries of one sequence), 256 threads (4 waves).
 // Group gy covers rows row_lo(gy) .. ; row r writes scores at sbase + (r - srow0) * N.
-template <int FMT, int DI, int HB, int QB>
+template <int FMT, int DI, int HB, int QB, int UB, bool DBUF>
 __global__ __launch_bounds__(256) void k_index_score(
     const void* __restrict__ q_idx, const void* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k_idx, const void* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
     int64_t Tq, int64_t N, int H_I, int ratio, int64_t group0, int64_t groups_per_batch,
-    int64_t chunk_entries, float* __restrict__ sbase, int64_t srow0) {
+    int64_t chunk_entries, float* __restrict__ sbase, int64_t srow0, float* __restrict__ gbase, int64_t grow0) {
   typedef typename Storage<FMT>::type ST;
   constexpr int RU = row_units<FMT, DI>();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -168,7 +196,8 @@ __global__ __launch_bounds__(256) void k_index_score(
       else
         qa[qi][hb].load(qrow, g);
       if (hrow >= H_I) {   // padded head: zero operand
-        if constexpr (FMT == CSA_FP8_E4M3 || FMT == CSA_FP4_E2M1) qa[qi][hb].v = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (FMT == CSA_FP8_E4M3) qa[qi][hb].v = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        else if constexpr (FMT == CSA_FP4_E2M1) qa[qi][hb].v = i32x4{0, 0, 0, 0};
         else if constexpr (FMT == CSA_BF16) {
 #pragma unroll
           for (int ks = 0; ks < DI / 32; ++ks) qa[qi][hb].v[ks] = __builtin_bit_cast(bf16x8, i32x4{0, 0, 0, 0});
@@ -193,33 +222,68 @@ __global__ __launch_bounds__(256) void k_index_score(
   }
 
   const ST* kbase = reinterpret_cast<const ST*>(k_idx) + b * N * RU;
-  for (int64_t e0 = e_begin + 16 * wv; e0 < e_end; e0 += 64) {
-    const int64_t e = e0 + col;
-    const int64_t esafe = e < N ? e : N - 1;
-    Operand<FMT, DI> kb;
-    if constexpr (FMT == CSA_FP4_E2M1)
-      kb.load(kbase + esafe * RU, reinterpret_cast<const uint8_t*>(k_scale) + (b * N + esafe) * (DI / 32), g);
-    else
-      kb.load(kbase + esafe * RU, g);
-    float ks = 1.f;
-    if constexpr (FMT == CSA_FP8_E4M3) ks = reinterpret_cast<const float*>(k_scale)[b * N + esafe];
+  const int64_t G = (N + kGroup - 1) / kGroup;
+  // Keys are consumed in batches of UB 16-entry blocks per wave (64*UB
+  // entries per block-wide batch); with DBUF the loads of batch i+1 are in
+  // flight while batch i is computed.
+  constexpr int64_t STEP = 64 * UB;
+  auto load_batch = [&](Operand<FMT, DI>* kb, float* ks, int64_t base) {
 #pragma unroll
-    for (int qi = 0; qi < QB; ++qi) {
-      if (qi >= nq) break;
-      float part = 0.f;
+    for (int u = 0; u < UB; ++u) {
+      const int64_t e = base + 16 * wv + 64 * u + col;
+      const int64_t esafe = e < N ? e : N - 1;
+      if constexpr (FMT == CSA_FP4_E2M1)
+        kb[u].load(kbase + esafe * RU, reinterpret_cast<const uint8_t*>(k_scale) + (b * N + esafe) * (DI / 32), g);
+      else
+        kb[u].load(kbase + esafe * RU, g);
+      ks[u] = 1.f;
+      if constexpr (FMT == CSA_FP8_E4M3) ks[u] = reinterpret_cast<const float*>(k_scale)[b * N + esafe];
+    }
+  };
+  auto compute_batch = [&](const Operand<FMT, DI>* kb, const float* ks, int64_t base) {
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const f32x4 acc = mma_tile<FMT, DI>(qa[qi][hb], kb);
+    for (int u = 0; u < UB; ++u) {
+      const int64_t e0 = base + 16 * wv + 64 * u;
+      if (e0 >= e_end) break;
+      const int64_t e = e0 + col;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) part = fmaf(wq[qi][hb][rr], fmaxf(acc[rr], 0.f), part);
-      }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if constexpr (FMT == CSA_FP8_E4M3) part *= ks;
-      if (g == 0 && e < nvis[qi]) {
+      for (int qi = 0; qi < QB; ++qi) {
+        if (qi >= nq) break;
+        float part = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const f32x4 acc = mma_tile<FMT, DI>(qa[qi][hb], kb[u]);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) part = fmaf(wq[qi][hb][rr], fmaxf(acc[rr], 0.f), part);
+        }
+        part = sum_xor16_32(part);
+        if constexpr (FMT == CSA_FP8_E4M3) part *= ks[u];
+        const bool ok = e < nvis[qi];
+        // group maximum over the 16 entries of this block (valid entries only)
+        const float gm = max_row16(ok ? part : -INFINITY);
         const int64_t r = b * Tq + t0 + qi;
-        sbase[(r - srow0) * N + e] = part;
+        if (g == 0 && ok) sbase[(r - srow0) * N + e] = part;
+        if (lane == 0 && e0 < nvis[qi]) gbase[(r - grow0) * G + e0 / kGroup] = gm;
       }
+    }
+  };
+  if constexpr (DBUF) {
+    Operand<FMT, DI> kA[UB], kB[UB];
+    float sA[UB], sB[UB];
+    load_batch(kA, sA, e_begin);
+    for (int64_t base = e_begin; base < e_end; base += 2 * STEP) {
+      if (base + STEP < e_end) load_batch(kB, sB, base + STEP);
+      compute_batch(kA, sA, base);
+      if (base + STEP >= e_end) break;
+      if (base + 2 * STEP < e_end) load_batch(kA, sA, base + 2 * STEP);
+      compute_batch(kB, sB, base + STEP);
+    }
+  } else {
+    for (int64_t base = e_begin; base < e_end; base += STEP) {
+      Operand<FMT, DI> kA[UB];
+      float sA[UB];
+      load_batch(kA, sA, base);
+      compute_batch(kA, sA, base);
     }
   }
 }
@@ -242,18 +306,16 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* w
   return v + add;
 }
 
-// Top-k of one row of scores (n entries, keff = min(k, n) > 0 entries wanted,
-// n > k). Writes the ascending selection into sel[0..keff).
 struct TopkSmem {
-  union {
-    uint32_t hist[kHistBins];
-    unsigned long long cand[kCandCap];
-  };
+  uint32_t hist[kHistBins];
+  unsigned long long cand[kCandCap];
   int sel[kMaxK];
   uint32_t h256[256];
   uint32_t wsum[16];
-  int nsel, ncand;
-  uint32_t d1, need;
+  unsigned long long red_and[kTopkThreads / 64], red_or[kTopkThreads / 64];
+  float redf[kTopkThreads / 64];
+  int nsel, ncand, ngrp;
+  uint32_t bin, need;
   unsigned long long prefix, mask, thresh;
   int done;
 };
@@ -261,19 +323,79 @@ struct TopkSmem {
 __device__ __forceinline__ unsigned long long composite(uint32_t key, int64_t i) {
   return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
 }
+__device__ __forceinline__ int composite_index(unsigned long long c) {
+  return (int)(0xffffffffu - (uint32_t)(c & 0xffffffffu));
+}
 
-// Radix select: the need-th largest composite among alive elements
-// (those whose masked bits equal the prefix). get(i) -> (valid, key64).
+// Bucket of the target-th largest element of sm.hist (bins scanned from the
+// top); sets sm.bin and sm.need = target - (count in higher bins).
+__device__ void find_bucket(TopkSmem& sm, uint32_t target) {
+  const int tid = threadIdx.x;
+  constexpr int BPT = kHistBins / kTopkThreads;
+  const int top = kHistBins - BPT * tid;   // owns bins [top - BPT, top)
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 1; i <= BPT; ++i) mine += sm.hist[top - i];
+  const uint32_t incl = block_inclusive_scan(mine, sm.wsum);
+  const uint32_t excl = incl - mine;
+  if (excl < target && incl >= target) {
+    uint32_t above = excl;
+    int bin = top - 1;
+    for (; bin > top - BPT; --bin) {
+      if (above + sm.hist[bin] >= target) break;
+      above += sm.hist[bin];
+    }
+    sm.bin = (uint32_t)bin;
+    sm.need = target - above;
+  }
+  __syncthreads();
+}
+
+// Radix select: the need-th largest composite among alive elements (those
+// whose masked bits equal the prefix). get(i, ok) returns element i's key.
+// First the bits on which every alive element agrees are fixed at once (AND /
+// OR reduction); then 8-bit digits are resolved from the top, each with a
+// 256-bin LDS histogram and a one-wave parallel search for the digit that
+// holds the need-th largest. Stops as soon as the chosen digit's bucket is
+// taken whole.
 template <typename Get>
 __device__ void radix_threshold(TopkSmem& sm, int64_t count, Get get) {
-  const int tid = threadIdx.x;
-  int shift = 64;
-  // bits already fixed: the mask's leading ones
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  {
+    unsigned long long a = ~0ull, o = 0ull;
+    const unsigned long long mask = sm.mask, prefix = sm.prefix;
+    for (int64_t i = tid; i < count; i += kTopkThreads) {
+      bool ok;
+      const unsigned long long key = get(i, ok);
+      if (ok && (key & mask) == prefix) { a &= key; o |= key; }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      a &= __shfl_xor(a, off);
+      o |= __shfl_xor(o, off);
+    }
+    if (lane == 0) { sm.red_and[wv] = a; sm.red_or[wv] = o; }
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long A = ~0ull, Ov = 0ull;
+      for (int w = 0; w < kTopkThreads / 64; ++w) { A &= sm.red_and[w]; Ov |= sm.red_or[w]; }
+      const unsigned long long diff = A ^ Ov;          // bits on which alive keys differ
+      const int lead = diff ? __clzll(diff) : 64;
+      const unsigned long long lm = lead >= 64 ? ~0ull : (lead == 0 ? 0ull : (~0ull << (64 - lead)));
+      if ((lm | sm.mask) != sm.mask) {
+        sm.mask |= lm;
+        sm.prefix = A & sm.mask;
+      }
+      sm.done = sm.mask == ~0ull;
+      sm.thresh = sm.prefix;
+    }
+    __syncthreads();
+    if (sm.done) return;
+  }
   for (;;) {
-    // next digit: up to 8 bits directly below the fixed bits
     const int fixed = __popcll(sm.mask);
     const int width = (64 - fixed) < 8 ? (64 - fixed) : 8;
-    shift = 64 - fixed - width;
+    const int shift = 64 - fixed - width;
     const unsigned long long dmask = ((1ull << width) - 1ull) << shift;
     for (int i = tid; i < 256; i += kTopkThreads) sm.h256[i] = 0;
     __syncthreads();
@@ -284,90 +406,143 @@ __device__ void radix_threshold(TopkSmem& sm, int64_t count, Get get) {
       if (ok && (key & mask) == prefix) atomicAdd(&sm.h256[(key & dmask) >> shift], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t need = sm.need, above = 0;
-      int dd = (1 << width) - 1;
-      for (; dd > 0; --dd) {
-        if (above + sm.h256[dd] >= need) break;
-        above += sm.h256[dd];
+    if (wv == 0) {
+      // lane l owns digits [252 - 4l, 255 - 4l], scanned from the top
+      const int top = 255 - 4 * lane;
+      uint32_t h[4], mine = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { h[j] = sm.h256[top - j]; mine += h[j]; }
+      uint32_t incl = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
       }
-      need -= above;
-      sm.prefix = prefix | ((unsigned long long)dd << shift);
-      sm.mask = mask | dmask;
-      sm.need = need;
-      sm.done = (sm.h256[dd] == need) || (sm.mask == ~0ull);
-      sm.thresh = sm.prefix;   // remaining low bits zero: key >= thresh <=> chosen
+      const uint32_t need = sm.need, excl = incl - mine;
+      if (excl < need && incl >= need) {
+        uint32_t above = excl;
+        int j = 0;
+        for (; j < 3; ++j) {
+          if (above + h[j] >= need) break;
+          above += h[j];
+        }
+        const int dd = top - j;
+        const uint32_t rest = need - above;
+        sm.prefix = prefix | ((unsigned long long)dd << shift);
+        sm.mask = mask | dmask;
+        sm.need = rest;
+        sm.done = (h[j] == rest) || (sm.mask == ~0ull);
+        sm.thresh = sm.prefix;   // remaining low bits zero: key >= thresh <=> chosen
+      }
     }
     __syncthreads();
     if (sm.done) break;
   }
 }
 
-__device__ void bitonic_sort_sel(TopkSmem& sm, int keff) {
-  int P = 1;
-  while (P < keff) P <<= 1;
-  for (int i = keff + threadIdx.x; i < P; i += kTopkThreads) sm.sel[i] = 0x7fffffff;
+// Append slot for each lane with pred set: one atomic per wave (ballot +
+// prefix popcount). Returns -1 for lanes without pred.
+__device__ __forceinline__ int wave_append(bool pred, int* counter) {
+  const unsigned long long mask = __ballot(pred);
+  if (mask == 0ull) return -1;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)mask) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(mask));
+  base = __shfl(base, leader);
+  return pred ? base + __popcll(mask & ((1ull << lane) - 1ull)) : -1;
+}
+
+__device__ __forceinline__ float block_min(float v, float* red) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int k2 = 2; k2 <= P; k2 <<= 1) {
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += kTopkThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const int a = sm.sel[i], c = sm.sel[ixj];
-          const bool up = (i & k2) == 0;
-          if ((a > c) == up) { sm.sel[i] = c; sm.sel[ixj] = a; }
-        }
-      }
-      __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < kTopkThreads / 64; ++w) r = fminf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < kTopkThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// Write the keff distinct indices of sm.sel in ascending order. For rows of
+// up to 32 * kHistBins entries a bitmap of the chosen entries is built in the
+// (then unused) histogram area and compacted in order with one block scan;
+// longer rows place each index at its rank among the chosen.
+__device__ void write_sorted(TopkSmem& sm, int keff, int64_t n, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  if (n <= (int64_t)32 * kHistBins) {
+    constexpr int WPT = kHistBins / kTopkThreads;          // bitmap words per thread
+    for (int i = tid; i < kHistBins; i += kTopkThreads) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < keff; i += kTopkThreads) {
+      const int v = sm.sel[i];
+      atomicOr(&sm.hist[v >> 5], 1u << (v & 31));
     }
+    __syncthreads();
+    uint32_t w[WPT], cnt = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) { w[j] = sm.hist[tid * WPT + j]; cnt += __popc(w[j]); }
+    const uint32_t incl = block_inclusive_scan(cnt, sm.wsum);
+    int pos = (int)(incl - cnt);
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      uint32_t x = w[j];
+      while (x) {
+        const int bit = __ffs((int)x) - 1;
+        out[pos++] = (tid * WPT + j) * 32 + bit;
+        x &= x - 1u;
+      }
+    }
+    return;
+  }
+  for (int i = tid; i < keff; i += kTopkThreads) {
+    const int v = sm.sel[i];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < keff; ++j) rank += sm.sel[j] < v;
+    out[rank] = v;
   }
 }
 
-// One block per row of the current chunk. Scores of row r live at
-// sbase + (r - srow0) * N.
-__global__ __launch_bounds__(kTopkThreads) void k_topk_rows(const float* __restrict__ sbase, int64_t srow0,
-                                                            int64_t row0, const int32_t* __restrict__ q_pos,
-                                                            int64_t N, int ratio, int k, int32_t* __restrict__ idx_out) {
-  __shared__ TopkSmem sm;
+// Take the candidates whose composite is >= the need-th largest among
+// sm.cand[0..ncand) into sm.sel (appending after sm.nsel).
+__device__ void take_top_candidates(TopkSmem& sm, int ncand) {
   const int tid = threadIdx.x;
-  const int64_t r = row0 + blockIdx.x;
-  const int64_t n = visible(q_pos[r], ratio, N);
-  int32_t* out = idx_out + r * (int64_t)k;
-  if (n <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
+  if ((uint32_t)ncand == sm.need) {
+    for (int c = tid; c < ncand; c += kTopkThreads) sm.sel[atomicAdd(&sm.nsel, 1)] = composite_index(sm.cand[c]);
+  } else {
+    radix_threshold(sm, ncand, [&](int64_t i, bool& ok) { ok = true; return sm.cand[i]; });
+    const unsigned long long th = sm.thresh;
+    for (int c = tid; c < ncand; c += kTopkThreads)
+      if (sm.cand[c] >= th) sm.sel[atomicAdd(&sm.nsel, 1)] = composite_index(sm.cand[c]);
   }
-  const int keff = k;
-  const float* srow = sbase + (r - srow0) * N;
+  __syncthreads();
+}
 
-  // Pass 1: 13-bit histogram of the order keys.
+// Full-row path: 13-bit histogram of all n scores, take the higher buckets,
+// resolve the boundary bucket exactly. Leaves k indices in sm.sel.
+__device__ void select_full_row(TopkSmem& sm, const float* __restrict__ srow, int64_t n, int k) {
+  const int tid = threadIdx.x;
   for (int i = tid; i < kHistBins; i += kTopkThreads) sm.hist[i] = 0;
   if (tid == 0) { sm.nsel = 0; sm.ncand = 0; }
   __syncthreads();
+#pragma unroll 8
   for (int64_t i = tid; i < n; i += kTopkThreads) atomicAdd(&sm.hist[order_key(srow[i]) >> (32 - kHistBits)], 1u);
   __syncthreads();
-  // Locate the bucket of the keff-th largest: thread t owns 16 bins from the top.
-  constexpr int BPT = kHistBins / kTopkThreads;
-  const int top = kHistBins - BPT * tid;   // owns bins [top - BPT, top)
-  uint32_t mine = 0;
-#pragma unroll
-  for (int i = 1; i <= BPT; ++i) mine += sm.hist[top - i];
-  const uint32_t incl = block_inclusive_scan(mine, sm.wsum);
-  const uint32_t excl = incl - mine;
-  if (excl < (uint32_t)keff && incl >= (uint32_t)keff) {
-    uint32_t above = excl;
-    int bin = top - 1;
-    for (; bin > top - BPT; --bin) {
-      if (above + sm.hist[bin] >= (uint32_t)keff) break;
-      above += sm.hist[bin];
-    }
-    sm.d1 = (uint32_t)bin;
-    sm.need = (uint32_t)keff - above;
-  }
-  __syncthreads();
-  const uint32_t d1 = sm.d1;
-
-  // Pass 2: take rows above the bucket, collect the bucket's members.
+  find_bucket(sm, (uint32_t)k);
+  const uint32_t d1 = sm.bin;
+#pragma unroll 8
   for (int64_t i = tid; i < n; i += kTopkThreads) {
     const uint32_t key = order_key(srow[i]);
     const uint32_t d = key >> (32 - kHistBits);
@@ -386,14 +561,8 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_rows(const float* __restr
     sm.done = 0;
   }
   __syncthreads();
-  if ((uint32_t)ncand == sm.need) {
-    for (int c = tid; c < ncand; c += kTopkThreads)
-      sm.sel[atomicAdd(&sm.nsel, 1)] = (int)(0xffffffffu - (uint32_t)(sm.cand[c] & 0xffffffffu));
-  } else if (ncand <= kCandCap) {
-    radix_threshold(sm, ncand, [&](int64_t i, bool& ok) { ok = true; return sm.cand[i]; });
-    const unsigned long long th = sm.thresh;
-    for (int c = tid; c < ncand; c += kTopkThreads)
-      if (sm.cand[c] >= th) sm.sel[atomicAdd(&sm.nsel, 1)] = (int)(0xffffffffu - (uint32_t)(sm.cand[c] & 0xffffffffu));
+  if (ncand <= kCandCap) {
+    take_top_candidates(sm, ncand);
   } else {
     // Bucket larger than the LDS list (heavy ties): select straight from the row.
     radix_threshold(sm, n, [&](int64_t i, bool& ok) {
@@ -405,10 +574,150 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_rows(const float* __restr
       const uint32_t key = order_key(srow[i]);
       if ((key >> (32 - kHistBits)) == d1 && composite(key, i) >= th) sm.sel[atomicAdd(&sm.nsel, 1)] = (int)i;
     }
+    __syncthreads();
+  }
+}
+
+// Group path. tau is a lower bound of the k-th largest group maximum: the
+// maxima are binned linearly between their minimum and maximum (a monotone
+// map, so bins above the boundary bin hold only larger values), and tau is
+// the smallest maximum in the bin that holds the k-th largest. At least k
+// groups have maximum >= tau, so at least k entries are >= tau and the top-k
+// lies among them. Each thread loads its kGPT maxima into registers once
+// (all loads in flight); qualifying groups are listed in LDS with one block
+// scan; their scores are then read flat, kGPT per thread per batch, and the
+// entries >= tau appended as candidates. Returns false (nothing written to
+// the output) if the row has more maxima than the registers hold or the
+// candidates do not fit in LDS.
+constexpr int kGPT = 32;
+
+__device__ bool select_by_groups(TopkSmem& sm, const float* __restrict__ srow, const float* __restrict__ grow,
+                                 int64_t n, int64_t m, int k) {
+  const int tid = threadIdx.x;
+  if (m > (int64_t)kGPT * kTopkThreads) return false;
+  float gv[kGPT];
+#pragma unroll
+  for (int j = 0; j < kGPT; ++j) {
+    const int gi = tid + j * kTopkThreads;
+    gv[j] = gi < m ? grow[gi] : 0.f;
+  }
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kGPT; ++j)
+    if (tid + j * kTopkThreads < m) { lo = fminf(lo, gv[j]); hi = fmaxf(hi, gv[j]); }
+  for (int i = tid; i < kHistBins; i += kTopkThreads) sm.hist[i] = 0;
+  lo = block_min(lo, sm.redf);
+  hi = block_max(hi, sm.redf);
+  const float inv = hi > lo ? (float)(kHistBins - 1) / (hi - lo) : 0.f;
+  auto bin_of = [&](float v) -> int {
+    const float t = (v - lo) * inv;
+    return t >= (float)(kHistBins - 1) ? kHistBins - 1 : (int)t;
+  };
+#pragma unroll
+  for (int j = 0; j < kGPT; ++j)
+    if (tid + j * kTopkThreads < m) atomicAdd(&sm.hist[bin_of(gv[j])], 1u);
+  __syncthreads();
+  find_bucket(sm, (uint32_t)k);
+  const int b = (int)sm.bin;
+  float tmin = INFINITY;
+#pragma unroll
+  for (int j = 0; j < kGPT; ++j)
+    if (tid + j * kTopkThreads < m && bin_of(gv[j]) == b) tmin = fminf(tmin, gv[j]);
+  const float tau = block_min(tmin, sm.redf);
+  const uint32_t tau_key = order_key(tau);
+  // list the qualifying groups (the LDS histogram area is free now)
+  int* glist = reinterpret_cast<int*>(sm.hist);
+  uint32_t qual = 0, cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kGPT; ++j) {
+    const bool q = tid + j * kTopkThreads < m && order_key(gv[j]) >= tau_key;
+    qual |= (uint32_t)q << j;
+    cnt += q;
+  }
+  const uint32_t incl = block_inclusive_scan(cnt, sm.wsum);
+  const int ngrp = (int)(sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3] + sm.wsum[4] + sm.wsum[5] +
+                         sm.wsum[6] + sm.wsum[7]);
+  if (ngrp > kHistBins) return false;      // uniform across the block
+  {
+    int pos = (int)(incl - cnt);
+#pragma unroll
+    for (int j = 0; j < kGPT; ++j)
+      if ((qual >> j) & 1u) glist[pos++] = tid + j * kTopkThreads;
+  }
+  if (tid == 0) { sm.nsel = 0; sm.ncand = 0; }
+  __syncthreads();
+  // their scores, one per lane, kGPT per thread per batch
+  const int total = ngrp * kGroup;
+  for (int base = 0; base < total; base += kGPT * kTopkThreads) {
+    float v[kGPT];
+#pragma unroll
+    for (int u = 0; u < kGPT; ++u) {
+      const int f = base + u * kTopkThreads + tid;
+      const int64_t e = f < total ? (int64_t)glist[f >> 4] * kGroup + (f & (kGroup - 1)) : n;
+      v[u] = e < n ? srow[e] : -INFINITY;
+    }
+    uint32_t take = 0, c = 0;
+#pragma unroll
+    for (int u = 0; u < kGPT; ++u) {
+      const int f = base + u * kTopkThreads + tid;
+      const int64_t e = f < total ? (int64_t)glist[f >> 4] * kGroup + (f & (kGroup - 1)) : n;
+      const bool t = e < n && order_key(v[u]) >= tau_key;
+      take |= (uint32_t)t << u;
+      c += t;
+    }
+    const uint32_t ci = block_inclusive_scan(c, sm.wsum);
+    int pos = sm.ncand + (int)(ci - c);
+    const int added = (int)(sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3] + sm.wsum[4] + sm.wsum[5] +
+                            sm.wsum[6] + sm.wsum[7]);
+#pragma unroll
+    for (int u = 0; u < kGPT; ++u) {
+      if (!((take >> u) & 1u)) continue;
+      const int f = base + u * kTopkThreads + tid;
+      const int64_t e = (int64_t)glist[f >> 4] * kGroup + (f & (kGroup - 1));
+      if (pos < kCandCap) sm.cand[pos] = composite(order_key(v[u]), e);
+      ++pos;
+    }
+    __syncthreads();
+    if (tid == 0) sm.ncand += added;
+    __syncthreads();
+  }
+  const int ncand = sm.ncand;
+  if (ncand > kCandCap) return false;
+  if (tid == 0) {
+    sm.prefix = 0;
+    sm.mask = 0;
+    sm.need = (uint32_t)k;
+    sm.done = 0;
   }
   __syncthreads();
-  bitonic_sort_sel(sm, keff);
-  for (int i = tid; i < k; i += kTopkThreads) out[i] = i < keff ? sm.sel[i] : -1;
+  take_top_candidates(sm, ncand);
+  return true;
+}
+
+// One block per row of the current pass. Row r's scores live at
+// sbase + (r - srow0) * N and its group maxima at gbase + (r - grow0) * G.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float* __restrict__ sbase, int64_t srow0,
+                                                              const float* __restrict__ gbase, int64_t grow0,
+                                                              int64_t row0, const int32_t* __restrict__ q_pos,
+                                                              int64_t N, int ratio, int k, int32_t* __restrict__ idx_out) {
+  __shared__ TopkSmem sm;
+  const int tid = threadIdx.x;
+  const int64_t r = row0 + blockIdx.x;
+  const int64_t n = visible(q_pos[r], ratio, N);
+  int32_t* out = idx_out + r * (int64_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int64_t G = (N + kGroup - 1) / kGroup;
+  const float* srow = sbase + (r - srow0) * N;
+  const float* grow = gbase + (r - grow0) * G;
+  const int64_t m = (n + kGroup - 1) / kGroup;
+  bool done = false;
+  if (m >= (int64_t)kGroupFactor * k) done = select_by_groups(sm, srow, grow, n, m, k);
+  if (!done) select_full_row(sm, srow, n, k);
+  __syncthreads();
+  write_sorted(sm, k, n, out);
 }
 
 // ------------------------------------------------------------------ host side
@@ -433,7 +742,7 @@ static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N) {
   if (p.chunk_entries < 64) p.chunk_entries = 64;
   // Score buffer budget per pass: 1 GiB.
   const int64_t budget = (int64_t)1 << 30;
-  const int64_t row_bytes = (N > 0 ? N : 1) * 4;
+  const int64_t row_bytes = (N > 0 ? N : 1) * 4 + ((N + kGroup - 1) / kGroup) * 4;
   int64_t gpp = budget / (row_bytes * p.QB);
   if (gpp < 1) gpp = 1;
   if (gpp > 65535) gpp = 65535;
@@ -443,40 +752,52 @@ static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N) {
   return p;
 }
 
+static int64_t groups_of(int64_t N) { return (N + kGroup - 1) / kGroup; }
+
+// Workspace: per pass, the scores [rows, N] and the group maxima [rows, G].
 size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N) {
   const IndexPlan p = make_plan(B, Tq, N);
-  return (size_t)p.max_rows_per_pass * (size_t)N * 4 + 256;
+  const size_t rows = (size_t)p.max_rows_per_pass;
+  return rows * (size_t)N * 4 + rows * (size_t)groups_of(N) * 4 + 256;
 }
+
+// Batch shape of the key stream per format and queries per block (from a
+// sweep on MI355X at the 262k/1M-context decode shapes: deeper batching or
+// double buffering lowered occupancy without raising bandwidth).
+template <int FMT, int QB> struct ScoreCfg {
+  static constexpr int UB = (FMT == CSA_FP4_E2M1 || QB > 1) ? 1 : 4;
+  static constexpr bool DBUF = false;
+};
 
 template <int FMT, int DI, int HB, int QB>
 static void launch_score(dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w, const void* kk,
                          const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I, int ratio, int64_t g0,
-                         int64_t gpb, int64_t ce, float* sb, int64_t sr0) {
-  k_index_score<FMT, DI, HB, QB><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0);
+                         int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
+  k_index_score<FMT, DI, HB, QB, ScoreCfg<FMT, QB>::UB, ScoreCfg<FMT, QB>::DBUF><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
 }
 
 template <int FMT, int DI, int QB>
 static void dispatch_hb(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
                         const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
-                        int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0) {
+                        int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
   switch (HB) {
-    case 1: launch_score<FMT, DI, 1, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0); break;
-    case 2: launch_score<FMT, DI, 2, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0); break;
-    case 3: launch_score<FMT, DI, 3, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0); break;
-    default: launch_score<FMT, DI, 4, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0); break;
+    case 1: launch_score<FMT, DI, 1, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 2: launch_score<FMT, DI, 2, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 3: launch_score<FMT, DI, 3, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    default: launch_score<FMT, DI, 4, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
   }
 }
 
 template <int FMT>
 static void dispatch_fmt(int DI, int QB, int HB, dim3 grid, hipStream_t s, const void* q, const void* qs,
                          const float* w, const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N,
-                         int H_I, int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0) {
+                         int H_I, int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
   if (DI == 128) {
-    if (QB == 4) dispatch_hb<FMT, 128, 4>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0);
-    else dispatch_hb<FMT, 128, 1>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0);
+    if (QB == 4) dispatch_hb<FMT, 128, 4>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+    else dispatch_hb<FMT, 128, 1>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
   } else {
-    if (QB == 4) dispatch_hb<FMT, 64, 4>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0);
-    else dispatch_hb<FMT, 64, 1>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0);
+    if (QB == 4) dispatch_hb<FMT, 64, 4>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+    else dispatch_hb<FMT, 64, 1>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
   }
 }
 
@@ -496,21 +817,25 @@ hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const flo
     if (rhi > bend) rhi = bend;
     float* sb = score_out ? score_out : reinterpret_cast<float*>(ws);
     const int64_t sr0 = score_out ? 0 : rlo;
+    // group maxima live after the pass's score rows in the workspace (rows rlo..rhi)
+    // group maxima follow the pass's score rows in the workspace
+    float* gb = reinterpret_cast<float*>(ws) + (size_t)p.max_rows_per_pass * (size_t)N;
+    const int64_t gr0 = rlo;
     if (N > 0) {
       const dim3 grid((unsigned)cdiv(N, p.chunk_entries), (unsigned)(g1 - g0));
       timer_before(CSA_KID_INDEX_SCORE, s);
       switch (fmt) {
-        case CSA_FP8_E4M3: dispatch_fmt<CSA_FP8_E4M3>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0); break;
-        case CSA_FP4_E2M1: dispatch_fmt<CSA_FP4_E2M1>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0); break;
-        case CSA_BF16: dispatch_fmt<CSA_BF16>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0); break;
-        default: dispatch_fmt<CSA_F32>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0); break;
+        case CSA_FP8_E4M3: dispatch_fmt<CSA_FP8_E4M3>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
+        case CSA_FP4_E2M1: dispatch_fmt<CSA_FP4_E2M1>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
+        case CSA_BF16: dispatch_fmt<CSA_BF16>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
+        default: dispatch_fmt<CSA_F32>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
       }
       hipError_t e = hipGetLastError();
       timer_after(CSA_KID_INDEX_SCORE, s);
       if (e != hipSuccess) return e;
     }
     timer_before(CSA_KID_TOPK, s);
-    k_topk_rows<<<dim3((unsigned)(rhi - rlo)), kTopkThreads, 0, s>>>(sb, sr0, rlo, q_pos, N, ratio, k, idx_out);
+    k_topk_select<<<dim3((unsigned)(rhi - rlo)), kTopkThreads, 0, s>>>(sb, sr0, gb, gr0, rlo, q_pos, N, ratio, k, idx_out);
     hipError_t e = hipGetLastError();
     timer_after(CSA_KID_TOPK, s);
     if (e != hipSuccess) return e;

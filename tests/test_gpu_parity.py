@@ -143,6 +143,55 @@ def test_indexer_exact_grid_decode(fmt):
     assert np.array_equal(host(idx), want)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4", "f32", "bf16"])
+def test_indexer_exact_grid_decode_group_path(fmt):
+    """Decode rows with n/16 >= 4k take the group-maximum path; integer scores
+    tie often at the threshold."""
+    B, N, d_I, k = 2, 20011, 128, 128
+    d = syn.csa_decode(26, B=B, N=N, H=16, H_I=64, d_I=d_I, key_grid=("fp4" if fmt == "fp4" else "int"))
+    q_i = d["q_i"][:, None]
+    q_pos = np.array([[4 * N + 2], [4 * 9001 + 3]], np.int32)
+    _print("indexer grid decode group path", fmt)
+    qc, qs, kc, ks = _grid_operands(fmt, q_i, d["k_i"])
+    idx = C.indexer_topk(qc, qs, dev(d["w"][:, None]), kc, ks, fmt, dev(q_pos, torch.int32), 4, k, d_I)
+    _, want = _oracle_topk(q_i, d["w"][:, None], d["k_i"], q_pos, 4, k)
+    assert np.array_equal(host(idx), want)
+
+
+def test_indexer_normal_group_path_large_n():
+    """N(0,1) operands, n = 70,000 entries, k = 1024 (group path): selection over
+    the GPU's own scores is exact; float64 differences are certified ties."""
+    B, N, H_I, d_I, k = 2, 70001, 64, 128, 1024
+    d = syn.csa_decode(27, B=B, N=N, H=16, H_I=H_I, d_I=d_I)
+    q_pos = np.array([[4 * N], [4 * 66000 + 1]], np.int32)
+    _print("indexer normal group path")
+    idx, sc = C.indexer_topk(dev(d["q_i"][:, None]), None, dev(d["w"][:, None]), dev(d["k_i"]), None, "f32",
+                             dev(q_pos, torch.int32), 4, k, d_I, want_scores=True)
+    got_idx, got_s = host(idx), host(sc)
+    scores, want = _oracle_topk(d["q_i"][:, None], d["w"][:, None], d["k_i"], q_pos, 4, k)
+    for b in range(B):
+        n_vis = O.visible_entries(q_pos[b], 4, N)
+        assert np.array_equal(got_idx[b], O.topk_select(got_s[b].astype(np.float64), n_vis, k))
+        assert certified_index_mismatches(got_idx[b], want[b], scores[b], n_vis, k) <= 1
+
+
+def test_indexer_group_path_ties_fallback():
+    """Group path with every score equal: the candidate set overflows LDS, the
+    full-row path and then its row-scan fallback run; lowest indices win. A
+    second row has only a few distinct score values (moderate ties)."""
+    N, k = 40000, 100
+    q_i = np.zeros((1, 2, 4, 64), np.float32)
+    q_i[0, 1, :, 0] = 1.0
+    k_i = np.ones((1, N, 64), np.float32)
+    k_i[0, :, 0] = (np.arange(N) % 3).astype(np.float32)
+    w = np.ones((1, 2, 4), np.float32)
+    q_pos = np.array([[4 * N, 4 * N]], np.int32)
+    idx = C.indexer_topk(dev(q_i), None, dev(w), dev(k_i), None, "f32", dev(q_pos, torch.int32), 4, k, 64)
+    got = host(idx)[0]
+    assert np.array_equal(got[0], np.arange(k))
+    assert np.array_equal(got[1], np.arange(2, 3 * k, 3))
+
+
 @pytest.mark.parametrize("fmt", ["fp8", "fp4", "f32"])
 @pytest.mark.parametrize("d_I,H_I", [(128, 64), (64, 4), (64, 19)])
 def test_indexer_exact_grid_prefill(fmt, d_I, H_I):
