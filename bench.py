@@ -43,9 +43,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def recorded_traffic(kernel: str, source: str):
+    """HBM bytes per launch (read + written) of `kernel` from the committed
+    rocprofv3 counter summary, or None if the kernel's source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "csa_hca_decode_1m_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(os.path.join(ROOT, source), "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        if line.startswith("TRAFFIC ") and f"kernel={kernel} " in line:
+            kv = dict(f.split("=", 1) for f in line.split()[1:])
+            if kv.get("src_sha256_16") == sha:
+                return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
 # ----------------------------------------------------------------------------- decode workloads
 
-def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies, wid):
+def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies, wid, host_sample=True):
     """Build the caches (copies of them) and one-step closures for a decode workload."""
     dev = "cuda"
     N = L // 4
@@ -56,10 +72,12 @@ def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies,
     # keys: generate once in float32 on the device, quantise with the library
     ki32 = syn.normal_device(s + 2, (B, N, d_I), dev)
     codes, scales = C.csa_quantize_rows(ki32, fmt)
-    st["ki_host_rows"] = ki32[: min(B, 8)].cpu()       # for the CPU baseline sample
+    if host_sample:
+        st["ki_host_rows"] = ki32[: min(B, 8)].cpu()   # for the CPU baseline sample
     del ki32
     kv = syn.normal_device(s + 1, (B, N, 128), dev, bf)
-    st["kv_host"] = kv[: min(B, 8)].float().cpu()
+    if host_sample:
+        st["kv_host"] = kv[: min(B, 8)].float().cpu()
     st["codes"], st["scales"], st["kv"] = [codes], [scales], [kv]
     for _ in range(copies - 1):
         st["codes"].append(codes.clone())
@@ -84,7 +102,8 @@ def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies,
     st["bytes"] = bytes_idx + bytes_sp
     if hca:
         kvh = syn.normal_device(s + 11, (B, NH, 128), dev, bf)
-        st["kvh_host"] = kvh[: min(B, 8)].float().cpu()
+        if host_sample:
+            st["kvh_host"] = kvh[: min(B, 8)].float().cpu()
         st["kvh"] = [kvh] + [kvh.clone() for _ in range(copies - 1)]
         st["xh"] = syn.normal_device(s + 12, (B, 128, 128), dev, bf)
         st["qh"] = syn.normal_device(s + 13, (B, 1, H, 128), dev, bf, scale=1 / np.sqrt(128))
@@ -157,10 +176,11 @@ def kernel_times(torch, C, st, copies, steps, kernel):
 
 
 def cpu_baseline_decode(O, st, seconds):
-    """The oracle on the host: whole decode step for as many sequences as fit in
-    about `seconds` of CPU time (at least one), inputs prepared outside the timer."""
-    import torch
-    B, N, NH, k, fmt = st["B"], st["N"], st["NH"], st["k"], st["fmt"]
+    """The oracle on the host: the whole decode step (indexer scores, top-k,
+    sparse attention, and the HCA layer's dense attention), one sequence at a
+    time, repeated over the sampled sequences until about `seconds` of CPU
+    time are spent. Inputs (dequantised keys) are prepared outside the timer."""
+    B, N, k, fmt = st["B"], st["N"], st["k"], st["fmt"]
     L = st["L"]
     quant, deq = ((O.quant_mxfp4_rows, O.dequant_mxfp4_rows) if fmt == "fp4" else (O.quant_fp8_rows, O.dequant_fp8_rows))
     qi = st["qi32"].cpu().numpy()
@@ -172,13 +192,17 @@ def cpu_baseline_decode(O, st, seconds):
         qh = st["qh"].float().cpu().numpy()
         xh = st["xh"].float().cpu().numpy()
         sinkh = st["sinkh"].cpu().numpy()
-    done, spent = 0, 0.0
-    nsample = st["ki_host_rows"].shape[0]
+    nsample = min(2, st["ki_host_rows"].shape[0])
+    prep = []
     for b in range(nsample):
         kd = deq(*quant(st["ki_host_rows"][b].numpy()))
         qd = deq(*quant(qi[b]))
         kvb = st["kv_host"][b].numpy()
         kvh = st["kvh_host"][b].numpy() if st["hca"] else None
+        prep.append((b, kd, qd, kvb, kvh))
+    done, spent = 0, 0.0
+    while spent < seconds:
+        b, kd, qd, kvb, kvh = prep[done % nsample]
         t0 = time.perf_counter()
         s = O.indexer_scores(qd, w[b], kd, [L], 4)
         idx = O.topk_select(s, O.visible_entries([L], 4, N), k)
@@ -187,18 +211,17 @@ def cpu_baseline_decode(O, st, seconds):
             O.dense_attn(qh[b], kvh, xh[b], L - 127, sinkh, [L], 128, 128)
         spent += time.perf_counter() - t0
         done += 1
-        if spent >= seconds:
-            break
     return done, spent
 
 
 def run_decode(torch, C, syn, O, args, which):
     if which == "pair1m":
         st = decode_workload(torch, C, syn, "csa_hca_decode_pair_1m_ctx", B=8, L=1 << 20, H=128, H_I=64, d_I=128,
-                             k=1024, fmt="fp4", hca=True, copies=args.copies, wid=5)
+                             k=1024, fmt="fp4", hca=True, copies=args.copies, wid=5,
+                             host_sample=not args.no_cpu_baseline)
     else:
         st = decode_workload(torch, C, syn, "csa_decode_262k_ctx", B=32, L=1 << 18, H=128, H_I=64, d_I=128,
-                             k=1024, fmt="fp8", hca=False, copies=args.copies, wid=4)
+                             k=1024, fmt="fp8", hca=False, copies=args.copies, wid=4, host_sample=False)
     torch.cuda.synchronize()
     log(f"[bench] {st['name']}: setup done")
     ms, wall = time_graphs(torch, st, args.copies, args.steps, args.warmup, use_graph=not args.eager)
@@ -221,9 +244,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
     ap.add_argument("--extras", default="decode4", help="comma list of decode4,prefill2,prefill3 or 'none'")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the timed region, copy 512 MiB device to device once (the reference "
+                         "transfer for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
@@ -269,14 +295,16 @@ def main():
         "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in kt.items()},
         "roofline": {"bound": "hbm", "kernel": "k_index_score (fp4 keys)", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": st["bytes_index_score"]},
+                     "traffic": recorded_traffic("k_index_score",
+                                                 "long_context_attention_csa_amd/csrc/indexer.hip"),
+                     "bytes_per_launch": st["bytes_index_score"]},
     }
     if not args.no_cpu_baseline:
         done, spent = cpu_baseline_decode(O, st, args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(done / spent, 3), "unit": "queries/s",
                                   "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-                                  "sample": f"{done} of {B} sequences of one decode step (whole CSA+HCA pair, "
-                                            f"float64 NumPy), {spent:.1f} s"}
+                                  "sample": f"{done} single-sequence decode steps of the whole CSA+HCA pair "
+                                            f"(float64 NumPy, 2 sequences of the batch cycled), {spent:.1f} s"}
     extras = {}
     wanted = [] if args.extras == "none" else [x for x in args.extras.split(",") if x]
     del st
@@ -292,6 +320,13 @@ def main():
         torch.cuda.empty_cache()
     if extras:
         result["extras"] = extras
+    if args.calib_copy:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        bcopy = torch.empty_like(a)
+        torch.cuda.synchronize()
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = 512 << 20
     print(json.dumps(result), flush=True)
 
 
