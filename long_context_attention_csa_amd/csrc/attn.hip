@@ -330,6 +330,291 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
   }
 }
 
+// ------------------------------------------------------------------ bf16 path
+// Same computation for bf16, restructured around two gfx950 instructions:
+//  * global_load_lds_dwordx4 gathers key rows from HBM straight into LDS
+//    (no staging registers), into a ring of NBUF 64-key tiles, so up to
+//    NBUF-1 tiles of gathers are in flight while a tile is computed;
+//  * ds_read_b64_tr_b16 reads the V^T fragments of the P*V product
+//    transposed out of the same row-major tile, so no transposed copy is built.
+// Tiles are 64 rows x 256 B; each row's 16-byte chunk c is stored at position
+// c ^ (row & 7), which spreads both the QK fragment reads (16 rows, same chunk)
+// and the transposed reads (16 rows, 32 bytes) over all LDS banks. A lane of
+// a gather instruction fetches exactly the chunk its LDS slot must hold.
+constexpr int kSelChunk = 1024;     // selected indices staged in LDS at a time
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kD + ((chunk ^ (row & 7)) << 3); }
+
+template <int N_OUT>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(N_OUT), leaving expcnt and lgkmcnt unconstrained
+  static_assert(N_OUT >= 0 && N_OUT < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N_OUT & 15) | ((N_OUT >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <bool SPARSE, int NW, int HPW, int NBUF>
+__global__ __launch_bounds__(NW * 64, 2) void k_attn16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    const uint16_t* __restrict__ x_win, const int32_t* __restrict__ win_start, const float* __restrict__ sink,
+    const int32_t* __restrict__ q_pos, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio,
+    float scale, int S, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  constexpr int NT = NW * 64;
+  constexpr int LPT = (kKT * kD * 2 / 16) / NT;   // 16-byte gathers per thread per tile
+  __shared__ __align__(16) uint16_t ring[NBUF][kKT * kD];
+  __shared__ int tvalid[NBUF][kKT];
+  __shared__ int tbad[NBUF];
+  __shared__ int sidx[SPARSE ? kSelChunk : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t r = blockIdx.x;
+  const int hg = blockIdx.y / S, sp = blockIdx.y % S;
+  const int64_t b = r / Tq;
+  const int64_t p = q_pos[r];
+  const int64_t n_sel = SPARSE ? (int64_t)k : visible(p, ratio, N);
+  const int64_t w0 = win_start[b];
+  int64_t lo = p - window + 1;
+  if (lo < 0) lo = 0;
+  if (lo < w0) lo = w0;
+  int64_t hi = p;
+  if (hi > w0 + T_win - 1) hi = w0 + T_win - 1;
+  const int64_t n_win = (window > 0 && hi >= lo) ? hi - lo + 1 : 0;
+  const int64_t nk = n_sel + n_win;
+  const int64_t chunk = (nk + S - 1) / S;
+  const int64_t kbeg = (int64_t)sp * chunk;
+  const int64_t kend = (kbeg + chunk) < nk ? (kbeg + chunk) : nk;
+
+  const int h0 = hg * (NW * 16 * HPW) + wv * 16 * HPW;
+  Frag<uint16_t> qf[HPW][kD / 32];
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) {
+    const uint16_t* qrow = q + (r * H + h0 + 16 * hb + col) * kD;
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) qf[hb][ks].load(qrow + 32 * ks + 8 * g);
+  }
+  // Logits are kept in base 2 (log2(e) folded into the scale) so each
+  // probability is one v_exp_f32.
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  const float scale2 = scale * kLog2e;
+  const bool has_sink = (sink != nullptr) && sp == 0;
+  float m[HPW], lsum[HPW];
+  f32x4 O[HPW][kD / 16];
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) {
+    m[hb] = has_sink ? sink[h0 + 16 * hb + col] * kLog2e : -INFINITY;
+    lsum[hb] = (has_sink && g == 0) ? 1.f : 0.f;
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint16_t* dummy = q + r * H * kD;   // any readable row; its tile rows are zeroed
+  const uint16_t* kvb = kv + b * N * kD;
+  const uint16_t* xwb = x_win + b * T_win * kD;
+
+  // Keys are processed in sections of up to kSelChunk (the selected indices
+  // of a section are staged in LDS first), each as a pipeline of 64-key tiles.
+  for (int64_t c0 = kbeg; c0 < kend; c0 += kSelChunk) {
+    const int clen = (int)((kend - c0) < kSelChunk ? (kend - c0) : kSelChunk);
+    if (SPARSE) {
+      for (int i = tid; i < clen; i += NT) {
+        const int64_t ki = c0 + i;
+        sidx[i] = ki < n_sel ? idx[r * k + ki] : -1;
+      }
+      __syncthreads();
+    }
+    const int ntiles = (clen + kKT - 1) / kKT;
+    auto issue = [&](int t) {
+      const int slot = t % NBUF;
+      uint16_t* base = ring[slot];
+      bool bad = false;
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const int row = (j * NW + wv) * 4 + (lane >> 4);          // 4 rows per wave instruction
+        const int cs = lane & 15;
+        const int kk = t * kKT + row;                              // key within the section
+        const int64_t ki = c0 + kk;
+        const uint16_t* src = nullptr;
+        if (kk < clen) {
+          if (ki < n_sel) {
+            const int64_t e = SPARSE ? (int64_t)sidx[kk] : ki;
+            if (e >= 0 && e < N) src = kvb + e * kD;
+          } else {
+            src = xwb + (lo + (ki - n_sel) - w0) * kD;
+          }
+        }
+        if (cs == 0) tvalid[slot][row] = src != nullptr;
+        bad |= src == nullptr;
+        const uint16_t* gsrc = (src ? src : dummy) + ((cs ^ (row & 7)) << 3);
+        __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(base + (j * NW + wv) * 4 * kD),
+                                         16, 0, 0);
+      }
+      if (__ballot(bad)) {
+        if (lane == 0) atomicOr(&tbad[slot], 1);
+      }
+    };
+    for (int i = tid; i < NBUF; i += NT) tbad[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+      if (t < ntiles) issue(t);
+
+    for (int t = 0; t < ntiles; ++t) {
+      const int slot = t % NBUF;
+      if (t + NBUF - 1 < ntiles) {
+        issue(t + NBUF - 1);
+        wait_vm<(NBUF - 1) * LPT>();
+      } else {
+        wait_vm<0>();
+      }
+      __syncthreads();
+      uint16_t* tile = ring[slot];
+      if (tbad[slot]) {   // rows without a key: clear them so 0 * garbage cannot poison O
+        for (int i = tid; i < kKT * 16; i += NT) {
+          const int row = i >> 4;
+          if (!tvalid[slot][row]) *reinterpret_cast<i32x4*>(tile + row * kD + ((i & 15) << 3)) = i32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
+      }
+      const int nt = (clen - t * kKT) < kKT ? (clen - t * kKT) : kKT;
+
+      // ---- S^T = K Q^T for 4 blocks of 16 keys
+      float s[HPW][4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        f32x4 acc[HPW];
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int row = 16 * kb + col;
+#pragma unroll
+        for (int ks = 0; ks < kD / 32; ++ks) {
+          Frag<uint16_t> a;
+          a.load(tile + swz(row, 4 * ks + g));
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) acc[hb] = mma8(a, qf[hb][ks], acc[hb]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = acc[hb][rr] * scale2;
+      }
+      if (nt < kKT || tbad[slot]) {   // uniform: only partial or holed tiles are masked
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int key = 16 * kb + 4 * g + rr;
+            if (!(key < nt && tvalid[slot][key])) {
+#pragma unroll
+              for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = -INFINITY;
+            }
+          }
+      }
+      // ---- online softmax (per head = per column)
+#pragma unroll
+      for (int hb = 0; hb < HPW; ++hb) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) tmax = fmaxf(tmax, s[hb][kb][rr]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mnew = fmaxf(m[hb], tmax);
+        const bool live = mnew != -INFINITY;
+        const float msafe = live ? mnew : 0.f;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float pv = __builtin_amdgcn_exp2f(s[hb][kb][rr] - msafe);   // exp2(-inf) = 0
+            s[hb][kb][rr] = pv;
+            psum += pv;
+          }
+        if (__ballot(mnew != m[hb])) {   // rescale only when some running max moved
+          const float alpha = live ? __builtin_amdgcn_exp2f(m[hb] - mnew) : 1.f;
+          lsum[hb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
+        }
+        lsum[hb] += psum;
+        m[hb] = mnew;
+      }
+      // ---- O^T += V^T P^T. K-slot t of lane group g is key 4g+t (t < 4) or
+      // 16+4g+(t-4) (t >= 4) of the 32-key group; the transposed reads deliver
+      // exactly those keys for value column 16*db + col.
+      const int trow = 4 * g + (col >> 2);
+      const int tc = col & 3;
+#pragma unroll
+      for (int grp = 0; grp < 2; ++grp) {
+        Frag<uint16_t> pf[HPW];
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+          pf[hb].v[0] = (int)cvt_pk_bf16(s[hb][2 * grp][0], s[hb][2 * grp][1]);
+          pf[hb].v[1] = (int)cvt_pk_bf16(s[hb][2 * grp][2], s[hb][2 * grp][3]);
+          pf[hb].v[2] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][0], s[hb][2 * grp + 1][1]);
+          pf[hb].v[3] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][2], s[hb][2 * grp + 1][3]);
+        }
+        const int r0 = 32 * grp + trow, r1 = r0 + 16;
+#pragma unroll
+        for (int db = 0; db < kD / 16; ++db) {
+          const int cch = 2 * db + (tc >> 1), half = (tc & 1) * 4;
+          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(tile + swz(r0, cch) + half));
+          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(tile + swz(r1, cch) + half));
+          Frag<uint16_t> va;
+          va.v = i32x4{(int)((uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16)),
+                       (int)((uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16)),
+                       (int)((uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16)),
+                       (int)((uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16))};
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) O[hb][db] = mma8(va, pf[hb], O[hb][db]);
+        }
+      }
+      __syncthreads();   // the slot is refilled by a later issue()
+    }
+  }
+
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) {
+    float l = lsum[hb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int head = h0 + 16 * hb + col;
+    if (S == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* orow = out + (r * H + head) * kD;
+#pragma unroll
+      for (int db = 0; db < kD / 16; ++db) {
+        const float v[4] = {O[hb][db][0] * inv, O[hb][db][1] * inv, O[hb][db][2] * inv, O[hb][db][3] * inv};
+        Elem<uint16_t>::store4(orow + 16 * db + 4 * g, v);
+      }
+      if (lse && g == 0) lse[r * H + head] = l > 0.f ? (m[hb] + __log2f(l)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t pi = (r * H + head) * S + sp;
+      float* po = part_o + pi * kD;
+#pragma unroll
+      for (int db = 0; db < kD / 16; ++db)
+        *reinterpret_cast<float4*>(po + 16 * db + 4 * g) = make_float4(O[hb][db][0], O[hb][db][1], O[hb][db][2], O[hb][db][3]);
+      if (g == 0) {
+        part_ml[2 * pi] = m[hb] * kLn2;   // the merge works in natural-log units
+        part_ml[2 * pi + 1] = l;
+      }
+    }
+  }
+}
+
 // Merge of S partial results per (row, head), in split order. 256 threads =
 // 8 (row, head) pairs x 32 lanes x 4 channels; loads are unrolled so the S
 // partials of a pair are in flight together.
@@ -397,14 +682,22 @@ size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max) {
   return (size_t)rows * H * S * (kD + 2) * 4;
 }
 
+constexpr int kRing = 4;   // tiles in flight per block (bf16 path)
+
 template <typename T, bool SPARSE, int NW, int HPW>
 static void launch_attn_t(dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                           const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                           int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
                           int S, void* out, float* lse, float* po, float* pml) {
-  k_attn<T, SPARSE, NW, HPW><<<grid, NW * 64, 0, st>>>((const T*)q, (const T*)kv, idx, (const T*)x_win, win_start,
-                                                       sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S,
-                                                       (T*)out, lse, po, pml);
+  if constexpr (sizeof(T) == 2)
+    k_attn16<SPARSE, NW, HPW, kRing><<<grid, NW * 64, 0, st>>>((const uint16_t*)q, (const uint16_t*)kv, idx,
+                                                               (const uint16_t*)x_win, win_start, sink, q_pos, Tq, N,
+                                                               T_win, H, k, window, ratio, scale, S, (uint16_t*)out,
+                                                               lse, po, pml);
+  else
+    k_attn<T, SPARSE, NW, HPW><<<grid, NW * 64, 0, st>>>((const T*)q, (const T*)kv, idx, (const T*)x_win, win_start,
+                                                         sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S,
+                                                         (T*)out, lse, po, pml);
 }
 
 template <typename T, bool SPARSE>

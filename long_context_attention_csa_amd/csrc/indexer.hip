@@ -149,6 +149,26 @@ __device__ __forceinline__ float max_row16(float v) {
   return v;
 }
 
+// Wave-wide max / min / inclusive sum on the VALU (DPP row rotations and
+// shifts, row broadcasts and permlane swaps; no LDS traffic).
+__device__ __forceinline__ float wave_max(float v) {
+  v = max_row16(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float wave_min(float v) { return -wave_max(-v); }
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // ------------------------------------------------------------------ score kernel
 // grid.x: entry chunk (chunk_entries entries each), grid.y: query group
 // (QB consecutive queries of one sequence), 256 threads (4 waves).
@@ -290,14 +310,11 @@ __global__ __launch_bounds__(256) void k_index_score(
 
 // ------------------------------------------------------------------ block helpers
 
-// Inclusive scan across the block of one value per thread (kTopkThreads threads).
+// Inclusive scan across the block of one value per thread (kTopkThreads
+// threads); the wave sums are left in wsum[0 .. waves).
 __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* wsum) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_sum(v);
   if (lane == 63) wsum[wv] = v;
   __syncthreads();
   uint32_t add = 0;
@@ -412,12 +429,7 @@ __device__ void radix_threshold(TopkSmem& sm, int64_t count, Get get) {
       uint32_t h[4], mine = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) { h[j] = sm.h256[top - j]; mine += h[j]; }
-      uint32_t incl = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_up(incl, off);
-        if (lane >= off) incl += t;
-      }
+      const uint32_t incl = wave_incl_sum(mine);
       const uint32_t need = sm.need, excl = incl - mine;
       if (excl < need && incl >= need) {
         uint32_t above = excl;
@@ -454,8 +466,7 @@ __device__ __forceinline__ int wave_append(bool pred, int* counter) {
 }
 
 __device__ __forceinline__ float block_min(float v, float* red) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fminf(v, __shfl_xor(v, o));
+  v = wave_min(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float r = red[0];
@@ -465,8 +476,7 @@ __device__ __forceinline__ float block_min(float v, float* red) {
 }
 
 __device__ __forceinline__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+  v = wave_max(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float r = red[0];
@@ -646,37 +656,48 @@ __device__ bool select_by_groups(TopkSmem& sm, const float* __restrict__ srow, c
   }
   if (tid == 0) { sm.nsel = 0; sm.ncand = 0; }
   __syncthreads();
-  // their scores, one per lane, kGPT per thread per batch
-  const int total = ngrp * kGroup;
-  for (int base = 0; base < total; base += kGPT * kTopkThreads) {
-    float v[kGPT];
+  // their scores: each thread reads whole groups (4 x 16 bytes each), up to
+  // kGB groups per round with every load in flight, then appends the entries
+  // >= tau (one block scan per round).
+  constexpr int kGB = 4;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+  for (int base = 0; base < ngrp; base += kGB * kTopkThreads) {
+    float v[kGB][kGroup];
+    int64_t e0[kGB];
 #pragma unroll
-    for (int u = 0; u < kGPT; ++u) {
-      const int f = base + u * kTopkThreads + tid;
-      const int64_t e = f < total ? (int64_t)glist[f >> 4] * kGroup + (f & (kGroup - 1)) : n;
-      v[u] = e < n ? srow[e] : -INFINITY;
-    }
-    uint32_t take = 0, c = 0;
+    for (int u = 0; u < kGB; ++u) {
+      const int gi = base + u * kTopkThreads + tid;
+      e0[u] = gi < ngrp ? (int64_t)glist[gi] * kGroup : n;
+      if (e0[u] + kGroup <= n && vec_ok) {
 #pragma unroll
-    for (int u = 0; u < kGPT; ++u) {
-      const int f = base + u * kTopkThreads + tid;
-      const int64_t e = f < total ? (int64_t)glist[f >> 4] * kGroup + (f & (kGroup - 1)) : n;
-      const bool t = e < n && order_key(v[u]) >= tau_key;
-      take |= (uint32_t)t << u;
-      c += t;
+        for (int j = 0; j < kGroup; j += 4) {
+          const float4 t4 = *reinterpret_cast<const float4*>(srow + e0[u] + j);
+          v[u][j] = t4.x; v[u][j + 1] = t4.y; v[u][j + 2] = t4.z; v[u][j + 3] = t4.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) v[u][j] = (e0[u] + j < n) ? srow[e0[u] + j] : -INFINITY;
+      }
     }
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < kGB; ++u)
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) c += (e0[u] + j < n && order_key(v[u][j]) >= tau_key);
     const uint32_t ci = block_inclusive_scan(c, sm.wsum);
     int pos = sm.ncand + (int)(ci - c);
     const int added = (int)(sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3] + sm.wsum[4] + sm.wsum[5] +
                             sm.wsum[6] + sm.wsum[7]);
 #pragma unroll
-    for (int u = 0; u < kGPT; ++u) {
-      if (!((take >> u) & 1u)) continue;
-      const int f = base + u * kTopkThreads + tid;
-      const int64_t e = (int64_t)glist[f >> 4] * kGroup + (f & (kGroup - 1));
-      if (pos < kCandCap) sm.cand[pos] = composite(order_key(v[u]), e);
-      ++pos;
-    }
+    for (int u = 0; u < kGB; ++u)
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) {
+        const uint32_t key = order_key(v[u][j]);
+        if (e0[u] + j < n && key >= tau_key) {
+          if (pos < kCandCap) sm.cand[pos] = composite(key, e0[u] + j);
+          ++pos;
+        }
+      }
     __syncthreads();
     if (tid == 0) sm.ncand += added;
     __syncthreads();
