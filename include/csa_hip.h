@@ -140,7 +140,9 @@ csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B,
  *   idx_out  int32 [B, Tq, k]: selected entries in ascending order, then -1
  *   score_out  NULL, or float32 [B, Tq, N]: the scores (entries >= n(p)
  *            are left untouched)
- *   H_I 1..64; d_I 64 or 128; k 1..2048; ratio >= 1; N < 2^30.
+ *   H_I 1..64; d_I 64 or 128; k 1..2048; ratio >= 1; N < 2^30; B*Tq < 2^31.
+ *   q_idx and k_idx must be 16-byte aligned, k_scale 4-byte aligned
+ *   (CSA_ERR_SHAPE otherwise).
  * Scores must be finite (NaN selection order is undefined).
  */
 size_t indexer_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I,

@@ -25,9 +25,16 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags. The indexer's MFMA results feed VALU math at once:
+# the VGPR form of the MFMA saves an accumulator-register read per element.
+EXTRA = {
+    "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"   # host pass does not know the device feature: harmless
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l and l.strip())

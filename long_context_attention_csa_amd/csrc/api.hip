@@ -160,7 +160,7 @@ csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w, 
                         float* score_out, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   CSA_REQUIRE(is_dtype(qk_t), CSA_ERR_UNSUPPORTED, "indexer_topk: unknown dtype %d", (int)qk_t);
-  CSA_REQUIRE(B >= 0 && Tq >= 0 && N >= 0 && N < (int64_t(1) << 30), CSA_ERR_SHAPE,
+  CSA_REQUIRE(B >= 0 && Tq >= 0 && N >= 0 && N < (int64_t(1) << 30) && B * Tq < (int64_t(1) << 31), CSA_ERR_SHAPE,
               "indexer_topk: B=%lld Tq=%lld N=%lld", (long long)B, (long long)Tq, (long long)N);
   CSA_REQUIRE(H_I >= 1 && H_I <= 64, CSA_ERR_UNSUPPORTED, "indexer_topk: H_I %d (1..64)", H_I);
   CSA_REQUIRE(d_I == 64 || d_I == 128, CSA_ERR_UNSUPPORTED, "indexer_topk: d_I %d (64 or 128)", d_I);
@@ -173,6 +173,8 @@ csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w, 
   CSA_REQUIRE(q_idx && w && q_pos && idx_out, CSA_ERR_NULL, "indexer_topk: NULL tensor");
   CSA_REQUIRE(N == 0 || k_idx, CSA_ERR_NULL, "indexer_topk: k_idx is NULL");
   CSA_REQUIRE(!quant || (q_scale && (N == 0 || k_scale)), CSA_ERR_NULL, "indexer_topk: scales required");
+  CSA_REQUIRE(((uintptr_t)q_idx & 15) == 0 && ((uintptr_t)k_idx & 15) == 0 && ((uintptr_t)k_scale & 3) == 0,
+              CSA_ERR_SHAPE, "indexer_topk: q_idx and k_idx must be 16-byte aligned, k_scale 4-byte aligned");
   const size_t need = indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, qk_t);
   CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "indexer_topk: workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(launch_indexer_topk(q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio, k,

@@ -144,9 +144,10 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 // ------------------------------------------------------------------ misc
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-__device__ __forceinline__ int64_t visible(int64_t p, int32_t ratio, int64_t N) {
-  int64_t n = (p + 1) / ratio;
-  return n < N ? (n < 0 ? 0 : n) : N;
+__device__ __forceinline__ int64_t visible(int32_t p, int32_t ratio, int64_t N) {
+  if (p < 0) return 0;
+  const int64_t n = (int64_t)(((uint32_t)p + 1u) / (uint32_t)ratio);   // 32-bit divide
+  return n < N ? n : N;
 }
 
 // Kernel timer hook (defined in api.hip).

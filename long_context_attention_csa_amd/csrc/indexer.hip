@@ -37,6 +37,8 @@
 // Deterministic by construction (atomics only build sets, never orders).
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace csa {
 
 constexpr int kTopkThreads = 512;
@@ -305,6 +307,202 @@ __global__ __launch_bounds__(256) void k_index_score(
       load_batch(kA, sA, base);
       compute_batch(kA, sA, base);
     }
+  }
+}
+
+// ------------------------------------------------------------------ decode score kernel
+// One query per block row, quantised keys (fp8 / fp4), d_I = 128: the path
+// that streams a whole long-context key cache per query.
+//
+// Each wave owns NB batches of 64 consecutive entries (4 MFMA tiles of 16);
+// batch i of wave w starts at entry chunk + 64 * (w + 4 * i), so the block's
+// four waves read 256 contiguous entries per step. Loads of batch i + DEPTH - 1
+// are issued before batch i is computed (a register ring of DEPTH batches)
+// and every result stays in registers until the loop ends: on gfx9 one
+// counter tracks both loads and stores, so a store between prefetched loads
+// would make each wait drain the whole pipeline.
+//
+// After the 4 tiles of a batch, a reduce-scatter over the four lane rows
+// (two permlane32 swaps, one permlane16 swap) leaves lane l holding the
+// full weighted score of entry base + l: the fp8 entry scale is one
+// coalesced dword per lane, the score store is one 256-byte store per batch.
+// fp4 block scales are loaded the same way (one word of 4 E8M0 bytes per
+// entry, lane l = entry base + l) and transposed across the rows so lane
+// (col, g) holds, in byte u, the scale of K-block g of entry 16u + col; the
+// MFMA's scale byte select picks byte u for tile u.
+// fp8 operands use a K order shared by queries and keys: lane group g holds
+// bytes [16g, 16g + 16) and [64 + 16g, 64 + 16g + 16) of a row, so each of the
+// two loads of a tile reads 64 contiguous bytes of every entry.
+
+template <int FMT> struct DecBatch;
+template <> struct DecBatch<CSA_FP4_E2M1> {
+  i32x4 v[4];
+  uint32_t sc;           // scale word of entry base + lane
+};
+template <> struct DecBatch<CSA_FP8_E4M3> {
+  i32x4 lo[4], hi[4];
+  float sc;              // float32 scale of entry base + lane
+};
+
+// max(x, 0) as one integer max on the bit pattern (a set sign bit reads as a
+// negative integer; -0 and negatives give +0), free of the NaN-quieting
+// canonicalisation a float max carries.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Sum over the four lane rows of tile part[g], delivered to lane (col, g).
+__device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  const float s0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  const float s1 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// 4x4 byte transpose across the lane rows: in lane (col, r), byte c of the
+// input belongs to row c; the result's byte u is byte r of row u's input.
+__device__ __forceinline__ uint32_t transpose_rows_bytes(uint32_t w, int lane) {
+  const auto a = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  const uint32_t m = __builtin_amdgcn_perm(a[1], a[0], lane < 32 ? 0x05040100u : 0x07060302u);
+  const auto b = __builtin_amdgcn_permlane16_swap(m, m, false, false);
+  return __builtin_amdgcn_perm(b[1], b[0], ((lane >> 4) & 1) ? 0x07030501u : 0x06020400u);
+}
+
+template <int FMT, int HB, int NB, int DEPTH>
+__global__ __launch_bounds__(256) void k_index_score_dec(
+    const void* __restrict__ q_idx, const void* __restrict__ q_scale, const float* __restrict__ w,
+    const void* __restrict__ k_idx, const void* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
+    int64_t Tq, int64_t N, int H_I, int ratio, int64_t row_begin, float* __restrict__ sbase, int64_t srow0,
+    float* __restrict__ gbase, int64_t grow0) {
+  constexpr int DI = 128;
+  constexpr int RB = FMT == CSA_FP4_E2M1 ? DI / 2 : DI;    // bytes per key row
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t r = row_begin + blockIdx.y;                  // query row
+  const int64_t b = (int64_t)((uint32_t)r / (uint32_t)Tq);   // its sequence (rows < 2^31)
+  // Batch i of wave w in block x covers entries 64 * (w + 4 * (x + X * i)) ..
+  // + 63 (X = grid width): at step i the whole grid reads one contiguous window.
+  const int64_t X = gridDim.x;
+  auto batch_base = [&](int i) -> int64_t { return 64 * (wv + 4 * ((int64_t)blockIdx.x + X * i)); };
+  const int64_t e_begin = 256 * (int64_t)blockIdx.x;        // the block's first entry
+
+  // The key stream depends only on the block: its first loads are issued
+  // before anything else. Each batch addresses from a uniform base (clamped
+  // to N - 1) with 32-bit lane offsets; entries past N read entry N - 1 and
+  // entries past the query's visible count are masked at the store.
+  const uint8_t* krow = reinterpret_cast<const uint8_t*>(k_idx) + b * N * RB;
+  const uint8_t* srow_k = reinterpret_cast<const uint8_t*>(k_scale) + b * N * 4;
+  auto load = [&](DecBatch<FMT>& d, int i) {
+    const int64_t bw = 256 * ((int64_t)blockIdx.x + X * i);   // block's entries this step
+    const int64_t bb = bw < N - 1 ? bw : N - 1;               // uniform, <= N - 1
+    const uint32_t lim = (uint32_t)(N - 1 - bb < 255 ? N - 1 - bb : 255);
+    const uint8_t* kbat = krow + bb * RB;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t e = 64u * wv + 16u * u + (uint32_t)col;
+      e = e < lim ? e : lim;
+      const uint32_t off = e * RB + 16u * g;
+      if constexpr (FMT == CSA_FP4_E2M1) {
+        d.v[u] = *reinterpret_cast<const i32x4*>(kbat + off);
+      } else {
+        d.lo[u] = *reinterpret_cast<const i32x4*>(kbat + off);
+        d.hi[u] = *reinterpret_cast<const i32x4*>(kbat + off + 64);
+      }
+    }
+    uint32_t el = 64u * wv + (uint32_t)lane;
+    el = el < lim ? el : lim;
+    if constexpr (FMT == CSA_FP4_E2M1)
+      d.sc = reinterpret_cast<const uint32_t*>(srow_k + bb * 4)[el];
+    else
+      d.sc = reinterpret_cast<const float*>(srow_k + bb * 4)[el];
+  };
+  DecBatch<FMT> ring[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH - 1 && i < NB; ++i) load(ring[i], i);
+
+  const int64_t nvis = visible(q_pos[r], ratio, N);
+  if (e_begin >= nvis) {             // nothing visible in this chunk (uniform)
+    __builtin_amdgcn_s_waitcnt(0);   // drain the prefetched loads before leaving
+    return;
+  }
+  // query operands (A: head = lane % 16 within head block hb) and folded
+  // weights; padded heads (>= H_I) read head 0 and are zeroed
+  i32x4 qa[HB], qb[HB];
+  int qs8[HB];
+  float wq[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int hrow = hb * 16 + col;
+    const bool live = hrow < H_I;
+    const int64_t qr = r * H_I + (live ? hrow : 0);
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q_idx) + qr * RB;
+    const i32x4 z = {0, 0, 0, 0};
+    qa[hb] = *reinterpret_cast<const i32x4*>(qrow + 16 * g);
+    qa[hb] = live ? qa[hb] : z;
+    if constexpr (FMT == CSA_FP4_E2M1) {
+      const int sc = reinterpret_cast<const uint8_t*>(q_scale)[qr * (DI / 32) + g];
+      qs8[hb] = live ? sc : 127;
+    } else {
+      qb[hb] = *reinterpret_cast<const i32x4*>(qrow + 64 + 16 * g);
+      qb[hb] = live ? qb[hb] : z;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = hb * 16 + 4 * g + rr;
+      const int hs = h < H_I ? h : 0;
+      float wv_ = w[r * H_I + hs];
+      if constexpr (FMT == CSA_FP8_E4M3) wv_ *= reinterpret_cast<const float*>(q_scale)[r * H_I + hs];
+      wq[hb][rr] = h < H_I ? wv_ : 0.f;
+    }
+  }
+
+  auto tile = [&](const DecBatch<FMT>& d, uint32_t st, auto U) -> float {
+    constexpr int u = decltype(U)::value;
+    float part = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (FMT == CSA_FP4_E2M1) {
+        const i32x8 av = {qa[hb][0], qa[hb][1], qa[hb][2], qa[hb][3], 0, 0, 0, 0};
+        const i32x8 bv = {d.v[u][0], d.v[u][1], d.v[u][2], d.v[u][3], 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, qs8[hb], u, (int)st);
+      } else {
+        const i32x8 av = {qa[hb][0], qa[hb][1], qa[hb][2], qa[hb][3], qb[hb][0], qb[hb][1], qb[hb][2], qb[hb][3]};
+        const i32x8 bv = {d.lo[u][0], d.lo[u][1], d.lo[u][2], d.lo[u][3], d.hi[u][0], d.hi[u][1], d.hi[u][2], d.hi[u][3]};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) part = fmaf(wq[hb][rr], relu_bits(acc[rr]), part);
+    }
+    return part;
+  };
+
+  float out_s[NB], out_g[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    __builtin_amdgcn_sched_barrier(0);   // keep the ring: no load hoisted across batches
+    if (i + DEPTH - 1 < NB) load(ring[(i + DEPTH - 1) % DEPTH], i + DEPTH - 1);
+    const DecBatch<FMT>& d = ring[i % DEPTH];
+    uint32_t st = 0;
+    if constexpr (FMT == CSA_FP4_E2M1) st = transpose_rows_bytes(d.sc, lane);
+    const float p0 = tile(d, st, std::integral_constant<int, 0>{});
+    const float p1 = tile(d, st, std::integral_constant<int, 1>{});
+    const float p2 = tile(d, st, std::integral_constant<int, 2>{});
+    const float p3 = tile(d, st, std::integral_constant<int, 3>{});
+    float s = reduce_scatter4(p0, p1, p2, p3);
+    if constexpr (FMT == CSA_FP8_E4M3) s *= d.sc;
+    const bool ok = batch_base(i) + lane < nvis;
+    out_s[i] = s;
+    out_g[i] = max_row16(ok ? s : -INFINITY);
+  }
+  const int64_t G = (N + kGroup - 1) / kGroup;
+  float* srow = sbase + (r - srow0) * N;
+  float* grow = gbase + (r - grow0) * G;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int64_t e0 = batch_base(i);
+    if (e0 + lane < nvis) srow[e0 + lane] = out_s[i];
+    if (col == 0 && e0 + 16 * g < nvis) grow[(e0 + 16 * g) / kGroup] = out_g[i];
   }
 }
 
@@ -790,6 +988,22 @@ template <int FMT, int QB> struct ScoreCfg {
   static constexpr bool DBUF = false;
 };
 
+// Decode score kernel shape: 4 batches of 64 entries per wave, 2-deep ring
+// (sweep at the 1M-context fp4 and 262k-context fp8 decode shapes).
+constexpr int kDecNB = 4, kDecDepth = 2;
+
+template <int FMT>
+static void launch_score_dec(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
+                             const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
+                             int ratio, int64_t r0, float* sb, int64_t sr0, float* gb, int64_t gr0) {
+  switch (HB) {
+    case 1: k_index_score_dec<FMT, 1, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+    case 2: k_index_score_dec<FMT, 2, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+    case 3: k_index_score_dec<FMT, 3, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+    default: k_index_score_dec<FMT, 4, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+  }
+}
+
 template <int FMT, int DI, int HB, int QB>
 static void launch_score(dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w, const void* kk,
                          const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I, int ratio, int64_t g0,
@@ -842,7 +1056,19 @@ hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const flo
     // group maxima follow the pass's score rows in the workspace
     float* gb = reinterpret_cast<float*>(ws) + (size_t)p.max_rows_per_pass * (size_t)N;
     const int64_t gr0 = rlo;
-    if (N > 0) {
+    const bool dec = p.QB == 1 && d_I == 128 && (fmt == CSA_FP8_E4M3 || fmt == CSA_FP4_E2M1);
+    if (N > 0 && dec) {
+      // one query per block row: rows rlo .. rlo + (g1 - g0)
+      const dim3 grid((unsigned)cdiv(N, (int64_t)256 * kDecNB), (unsigned)(g1 - g0));
+      timer_before(CSA_KID_INDEX_SCORE, s);
+      if (fmt == CSA_FP8_E4M3)
+        launch_score_dec<CSA_FP8_E4M3>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
+      else
+        launch_score_dec<CSA_FP4_E2M1>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
+      hipError_t e = hipGetLastError();
+      timer_after(CSA_KID_INDEX_SCORE, s);
+      if (e != hipSuccess) return e;
+    } else if (N > 0) {
       const dim3 grid((unsigned)cdiv(N, p.chunk_entries), (unsigned)(g1 - g0));
       timer_before(CSA_KID_INDEX_SCORE, s);
       switch (fmt) {

@@ -158,6 +158,29 @@ def test_indexer_exact_grid_decode_group_path(fmt):
     assert np.array_equal(host(idx), want)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+@pytest.mark.parametrize("H_I", [19, 64])
+def test_indexer_exact_grid_decode_multi_query(fmt, H_I):
+    """Three queries per sequence (one query per score block row), padded head
+    blocks when H_I < 64, positions that leave most chunks invisible: exact
+    scores on the visible entries and bit-exact indices."""
+    B, Tq, N, d_I, k = 2, 3, 3001, 128, 64
+    if fmt == "fp4":
+        q_i, k_i = syn.fp4_grid(41, (B, Tq, H_I, d_I)), syn.fp4_grid(42, (B, N, d_I))
+    else:
+        q_i, k_i = syn.integers(41, (B, Tq, H_I, d_I), -4, 4), syn.integers(42, (B, N, d_I), -4, 4)
+    w = syn.grid_weights(43, (B, Tq, H_I))
+    q_pos = np.array([[4 * N + 5, 4 * 1100 + 2, 37], [4 * 2999, 4 * 17, 4 * 1024]], np.int32)
+    _print("indexer grid decode multi-query", fmt, H_I)
+    qc, qs, kc, ks = _grid_operands(fmt, q_i, k_i)
+    idx, sc = C.indexer_topk(qc, qs, dev(w), kc, ks, fmt, dev(q_pos, torch.int32), 4, k, d_I, want_scores=True)
+    scores, want = _oracle_topk(q_i, w, k_i, q_pos, 4, k)
+    got_s = host(sc)
+    vis = np.isfinite(scores)
+    assert np.array_equal(got_s[vis], scores[vis])
+    assert np.array_equal(host(idx), want)
+
+
 def test_indexer_normal_group_path_large_n():
     """N(0,1) operands, n = 70,000 entries, k = 1024 (group path): selection over
     the GPU's own scores is exact; float64 differences are certified ties."""
