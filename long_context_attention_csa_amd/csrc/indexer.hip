@@ -41,7 +41,7 @@
 
 namespace csa {
 
-constexpr int kTopkThreads = 512;
+constexpr int kTopkThreads = 1024;
 constexpr int kHistBits = 13;
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandCap = 8192;            // candidates held in LDS
@@ -528,7 +528,7 @@ struct TopkSmem {
   uint32_t h256[256];
   uint32_t wsum[16];
   unsigned long long red_and[kTopkThreads / 64], red_or[kTopkThreads / 64];
-  float redf[kTopkThreads / 64];
+  float redf[kTopkThreads / 64], redg[kTopkThreads / 64];
   int nsel, ncand, ngrp;
   uint32_t bin, need;
   unsigned long long prefix, mask, thresh;
@@ -786,130 +786,266 @@ __device__ void select_full_row(TopkSmem& sm, const float* __restrict__ srow, in
   }
 }
 
-// Group path. tau is a lower bound of the k-th largest group maximum: the
-// maxima are binned linearly between their minimum and maximum (a monotone
-// map, so bins above the boundary bin hold only larger values), and tau is
-// the smallest maximum in the bin that holds the k-th largest. At least k
-// groups have maximum >= tau, so at least k entries are >= tau and the top-k
-// lies among them. Each thread loads its kGPT maxima into registers once
-// (all loads in flight); qualifying groups are listed in LDS with one block
-// scan; their scores are then read flat, kGPT per thread per batch, and the
-// entries >= tau appended as candidates. Returns false (nothing written to
-// the output) if the row has more maxima than the registers hold or the
-// candidates do not fit in LDS.
-constexpr int kGPT = 32;
+// Group path (one row, kTopkThreads = 1024 threads).
+//
+// Let G_k be the k-th largest group maximum. The k largest maxima are k
+// distinct entries >= G_k, so the k-th largest entry K* is >= G_k. The maxima
+// are binned linearly between their minimum and maximum; the map is monotone,
+// so with b the bin of G_k every entry of the top-k has bin >= b and lies in a
+// group whose maximum has bin >= b. Those groups are listed in index order
+// (one block scan); their entries with bin >= b are the candidates, again
+// compacted in index order. A second linear histogram over the candidates'
+// range finds the bin b2 that holds the k-th largest candidate; candidates in
+// higher bins are taken, and the ones in bin b2 are ranked among themselves
+// by (score descending, index ascending). The chosen candidates are still in
+// index order, so one more block scan writes the output.
+//
+// Each thread holds 16 consecutive group maxima in registers; 4096-bin
+// histograms; up to 4096 listed groups and 4096 candidates. Returns false
+// (nothing written) when the row does not fit these bounds (heavy ties).
+constexpr int kGPT = 16;                     // group maxima per thread
+constexpr int kGBins = 4096;                 // bins per histogram
+constexpr int kMaxGrp = 4096;                // listed groups
+constexpr int kMaxCand = 4096;               // candidates (cand[0 .. 4096))
+
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Exclusive scan of one value per thread; returns the exclusive prefix and
+// the block total. One barrier: the caller must pass another barrier before
+// wsum is written again.
+__device__ __forceinline__ uint32_t block_scan_excl(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(v);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  uint32_t add = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkThreads / 64; ++i) {
+    const uint32_t x = wsum[i];
+    add += i < wv ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  return add + incl - v;
+}
+
+// Boundary bin of the target-th largest element of hist[0 .. kGBins): sets
+// sm.bin and sm.need (target minus the count in higher bins). Two barriers.
+__device__ __forceinline__ void find_bin4096(TopkSmem& sm, const uint32_t* hist, uint32_t target) {
+  constexpr int BPT = kGBins / kTopkThreads;
+  const int top = kGBins - BPT * (int)threadIdx.x;    // owns bins [top - BPT, top)
+  uint32_t h[BPT], mine = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) { h[i] = hist[top - 1 - i]; mine += h[i]; }
+  uint32_t total;
+  const uint32_t excl = block_scan_excl(mine, sm.wsum, total);
+  if (excl < target && excl + mine >= target) {
+    uint32_t above = excl;
+    int i = 0;
+    for (; i < BPT - 1; ++i) {
+      if (above + h[i] >= target) break;
+      above += h[i];
+    }
+    sm.bin = (uint32_t)(top - 1 - i);
+    sm.need = target - above;
+  }
+  __syncthreads();
+}
+
+// a[j] for a register array a[0 .. 16) and a lane-varying j, as an OR of
+// equality-masked bit patterns (a form that stays in registers; an indexed
+// access would move the array to scratch memory).
+__device__ __forceinline__ float pick16(const float (&a)[16], int j) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r |= (uint32_t)(-(int32_t)(i == j)) & __float_as_uint(a[i]);
+  return __uint_as_float(r);
+}
 
 __device__ bool select_by_groups(TopkSmem& sm, const float* __restrict__ srow, const float* __restrict__ grow,
-                                 int64_t n, int64_t m, int k) {
-  const int tid = threadIdx.x;
+                                 int64_t n, int64_t m, int k, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (m > (int64_t)kGPT * kTopkThreads) return false;
+  uint32_t* hist1 = sm.hist;                    // group-maximum histogram, then the group list
+  uint32_t* hist2 = sm.hist + kGBins;           // candidate histogram
+  int* glist = reinterpret_cast<int*>(sm.hist);
+
+  // 1. this thread's 16 consecutive group maxima (nv of them valid)
   float gv[kGPT];
+  const int g0 = kGPT * tid;
+  const int mi = (int)m, ni = (int)n;                    // m <= 16384, n < 2^30
+  const int nv = mi - g0 < 0 ? 0 : (mi - g0 > kGPT ? kGPT : mi - g0);
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(grow) & 15) == 0;
+  if (vec_ok && nv == kGPT) {
 #pragma unroll
-  for (int j = 0; j < kGPT; ++j) {
-    const int gi = tid + j * kTopkThreads;
-    gv[j] = gi < m ? grow[gi] : 0.f;
+    for (int j = 0; j < kGPT; j += 4) {
+      const float4 t4 = *reinterpret_cast<const float4*>(grow + g0 + j);
+      gv[j] = t4.x; gv[j + 1] = t4.y; gv[j + 2] = t4.z; gv[j + 3] = t4.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kGPT; ++j) gv[j] = j < nv ? grow[g0 + j] : 0.f;
   }
+  // 2. range of the maxima; clear both histograms meanwhile
+#pragma unroll
+  for (int i = tid; i < 2 * kGBins; i += kTopkThreads) sm.hist[i] = 0u;
+  if (tid == 0) sm.nsel = 0;
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kGPT; ++j)
-    if (tid + j * kTopkThreads < m) { lo = fminf(lo, gv[j]); hi = fmaxf(hi, gv[j]); }
-  for (int i = tid; i < kHistBins; i += kTopkThreads) sm.hist[i] = 0;
-  lo = block_min(lo, sm.redf);
-  hi = block_max(hi, sm.redf);
-  const float inv = hi > lo ? (float)(kHistBins - 1) / (hi - lo) : 0.f;
+  for (int j = 0; j < kGPT; ++j) {
+    lo = j < nv ? fminf(lo, gv[j]) : lo;
+    hi = j < nv ? fmaxf(hi, gv[j]) : hi;
+  }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lane == 0) { sm.redf[wv] = lo; sm.redg[wv] = hi; }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) { lo = fminf(lo, sm.redf[w]); hi = fmaxf(hi, sm.redg[w]); }
+  const float inv = hi > lo ? (float)kGBins / (hi - lo) : 0.f;
   auto bin_of = [&](float v) -> int {
     const float t = (v - lo) * inv;
-    return t >= (float)(kHistBins - 1) ? kHistBins - 1 : (int)t;
+    return t >= (float)(kGBins - 1) ? kGBins - 1 : (int)t;    // monotone in v
   };
-#pragma unroll
-  for (int j = 0; j < kGPT; ++j)
-    if (tid + j * kTopkThreads < m) atomicAdd(&sm.hist[bin_of(gv[j])], 1u);
-  __syncthreads();
-  find_bucket(sm, (uint32_t)k);
-  const int b = (int)sm.bin;
-  float tmin = INFINITY;
-#pragma unroll
-  for (int j = 0; j < kGPT; ++j)
-    if (tid + j * kTopkThreads < m && bin_of(gv[j]) == b) tmin = fminf(tmin, gv[j]);
-  const float tau = block_min(tmin, sm.redf);
-  const uint32_t tau_key = order_key(tau);
-  // list the qualifying groups (the LDS histogram area is free now)
-  int* glist = reinterpret_cast<int*>(sm.hist);
-  uint32_t qual = 0, cnt = 0;
+  // 3. histogram of the maxima (bins kept: -1 for invalid slots)
+  int bn[kGPT];
 #pragma unroll
   for (int j = 0; j < kGPT; ++j) {
-    const bool q = tid + j * kTopkThreads < m && order_key(gv[j]) >= tau_key;
-    qual |= (uint32_t)q << j;
-    cnt += q;
+    bn[j] = j < nv ? bin_of(gv[j]) : -1;
+    if (j < nv) atomicAdd(&hist1[bn[j]], 1u);
   }
-  const uint32_t incl = block_inclusive_scan(cnt, sm.wsum);
-  const int ngrp = (int)(sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3] + sm.wsum[4] + sm.wsum[5] +
-                         sm.wsum[6] + sm.wsum[7]);
-  if (ngrp > kHistBins) return false;      // uniform across the block
-  {
-    int pos = (int)(incl - cnt);
-#pragma unroll
-    for (int j = 0; j < kGPT; ++j)
-      if ((qual >> j) & 1u) glist[pos++] = tid + j * kTopkThreads;
-  }
-  if (tid == 0) { sm.nsel = 0; sm.ncand = 0; }
   __syncthreads();
-  // their scores: each thread reads whole groups (4 x 16 bytes each), up to
-  // kGB groups per round with every load in flight, then appends the entries
-  // >= tau (one block scan per round).
-  constexpr int kGB = 4;
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
-  for (int base = 0; base < ngrp; base += kGB * kTopkThreads) {
-    float v[kGB][kGroup];
-    int64_t e0[kGB];
+  // 4. bin of the k-th largest maximum
+  find_bin4096(sm, hist1, (uint32_t)k);
+  const int b = (int)sm.bin;
+  // 5. groups with bin >= b, listed in index order (hist1 is free now); tau,
+  //    the smallest of their maxima, is <= G_k <= K*: entries >= tau are
+  //    exactly the entries with bin >= b, a superset of the top-k
+  uint32_t qual = 0;
+  float tmin = INFINITY;
 #pragma unroll
-    for (int u = 0; u < kGB; ++u) {
-      const int gi = base + u * kTopkThreads + tid;
-      e0[u] = gi < ngrp ? (int64_t)glist[gi] * kGroup : n;
-      if (e0[u] + kGroup <= n && vec_ok) {
+  for (int j = 0; j < kGPT; ++j) {
+    const bool q = bn[j] >= b;
+    qual |= (uint32_t)q << j;
+    tmin = q ? fminf(tmin, gv[j]) : tmin;
+  }
+  tmin = wave_min(tmin);
+  if (lane == 0) sm.redf[wv] = tmin;
+  uint32_t ngrp;
+  uint32_t pos = block_scan_excl((uint32_t)__popc(qual), sm.wsum, ngrp);   // its barrier also publishes redf
+  if (ngrp > (uint32_t)kMaxGrp) return false;            // uniform
+  float tau = INFINITY;
 #pragma unroll
-        for (int j = 0; j < kGroup; j += 4) {
-          const float4 t4 = *reinterpret_cast<const float4*>(srow + e0[u] + j);
-          v[u][j] = t4.x; v[u][j + 1] = t4.y; v[u][j + 2] = t4.z; v[u][j + 3] = t4.w;
-        }
+  for (int w = 0; w < kTopkThreads / 64; ++w) tau = fminf(tau, sm.redf[w]);
+  for (uint32_t qm = qual; qm; qm &= qm - 1u) glist[pos++] = g0 + __ffs((int)qm) - 1;
+  __syncthreads();
+  // 6. candidates: entries >= tau of the listed groups, in index order. Per
+  //    round of up to 2048 groups every thread takes 0-2 consecutive ones.
+  const bool svec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+  uint32_t ncand = 0;
+  for (uint32_t base = 0; base < ngrp; base += 2 * kTopkThreads) {
+    const uint32_t cr = ngrp - base < 2u * kTopkThreads ? ngrp - base : 2u * kTopkThreads;
+    const uint32_t ga = base + (uint32_t)tid * cr / kTopkThreads, gb = base + ((uint32_t)tid + 1) * cr / kTopkThreads;
+    float va[kGroup], vb[kGroup];
+    const int ea = ga < gb ? glist[ga] * kGroup : ni;
+    const int eb = ga + 1 < gb ? glist[ga + 1] * kGroup : ni;
+    if (svec && ea + kGroup <= ni) {
+#pragma unroll
+      for (int j = 0; j < kGroup; j += 4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(srow + ea + j);
+        va[j] = t4.x; va[j + 1] = t4.y; va[j + 2] = t4.z; va[j + 3] = t4.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) va[j] = ea + j < ni ? srow[ea + j] : -INFINITY;
+    }
+    if (svec && eb + kGroup <= ni) {
+#pragma unroll
+      for (int j = 0; j < kGroup; j += 4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(srow + eb + j);
+        vb[j] = t4.x; vb[j + 1] = t4.y; vb[j + 2] = t4.z; vb[j + 3] = t4.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j) vb[j] = eb + j < ni ? srow[eb + j] : -INFINITY;
+    }
+    uint32_t ma = 0, mb = 0;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {       // -inf past n fails
+      ma |= (uint32_t)(va[j] >= tau) << j;
+      mb |= (uint32_t)(vb[j] >= tau) << j;
+    }
+    uint32_t added;
+    uint32_t p = ncand + block_scan_excl((uint32_t)(__popc(ma) + __popc(mb)), sm.wsum, added);
+    for (uint32_t mk = ma; mk; mk &= mk - 1u) {
+      const int j = __ffs((int)mk) - 1;
+      if (p < (uint32_t)kMaxCand) sm.cand[p] = composite(order_key(pick16(va, j)), ea + j);
+      ++p;
+    }
+    for (uint32_t mk = mb; mk; mk &= mk - 1u) {
+      const int j = __ffs((int)mk) - 1;
+      if (p < (uint32_t)kMaxCand) sm.cand[p] = composite(order_key(pick16(vb, j)), eb + j);
+      ++p;
+    }
+    ncand += added;
+    __syncthreads();
+  }
+  if (ncand > (uint32_t)kMaxCand) return false;          // uniform
+  // 7. histogram of the candidates over [tau, hi]
+  const float inv2 = hi > tau ? (float)kGBins / (hi - tau) : 0.f;
+  auto bin2_of = [&](uint32_t key) -> int {
+    const float t = (key_value(key) - tau) * inv2;
+    return t >= (float)(kGBins - 1) ? kGBins - 1 : (int)t;
+  };
+  constexpr int CPT = kMaxCand / kTopkThreads;            // candidates per thread (consecutive)
+  const uint32_t per = (ncand + kTopkThreads - 1) / kTopkThreads;
+  unsigned long long cv[CPT];
+  int cb[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const uint32_t ci = per * tid + j;
+    const bool ok = j < (int)per && ci < ncand;
+    cv[j] = ok ? sm.cand[ci] : 0ull;
+    cb[j] = ok ? bin2_of((uint32_t)(cv[j] >> 32)) : -1;
+    if (ok) atomicAdd(&hist2[cb[j]], 1u);
+  }
+  __syncthreads();
+  find_bin4096(sm, hist2, (uint32_t)k);
+  const int b2 = (int)sm.bin;
+  const uint32_t need2 = sm.need;
+  // 8. rank the candidates of bin b2 among themselves (list at cand[kMaxCand ..))
+  unsigned long long* blist = sm.cand + kMaxCand;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int slot = wave_append(cb[j] == b2, &sm.nsel);
+    if (slot >= 0) blist[slot] = cv[j];
+  }
+  __syncthreads();
+  const int nb2 = sm.nsel;
+  uint32_t take = 0, tcnt = 0;
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    bool t = cb[j] > b2;
+    if (cb[j] == b2) {
+      if ((uint32_t)nb2 == need2) {
+        t = true;
       } else {
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) v[u][j] = (e0[u] + j < n) ? srow[e0[u] + j] : -INFINITY;
+        uint32_t rank = 0;
+        for (int i = 0; i < nb2; ++i) rank += blist[i] > cv[j];
+        t = rank < need2;
       }
     }
-    uint32_t c = 0;
-#pragma unroll
-    for (int u = 0; u < kGB; ++u)
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) c += (e0[u] + j < n && order_key(v[u][j]) >= tau_key);
-    const uint32_t ci = block_inclusive_scan(c, sm.wsum);
-    int pos = sm.ncand + (int)(ci - c);
-    const int added = (int)(sm.wsum[0] + sm.wsum[1] + sm.wsum[2] + sm.wsum[3] + sm.wsum[4] + sm.wsum[5] +
-                            sm.wsum[6] + sm.wsum[7]);
-#pragma unroll
-    for (int u = 0; u < kGB; ++u)
-#pragma unroll
-      for (int j = 0; j < kGroup; ++j) {
-        const uint32_t key = order_key(v[u][j]);
-        if (e0[u] + j < n && key >= tau_key) {
-          if (pos < kCandCap) sm.cand[pos] = composite(key, e0[u] + j);
-          ++pos;
-        }
-      }
-    __syncthreads();
-    if (tid == 0) sm.ncand += added;
-    __syncthreads();
+    take |= (uint32_t)t << j;
+    tcnt += t;
   }
-  const int ncand = sm.ncand;
-  if (ncand > kCandCap) return false;
-  if (tid == 0) {
-    sm.prefix = 0;
-    sm.mask = 0;
-    sm.need = (uint32_t)k;
-    sm.done = 0;
-  }
-  __syncthreads();
-  take_top_candidates(sm, ncand);
+  // 9. write the chosen indices in ascending order
+  uint32_t nout;
+  uint32_t o = block_scan_excl(tcnt, sm.wsum, nout);
+#pragma unroll
+  for (int j = 0; j < CPT; ++j)
+    if ((take >> j) & 1u) out[o++] = composite_index(cv[j]);
   return true;
 }
 
@@ -932,9 +1068,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float* __res
   const float* srow = sbase + (r - srow0) * N;
   const float* grow = gbase + (r - grow0) * G;
   const int64_t m = (n + kGroup - 1) / kGroup;
-  bool done = false;
-  if (m >= (int64_t)kGroupFactor * k) done = select_by_groups(sm, srow, grow, n, m, k);
-  if (!done) select_full_row(sm, srow, n, k);
+  if (m >= (int64_t)kGroupFactor * k && select_by_groups(sm, srow, grow, n, m, k, out)) return;
+  __syncthreads();   // the group path may have been left part way: LDS is reused
+  select_full_row(sm, srow, n, k);
   __syncthreads();
   write_sorted(sm, k, n, out);
 }
