@@ -345,6 +345,16 @@ constexpr int kSelChunk = 1024;     // selected indices staged in LDS at a time
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kD + ((chunk ^ (row & 7)) << 3); }
 
+// One global_load_lds_dwordx4: each lane's 16 bytes at src go to LDS address
+// lds_base + 16 * lane. Written as asm so that the compiler does not treat it
+// as an LDS store: it would otherwise drain every outstanding load before
+// each later LDS access or barrier (it cannot tell the ring slots apart),
+// which serialises the gather pipeline. Completion is tracked explicitly with
+// wait_vm() followed by a barrier before a slot is read. No register outputs.
+__device__ __forceinline__ void gather_lds16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
+}
+
 template <int N_OUT>
 __device__ __forceinline__ void wait_vm() {
   // s_waitcnt vmcnt(N_OUT), leaving expcnt and lgkmcnt unconstrained
@@ -361,22 +371,25 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <bool SPARSE, int NW, int HPW, int NBUF>
-__global__ __launch_bounds__(NW * 64, 2) void k_attn16(
+template <bool SPARSE, int NW, int HPW, int NBUF, int TS>
+__global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ x_win, const int32_t* __restrict__ win_start, const float* __restrict__ sink,
     const int32_t* __restrict__ q_pos, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio,
     float scale, int S, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-  constexpr int NT = NW * 64;
+  constexpr int NWT = NW * TS;                    // waves: TS streams of NW head waves
+  constexpr int NT = NWT * 64;
   constexpr int LPT = (kKT * kD * 2 / 16) / NT;   // 16-byte gathers per thread per tile
+  static_assert(NBUF % TS == 0 && NBUF > TS, "ring holds whole tile groups plus prefetch");
   __shared__ __align__(16) uint16_t ring[NBUF][kKT * kD];
   __shared__ int tvalid[NBUF][kKT];
   __shared__ int tbad[NBUF];
   __shared__ int sidx[SPARSE ? kSelChunk : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0 .. NWT-1: gathers
+  const int hw = wv % NW, ts = wv / NW;                      // head wave, tile stream
   const int g = lane >> 4, col = lane & 15;
   const int64_t r = blockIdx.x;
   const int hg = blockIdx.y / S, sp = blockIdx.y % S;
@@ -395,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
   const int64_t kbeg = (int64_t)sp * chunk;
   const int64_t kend = (kbeg + chunk) < nk ? (kbeg + chunk) : nk;
 
-  const int h0 = hg * (NW * 16 * HPW) + wv * 16 * HPW;
+  const int h0 = hg * (NW * 16 * HPW) + hw * 16 * HPW;
   Frag<uint16_t> qf[HPW][kD / 32];
 #pragma unroll
   for (int hb = 0; hb < HPW; ++hb) {
@@ -406,8 +419,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
   // Logits are kept in base 2 (log2(e) folded into the scale) so each
   // probability is one v_exp_f32.
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  constexpr float kLazy = 8.f;   // headroom of the lazily raised running max (base 2)
   const float scale2 = scale * kLog2e;
-  const bool has_sink = (sink != nullptr) && sp == 0;
+  const bool has_sink = (sink != nullptr) && sp == 0 && ts == 0;
   float m[HPW], lsum[HPW];
   f32x4 O[HPW][kD / 16];
 #pragma unroll
@@ -417,6 +431,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // The gathers are invisible to the compiler's wait counting, so the query
+  // loads must be complete before the first gather is issued (a wait placed
+  // at their first use could not count the gathers behind them). The sparse
+  // path waits after its index staging below, which covers both.
+  if (!SPARSE) wait_vm<0>();
   const uint16_t* dummy = q + r * H * kD;   // any readable row; its tile rows are zeroed
   const uint16_t* kvb = kv + b * N * kD;
   const uint16_t* xwb = x_win + b * T_win * kD;
@@ -430,6 +449,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
         const int64_t ki = c0 + i;
         sidx[i] = ki < n_sel ? idx[r * k + ki] : -1;
       }
+      wait_vm<0>();   // every thread: the query and index loads are done before any gather
       __syncthreads();
     }
     const int ntiles = (clen + kKT - 1) / kKT;
@@ -439,7 +459,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
       bool bad = false;
 #pragma unroll
       for (int j = 0; j < LPT; ++j) {
-        const int row = (j * NW + wv) * 4 + (lane >> 4);          // 4 rows per wave instruction
+        const int row = (j * NWT + wv) * 4 + (lane >> 4);         // 4 rows per wave instruction
         const int cs = lane & 15;
         const int kk = t * kKT + row;                              // key within the section
         const int64_t ki = c0 + kk;
@@ -455,8 +475,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
         if (cs == 0) tvalid[slot][row] = src != nullptr;
         bad |= src == nullptr;
         const uint16_t* gsrc = (src ? src : dummy) + ((cs ^ (row & 7)) << 3);
-        __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(base + (j * NW + wv) * 4 * kD),
-                                         16, 0, 0);
+        gather_lds16(gsrc, (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
       }
       if (__ballot(bad)) {
         if (lane == 0) atomicOr(&tbad[slot], 1);
@@ -464,48 +483,64 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
     };
     for (int i = tid; i < NBUF; i += NT) tbad[i] = 0;
     __syncthreads();
+    // Tiles are taken TS at a time (stream ts computes tile t0 + ts); the
+    // gathers of the next NBUF - TS tiles stay in flight meanwhile.
 #pragma unroll
-    for (int t = 0; t < NBUF - 1; ++t)
+    for (int t = 0; t < NBUF - TS; ++t)
       if (t < ntiles) issue(t);
 
-    for (int t = 0; t < ntiles; ++t) {
-      const int slot = t % NBUF;
-      if (t + NBUF - 1 < ntiles) {
-        issue(t + NBUF - 1);
-        wait_vm<(NBUF - 1) * LPT>();
-      } else {
-        wait_vm<0>();
-      }
+    for (int t0 = 0; t0 < ntiles; t0 += TS) {
+#pragma unroll
+      for (int j = 0; j < TS; ++j)
+        if (t0 + NBUF - TS + j < ntiles) issue(t0 + NBUF - TS + j);
+      if (t0 + NBUF - 1 < ntiles) wait_vm<(NBUF - TS) * LPT>();
+      else wait_vm<0>();
       __syncthreads();
-      uint16_t* tile = ring[slot];
-      if (tbad[slot]) {   // rows without a key: clear them so 0 * garbage cannot poison O
-        for (int i = tid; i < kKT * 16; i += NT) {
-          const int row = i >> 4;
-          if (!tvalid[slot][row]) *reinterpret_cast<i32x4*>(tile + row * kD + ((i & 15) << 3)) = i32x4{0, 0, 0, 0};
+      bool cleared = false;
+#pragma unroll
+      for (int j = 0; j < TS; ++j) {
+        const int sl = (t0 + j) % NBUF;
+        if (t0 + j < ntiles && tbad[sl]) {   // rows without a key: clear them so 0 * garbage cannot poison O
+          cleared = true;
+          for (int i = tid; i < kKT * 16; i += NT) {
+            const int row = i >> 4;
+            if (!tvalid[sl][row]) *reinterpret_cast<i32x4*>(ring[sl] + row * kD + ((i & 15) << 3)) = i32x4{0, 0, 0, 0};
+          }
         }
-        __syncthreads();
       }
+      if (cleared) __syncthreads();   // uniform: tbad is read by every thread
+      const int t = t0 + ts;
+      if (t < ntiles) {   // uniform per wave
+      const int slot = t % NBUF;
+      uint16_t* tile = ring[slot];
       const int nt = (clen - t * kKT) < kKT ? (clen - t * kKT) : kKT;
 
-      // ---- S^T = K Q^T for 4 blocks of 16 keys
+      // ---- S^T = K Q^T for 4 blocks of 16 keys: 8 independent accumulator
+      // chains (key block x head block) over the 4 d-chunks. Logits stay
+      // unscaled here; the scale enters the exponent below.
       float s[HPW][4][4];
+      {
+        f32x4 acc[4][HPW];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        f32x4 acc[HPW];
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int hb = 0; hb < HPW; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int row = 16 * kb + col;
+          for (int hb = 0; hb < HPW; ++hb) acc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kD / 32; ++ks) {
-          Frag<uint16_t> a;
-          a.load(tile + swz(row, 4 * ks + g));
+          Frag<uint16_t> a[4];
 #pragma unroll
-          for (int hb = 0; hb < HPW; ++hb) acc[hb] = mma8(a, qf[hb][ks], acc[hb]);
+          for (int kb = 0; kb < 4; ++kb) a[kb].load(tile + swz(16 * kb + col, 4 * ks + g));
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) acc[kb][hb] = mma8(a[kb], qf[hb][ks], acc[kb][hb]);
         }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = acc[hb][rr] * scale2;
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = acc[kb][hb][rr];
       }
       if (nt < kKT || tbad[slot]) {   // uniform: only partial or holed tiles are masked
 #pragma unroll
@@ -519,36 +554,44 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
             }
           }
       }
-      // ---- online softmax (per head = per column)
+      // ---- online softmax (per head = per column), base-2 logits scale2 * s.
+      // Lazy rescaling: probabilities are taken against the running reference
+      // max m[hb] while no logit of the tile exceeds it by more than kLazy, so
+      // P, O and l grow by at most 2^kLazy (exact in float32, and bf16 keeps
+      // its relative precision); only a larger logit raises m (the column max
+      // over the 4 lane rows, by permlane swaps) and rescales O and l. The
+      // result O / l and the log-sum m + log2(l) do not depend on m.
 #pragma unroll
       for (int hb = 0; hb < HPW; ++hb) {
-        float tmax = -INFINITY;
+        float lmax = s[hb][0][0];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) tmax = fmaxf(tmax, s[hb][kb][rr]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = fmaxf(m[hb], tmax);
-        const bool live = mnew != -INFINITY;
-        const float msafe = live ? mnew : 0.f;
+          for (int rr = 0; rr < 4; ++rr) lmax = fmaxf(lmax, s[hb][kb][rr]);
+        const float lm2 = lmax * scale2;
+        if (__ballot(lm2 > m[hb] + kLazy)) {   // wave-uniform
+          const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm2), __float_as_uint(lm2), false, false);
+          const float c1 = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+          const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(c1), __float_as_uint(c1), false, false);
+          const float cmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+          const float mnew = fmaxf(m[hb], cmax);
+          const float alpha = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mnew);
+          lsum[hb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
+          m[hb] = mnew;
+        }
+        const float negm = m[hb] == -INFINITY ? 0.f : -m[hb];
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const float pv = __builtin_amdgcn_exp2f(s[hb][kb][rr] - msafe);   // exp2(-inf) = 0
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[hb][kb][rr], scale2, negm));   // exp2(-inf) = 0
             s[hb][kb][rr] = pv;
             psum += pv;
           }
-        if (__ballot(mnew != m[hb])) {   // rescale only when some running max moved
-          const float alpha = live ? __builtin_amdgcn_exp2f(m[hb] - mnew) : 1.f;
-          lsum[hb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
-        }
         lsum[hb] += psum;
-        m[hb] = mnew;
       }
       // ---- O^T += V^T P^T. K-slot t of lane group g is key 4g+t (t < 4) or
       // 16+4g+(t-4) (t >= 4) of the 32-key group; the transposed reads deliver
@@ -582,7 +625,43 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attn16(
           for (int hb = 0; hb < HPW; ++hb) O[hb][db] = mma8(va, pf[hb], O[hb][db]);
         }
       }
-      __syncthreads();   // the slot is refilled by a later issue()
+      }   // t < ntiles
+      __syncthreads();   // the slots are refilled by later issue() calls
+    }
+  }
+
+  if constexpr (TS > 1) {
+    // Stream 1 hands (O, m, lsum) to stream 0 through the (now idle) ring, in
+    // lane order; stream 0 merges: every value is rescaled to the larger max.
+    static_assert(TS == 2, "two tile streams");
+    static_assert(NW * HPW * (kD / 16) * 64 * 4 * 4 + NW * HPW * 64 * 2 * 4 <= NBUF * kKT * kD * 2, "exchange fits");
+    float* xo = reinterpret_cast<float*>(&ring[0][0]);
+    float* xml = xo + NW * HPW * (kD / 16) * 64 * 4;
+    if (ts == 1) {
+#pragma unroll
+      for (int hb = 0; hb < HPW; ++hb) {
+#pragma unroll
+        for (int db = 0; db < kD / 16; ++db)
+          *reinterpret_cast<f32x4*>(xo + (((hw * HPW + hb) * (kD / 16) + db) * 64 + lane) * 4) = O[hb][db];
+        xml[((hw * HPW + hb) * 64 + lane) * 2] = m[hb];
+        xml[((hw * HPW + hb) * 64 + lane) * 2 + 1] = lsum[hb];
+      }
+    }
+    __syncthreads();
+    if (ts == 1) return;
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+      const float m1 = xml[((hw * HPW + hb) * 64 + lane) * 2], l1 = xml[((hw * HPW + hb) * 64 + lane) * 2 + 1];
+      const float mm = fmaxf(m[hb], m1);
+      const float a0 = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+      lsum[hb] = lsum[hb] * a0 + l1 * a1;
+      m[hb] = mm;
+#pragma unroll
+      for (int db = 0; db < kD / 16; ++db) {
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + (((hw * HPW + hb) * (kD / 16) + db) * 64 + lane) * 4);
+        O[hb][db] = O[hb][db] * a0 + o1 * a1;
+      }
     }
   }
 
@@ -659,19 +738,16 @@ static AttnShape pick_shape(int H) {
 }
 
 // Key splits per (row, head group): a fixed function of the shapes, so the
-// merge order (and the result) never depends on timing. Enough splits that a
-// split holds at most one bf16 super-tile of keys (one round of gathers), and
-// more while the grid is small, down to 128 keys per split.
+// merge order (and the result) never depends on timing. About one block per
+// compute unit, with at least kMinSplitKeys keys per split.
+constexpr int64_t kMinSplitKeys = 128;
 int attn_splits(int64_t rows, int H, int64_t nk_max) {
   const AttnShape sh = pick_shape(H);
   const int64_t base = rows * (H / (16 * sh.nw * sh.hpw));
   if (base >= 256) return 1;
-  const int64_t super_keys = 128;   // bf16 super-tile size
-  int64_t s = cdiv(nk_max, super_keys);
   const int64_t fill = cdiv(256, base);
-  const int64_t by_keys = nk_max / 128 > 1 ? nk_max / 128 : 1;
-  const int64_t more = fill < by_keys ? fill : by_keys;
-  if (s < more) s = more;
+  const int64_t by_keys = nk_max / kMinSplitKeys > 1 ? nk_max / kMinSplitKeys : 1;
+  int64_t s = fill < by_keys ? fill : by_keys;
   if (s > 128) s = 128;
   return (int)(s < 1 ? 1 : s);
 }
@@ -682,18 +758,25 @@ size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max) {
   return (size_t)rows * H * S * (kD + 2) * 4;
 }
 
-constexpr int kRing = 4;   // tiles in flight per block (bf16 path)
+constexpr int kRing = 4;   // ring slots per block (bf16 path, one tile stream)
+constexpr int kRing2 = 6;  // ring slots with two tile streams (2 computed + 4 in flight)
 
 template <typename T, bool SPARSE, int NW, int HPW>
 static void launch_attn_t(dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                           const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                           int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
                           int S, void* out, float* lse, float* po, float* pml) {
-  if constexpr (sizeof(T) == 2)
-    k_attn16<SPARSE, NW, HPW, kRing><<<grid, NW * 64, 0, st>>>((const uint16_t*)q, (const uint16_t*)kv, idx,
-                                                               (const uint16_t*)x_win, win_start, sink, q_pos, Tq, N,
-                                                               T_win, H, k, window, ratio, scale, S, (uint16_t*)out,
-                                                               lse, po, pml);
+  if constexpr (sizeof(T) == 2) {
+    // Few rows (decode): two tile streams per block, two waves per SIMD.
+    if (grid.x * grid.y <= 1024)
+      k_attn16<SPARSE, NW, HPW, kRing2, 2><<<grid, NW * 2 * 64, 0, st>>>(
+          (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)x_win, win_start, sink, q_pos, Tq, N, T_win,
+          H, k, window, ratio, scale, S, (uint16_t*)out, lse, po, pml);
+    else
+      k_attn16<SPARSE, NW, HPW, kRing, 1><<<grid, NW * 64, 0, st>>>(
+          (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)x_win, win_start, sink, q_pos, Tq, N, T_win,
+          H, k, window, ratio, scale, S, (uint16_t*)out, lse, po, pml);
+  }
   else
     k_attn<T, SPARSE, NW, HPW><<<grid, NW * 64, 0, st>>>((const T*)q, (const T*)kv, idx, (const T*)x_win, win_start,
                                                          sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S,
