@@ -17,7 +17,8 @@ kernel's roofline fraction (timed with HIP events on its own stream by the
 library's kernel timer), the CPU oracle timed on a bounded sample, and extra
 workloads (CSA decode at 262k context; prefill TFLOP/s) under "extras".
 
-Usage: python bench.py [--steps K] [--warmup W] [--extras decode4,prefill2,prefill3|none]
+Usage: python bench.py [--steps K] [--warmup W]
+                       [--extras decode4,prefill_csa,prefill_hca,prefill_chunk|none]
 """
 from __future__ import annotations
 
@@ -235,6 +236,164 @@ def run_decode(torch, C, syn, O, args, which):
     return st, ms, wall, kt
 
 
+# ----------------------------------------------------------------------------- prefill workloads
+
+def time_ops(torch, ops, iters, warmup=1):
+    """Median device time (ms) of each named op over `iters` runs; ops run on the
+    current stream, which is the stream the library launches on."""
+    for _ in range(warmup):
+        for _, f in ops:
+            f()
+    torch.cuda.synchronize()
+    res = {name: [] for name, _ in ops}
+    for _ in range(iters):
+        for name, f in ops:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name].append(e0.elapsed_time(e1))
+    return {k: float(np.median(v)) for k, v in res.items()}
+
+
+def attn_flops(n_keys, H, d=128):
+    """QK and PV: 4 flops per (query, key, head, channel)."""
+    return float(np.sum(n_keys, dtype=np.float64)) * H * d * 4
+
+
+def index_flops(n_vis, H_I, d_I):
+    return float(np.sum(n_vis, dtype=np.float64)) * H_I * d_I * 2
+
+
+def prefill_csa(torch, C, syn, iters):
+    """Single CSA layer prefill, bf16, T = 65,536: compress (KV and fp8 indexer
+    keys), indexer top-512 over 16,384 entries (64 heads x 128, fp8), sparse
+    attention with 64 heads, window 128, sink."""
+    dev, bf = "cuda", torch.bfloat16
+    T, H, H_I, d_I, k, W = 65536, 64, 64, 128, 512, 128
+    s = 2000
+    c = {n: syn.normal_device(s + i, (1, T, 128), dev, bf) for i, n in enumerate(["c_a", "c_b", "z_a", "z_b"])}
+    ci = {n: syn.normal_device(s + 10 + i, (1, T, d_I), dev, bf) for i, n in enumerate(["a", "b", "za", "zb"])}
+    q = syn.normal_device(s + 20, (1, T, H, 128), dev, bf, scale=1 / np.sqrt(128))
+    qi32 = syn.normal_device(s + 21, (1, T, H_I, d_I), dev)
+    qi, qs = C.csa_quantize_rows(qi32, "fp8")
+    del qi32
+    w = syn.uniform_device(s + 22, (1, T, H_I), dev)
+    sink = syn.normal_device(s + 23, (H,), dev)
+    q_pos = torch.arange(T, dtype=torch.int32, device=dev)[None]
+    win_start = torch.zeros(1, dtype=torch.int32, device=dev)
+    N = T // 4
+    st = {}
+    st["E"] = C.csa_compress(c["c_a"], c["c_b"], c["z_a"], c["z_b"], 4)
+    st["KI"] = C.csa_compress(ci["a"], ci["b"], ci["za"], ci["zb"], 4, out_fmt="fp8")
+    st["idx"] = torch.empty(1, T, k, dtype=torch.int32, device=dev)
+    ws_i = torch.empty(C.indexer_topk_workspace_size(1, T, N, H_I, d_I, k, "fp8"), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    ws_a = torch.empty(max(1, C.sparse_attn_workspace_size(1, T, H, 128, k, W)), dtype=torch.uint8, device=dev)
+    ops = [
+        ("compress_kv", lambda: st.__setitem__("E", C.csa_compress(c["c_a"], c["c_b"], c["z_a"], c["z_b"], 4))),
+        ("compress_index_keys", lambda: st.__setitem__("KI", C.csa_compress(ci["a"], ci["b"], ci["za"], ci["zb"], 4,
+                                                                             out_fmt="fp8"))),
+        ("indexer_topk", lambda: C.indexer_topk(qi, qs, w, st["KI"][0], st["KI"][1], "fp8", q_pos, 4, k, d_I,
+                                                ws=ws_i, idx_out=st["idx"])),
+        ("sparse_attn", lambda: C.sparse_attn_fwd(q, st["E"], st["idx"], c["c_a"], win_start, sink, q_pos, W, 1.0,
+                                                  ws=ws_a, out=out)),
+    ]
+    t = time_ops(torch, ops, iters)
+    p = np.arange(T, dtype=np.int64)
+    n = np.minimum(N, (p + 1) // 4)
+    keys = np.minimum(k, n) + np.minimum(p + 1, W)
+    fl_i, fl_a = index_flops(n, H_I, d_I), attn_flops(keys, H)
+    return {"workload": "csa_prefill_bf16_T65536", "tokens": T, "heads": H, "top_k": k, "index": "64x128 fp8",
+            "ms": {kk: round(v, 4) for kk, v in t.items()}, "layer_ms": round(sum(t.values()), 4),
+            "indexer_tflop": round(fl_i / 1e12, 4), "attn_tflop": round(fl_a / 1e12, 4),
+            "indexer_tflop_s": round(fl_i / (t["indexer_topk"] * 1e-3) / 1e12, 2),
+            "sparse_attn_tflop_s": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12, 2),
+            "sparse_attn_frac_bf16_peak": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
+def prefill_hca(torch, C, syn, iters):
+    """Single HCA layer prefill, bf16, T = 131,072: 128:1 compression to 1024
+    entries, then dense attention (64 heads) over all visible entries plus the
+    128-token window and the sink."""
+    dev, bf = "cuda", torch.bfloat16
+    T, H, W = 131072, 64, 128
+    s = 3000
+    cc = syn.normal_device(s, (1, T, 128), dev, bf)
+    zz = syn.normal_device(s + 1, (1, T, 128), dev, bf)
+    q = syn.normal_device(s + 2, (1, T, H, 128), dev, bf, scale=1 / np.sqrt(128))
+    sink = syn.normal_device(s + 3, (H,), dev)
+    q_pos = torch.arange(T, dtype=torch.int32, device=dev)[None]
+    win_start = torch.zeros(1, dtype=torch.int32, device=dev)
+    N = T // 128
+    st = {"E": C.hca_compress(cc, zz, 128)}
+    out = torch.empty_like(q)
+    ws = torch.empty(max(1, C.dense_attn_workspace_size(1, T, N, H, 128, W)), dtype=torch.uint8, device=dev)
+    ops = [("compress", lambda: st.__setitem__("E", C.hca_compress(cc, zz, 128))),
+           ("dense_attn", lambda: C.dense_compressed_attn_fwd(q, st["E"], cc, win_start, sink, q_pos, 128, W, 1.0,
+                                                              ws=ws, out=out))]
+    t = time_ops(torch, ops, iters)
+    p = np.arange(T, dtype=np.int64)
+    keys = np.minimum(N, (p + 1) // 128) + np.minimum(p + 1, W)
+    fl = attn_flops(keys, H)
+    return {"workload": "hca_prefill_bf16_T131072", "tokens": T, "heads": H,
+            "ms": {kk: round(v, 4) for kk, v in t.items()}, "layer_ms": round(sum(t.values()), 4),
+            "attn_tflop": round(fl / 1e12, 4), "dense_attn_tflop_s": round(fl / (t["dense_attn"] * 1e-3) / 1e12, 2),
+            "dense_attn_frac_bf16_peak": round(fl / (t["dense_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
+def prefill_chunk(torch, C, syn, iters):
+    """CSA + HCA layer pair for an 8192-query prefill chunk at the end of a
+    1,048,576-token context: indexer over 262,144 fp4 entries (top-1024),
+    sparse attention and HCA dense attention over 8192 entries, 128 heads."""
+    dev, bf = "cuda", torch.bfloat16
+    L, Tq, H, H_I, d_I, k, W = 1 << 20, 8192, 128, 64, 128, 1024, 128
+    N, NH = L // 4, L // 128
+    s = 4000
+    ki32 = syn.normal_device(s, (1, N, d_I), dev)
+    kc, ks = C.csa_quantize_rows(ki32, "fp4")
+    del ki32
+    E = syn.normal_device(s + 1, (1, N, 128), dev, bf)
+    xw = syn.normal_device(s + 2, (1, Tq + W - 1, 128), dev, bf)
+    q = syn.normal_device(s + 3, (1, Tq, H, 128), dev, bf, scale=1 / np.sqrt(128))
+    qi32 = syn.normal_device(s + 4, (1, Tq, H_I, d_I), dev)
+    qi, qs = C.csa_quantize_rows(qi32, "fp4")
+    del qi32
+    w = syn.uniform_device(s + 5, (1, Tq, H_I), dev)
+    sink = syn.normal_device(s + 6, (H,), dev)
+    Eh = syn.normal_device(s + 7, (1, NH, 128), dev, bf)
+    xh = syn.normal_device(s + 8, (1, Tq + W - 1, 128), dev, bf)
+    qh = syn.normal_device(s + 9, (1, Tq, H, 128), dev, bf, scale=1 / np.sqrt(128))
+    sinkh = syn.normal_device(s + 10, (H,), dev)
+    q_pos = torch.arange(L - Tq, L, dtype=torch.int32, device=dev)[None]
+    win_start = torch.full((1,), L - Tq - W + 1, dtype=torch.int32, device=dev)
+    idx = torch.empty(1, Tq, k, dtype=torch.int32, device=dev)
+    ws_i = torch.empty(C.indexer_topk_workspace_size(1, Tq, N, H_I, d_I, k, "fp4"), dtype=torch.uint8, device=dev)
+    out, outh = torch.empty_like(q), torch.empty_like(qh)
+    ws_a = torch.empty(max(1, C.sparse_attn_workspace_size(1, Tq, H, 128, k, W)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, C.dense_attn_workspace_size(1, Tq, NH, H, 128, W)), dtype=torch.uint8, device=dev)
+    ops = [("indexer_topk", lambda: C.indexer_topk(qi, qs, w, kc, ks, "fp4", q_pos, 4, k, d_I, ws=ws_i,
+                                                   idx_out=idx)),
+           ("sparse_attn", lambda: C.sparse_attn_fwd(q, E, idx, xw, win_start, sink, q_pos, W, 1.0, ws=ws_a,
+                                                     out=out)),
+           ("dense_attn", lambda: C.dense_compressed_attn_fwd(qh, Eh, xh, win_start, sinkh, q_pos, 128, W, 1.0,
+                                                              ws=ws_d, out=outh))]
+    t = time_ops(torch, ops, iters)
+    p = np.arange(L - Tq, L, dtype=np.int64)
+    n = np.minimum(N, (p + 1) // 4)
+    nh = np.minimum(NH, (p + 1) // 128)
+    fl_i = index_flops(n, H_I, d_I)
+    fl_a = attn_flops(np.minimum(k, n) + W, H)
+    fl_d = attn_flops(nh + W, H)
+    return {"workload": "csa_hca_prefill_chunk_8192q_1m_ctx", "queries": Tq, "context": L, "heads": H,
+            "ms": {kk: round(v, 4) for kk, v in t.items()}, "pair_ms": round(sum(t.values()), 4),
+            "indexer_tflop": round(fl_i / 1e12, 3), "indexer_tflop_s": round(fl_i / (t["indexer_topk"] * 1e-3) / 1e12, 2),
+            "sparse_attn_tflop_s": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12, 2),
+            "dense_attn_tflop_s": round(fl_d / (t["dense_attn"] * 1e-3) / 1e12, 2),
+            "dense_attn_frac_bf16_peak": round(fl_d / (t["dense_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -243,7 +402,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
-    ap.add_argument("--extras", default="decode4", help="comma list of decode4,prefill2,prefill3 or 'none'")
+    ap.add_argument("--extras", default="decode4,prefill_csa,prefill_hca,prefill_chunk",
+                    help="comma list of decode4,prefill_csa,prefill_hca,prefill_chunk or 'none'")
+    ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch eagerly instead of replaying HIP graphs")
@@ -318,6 +479,12 @@ def main():
             "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in kt4.items()}}
         del st4
         torch.cuda.empty_cache()
+    for key, fn in (("prefill_csa", prefill_csa), ("prefill_hca", prefill_hca), ("prefill_chunk", prefill_chunk)):
+        if key in wanted:
+            r = fn(torch, C, syn, args.prefill_iters)
+            log(f"[bench] {r['workload']}: {r}")
+            extras[r["workload"]] = r
+            torch.cuda.empty_cache()
     if extras:
         result["extras"] = extras
     if args.calib_copy:
