@@ -363,12 +363,136 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two floats to packed bf16 (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// One 64-key tile (row-major in LDS, swizzled chunks) for the HPW 16-head
+// blocks of one wave: S^T = K Q^T, online softmax against the lazily raised
+// running max, O^T += V^T P^T. With `masked`, key_ok(key) says whether tile
+// row `key` holds a key; other rows get probability 0 (their LDS rows must
+// hold finite values).
+template <int HPW, typename KeyOk>
+__device__ __forceinline__ void attn_tile16(const uint16_t* tile, bool masked, KeyOk key_ok,
+                                            const Frag<uint16_t> (&qf)[HPW][kD / 32], float scale2,
+                                            float (&m)[HPW], float (&lsum)[HPW], f32x4 (&O)[HPW][kD / 16]) {
+  constexpr float kLazy = 8.f;   // headroom of the lazily raised running max (base 2)
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, col = lane & 15;
+  // ---- S^T = K Q^T for 4 blocks of 16 keys: 8 independent accumulator
+  // chains (key block x head block) over the 4 d-chunks. Logits stay
+  // unscaled here; the scale enters the exponent below.
+  float s[HPW][4][4];
+  {
+    f32x4 acc[4][HPW];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int hb = 0; hb < HPW; ++hb) acc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      Frag<uint16_t> a[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) a[kb].load(tile + swz(16 * kb + col, 4 * ks + g));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) acc[kb][hb] = mma8(a[kb], qf[hb][ks], acc[kb][hb]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = acc[kb][hb][rr];
+  }
+  if (masked) {   // uniform: only partial or holed tiles are masked
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = 16 * kb + 4 * g + rr;
+        if (!key_ok(key)) {
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = -INFINITY;
+        }
+      }
+  }
+  // ---- online softmax (per head = per column), base-2 logits scale2 * s.
+  // Lazy rescaling: probabilities are taken against the running reference
+  // max m[hb] while no logit of the tile exceeds it by more than kLazy, so
+  // P, O and l grow by at most 2^kLazy (exact in float32, and bf16 keeps
+  // its relative precision); only a larger logit raises m (the column max
+  // over the 4 lane rows, by permlane swaps) and rescales O and l. The
+  // result O / l and the log-sum m + log2(l) do not depend on m.
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) {
+    float lmax = s[hb][0][0];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) lmax = fmaxf(lmax, s[hb][kb][rr]);
+    const float lm2 = lmax * scale2;
+    if (__ballot(lm2 > m[hb] + kLazy)) {   // wave-uniform
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm2), __float_as_uint(lm2), false, false);
+      const float c1 = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+      const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(c1), __float_as_uint(c1), false, false);
+      const float cmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+      const float mnew = fmaxf(m[hb], cmax);
+      const float alpha = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mnew);
+      lsum[hb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
+      m[hb] = mnew;
+    }
+    const float negm = m[hb] == -INFINITY ? 0.f : -m[hb];
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[hb][kb][rr], scale2, negm));   // exp2(-inf) = 0
+        s[hb][kb][rr] = pv;
+        psum += pv;
+      }
+    lsum[hb] += psum;
+  }
+  // ---- O^T += V^T P^T. K-slot t of lane group g is key 4g+t (t < 4) or
+  // 16+4g+(t-4) (t >= 4) of the 32-key group; the transposed reads deliver
+  // exactly those keys for value column 16*db + col.
+  const int trow = 4 * g + (col >> 2);
+  const int tc = col & 3;
+#pragma unroll
+  for (int grp = 0; grp < 2; ++grp) {
+    Frag<uint16_t> pf[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+      pf[hb].v[0] = (int)cvt_pk_bf16(s[hb][2 * grp][0], s[hb][2 * grp][1]);
+      pf[hb].v[1] = (int)cvt_pk_bf16(s[hb][2 * grp][2], s[hb][2 * grp][3]);
+      pf[hb].v[2] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][0], s[hb][2 * grp + 1][1]);
+      pf[hb].v[3] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][2], s[hb][2 * grp + 1][3]);
+    }
+    const int r0 = 32 * grp + trow, r1 = r0 + 16;
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db) {
+      const int cch = 2 * db + (tc >> 1), half = (tc & 1) * 4;
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(tile + swz(r0, cch) + half));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(tile + swz(r1, cch) + half));
+      // the 4 + 4 transposed bf16 values already sit in dword order
+      const i32x2 l2 = __builtin_bit_cast(i32x2, lo4), h2 = __builtin_bit_cast(i32x2, hi4);
+      Frag<uint16_t> va;
+      va.v = i32x4{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+      for (int hb = 0; hb < HPW; ++hb) O[hb][db] = mma8(va, pf[hb], O[hb][db]);
+    }
+  }
 }
 
 template <bool SPARSE, int NW, int HPW, int NBUF, int TS>
@@ -383,8 +507,7 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   constexpr int LPT = (kKT * kD * 2 / 16) / NT;   // 16-byte gathers per thread per tile
   static_assert(NBUF % TS == 0 && NBUF > TS, "ring holds whole tile groups plus prefetch");
   __shared__ __align__(16) uint16_t ring[NBUF][kKT * kD];
-  __shared__ int tvalid[NBUF][kKT];
-  __shared__ int tbad[NBUF];
+  __shared__ int tbadw[NBUF][NWT];   // per wave: its gathers of the slot's tile hit rows without a key
   __shared__ int sidx[SPARSE ? kSelChunk : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -419,7 +542,6 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   // Logits are kept in base 2 (log2(e) folded into the scale) so each
   // probability is one v_exp_f32.
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
-  constexpr float kLazy = 8.f;   // headroom of the lazily raised running max (base 2)
   const float scale2 = scale * kLog2e;
   const bool has_sink = (sink != nullptr) && sp == 0 && ts == 0;
   float m[HPW], lsum[HPW];
@@ -436,7 +558,7 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   // at their first use could not count the gathers behind them). The sparse
   // path waits after its index staging below, which covers both.
   if (!SPARSE) wait_vm<0>();
-  const uint16_t* dummy = q + r * H * kD;   // any readable row; its tile rows are zeroed
+  const uint16_t* dummy = q + r * H * kD;   // a finite row for slots without a key
   const uint16_t* kvb = kv + b * N * kD;
   const uint16_t* xwb = x_win + b * T_win * kD;
 
@@ -453,36 +575,47 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
       __syncthreads();
     }
     const int ntiles = (clen + kKT - 1) / kKT;
+    // Gather instruction j of this lane: tile row grow[j] (4 rows per wave
+    // instruction), 16-byte chunk gcol[j] of it (swizzled position lane & 15).
+    int grow[LPT], gcol[LPT];
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      grow[j] = (j * NWT + wv) * 4 + (lane >> 4);
+      gcol[j] = ((lane & 15) ^ (grow[j] & 7)) << 3;
+    }
+    // key kk of the section: its row, or null when the slot holds no key
+    auto key_src = [&](int kk) -> const uint16_t* {
+      if (kk >= clen) return nullptr;
+      const int64_t ki = c0 + kk;
+      if (ki < n_sel) {
+        const int64_t e = SPARSE ? (int64_t)sidx[kk] : ki;
+        return (e >= 0 && e < N) ? kvb + e * kD : nullptr;
+      }
+      return xwb + (lo + (ki - n_sel) - w0) * kD;
+    };
     auto issue = [&](int t) {
       const int slot = t % NBUF;
       uint16_t* base = ring[slot];
+      const int kk0 = t * kKT;
+      const int64_t t0k = c0 + kk0;
       bool bad = false;
+      if (kk0 + kKT <= clen && (t0k >= n_sel || (!SPARSE && t0k + kKT <= n_sel))) {
+        // the tile's keys are consecutive rows: window rows, or entries
+        const uint16_t* tb = t0k >= n_sel ? xwb + (lo + (t0k - n_sel) - w0) * kD : kvb + t0k * kD;
 #pragma unroll
-      for (int j = 0; j < LPT; ++j) {
-        const int row = (j * NWT + wv) * 4 + (lane >> 4);         // 4 rows per wave instruction
-        const int cs = lane & 15;
-        const int kk = t * kKT + row;                              // key within the section
-        const int64_t ki = c0 + kk;
-        const uint16_t* src = nullptr;
-        if (kk < clen) {
-          if (ki < n_sel) {
-            const int64_t e = SPARSE ? (int64_t)sidx[kk] : ki;
-            if (e >= 0 && e < N) src = kvb + e * kD;
-          } else {
-            src = xwb + (lo + (ki - n_sel) - w0) * kD;
-          }
+        for (int j = 0; j < LPT; ++j)
+          gather_lds16(tb + grow[j] * kD + gcol[j], (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
+      } else {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+          const uint16_t* src = key_src(kk0 + grow[j]);
+          bad |= src == nullptr;
+          gather_lds16((src ? src : dummy) + gcol[j], (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
         }
-        if (cs == 0) tvalid[slot][row] = src != nullptr;
-        bad |= src == nullptr;
-        const uint16_t* gsrc = (src ? src : dummy) + ((cs ^ (row & 7)) << 3);
-        gather_lds16(gsrc, (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
       }
-      if (__ballot(bad)) {
-        if (lane == 0) atomicOr(&tbad[slot], 1);
-      }
+      const bool wbad = __ballot(bad) != 0ull;
+      if (lane == 0) tbadw[slot][wv] = wbad;
     };
-    for (int i = tid; i < NBUF; i += NT) tbad[i] = 0;
-    __syncthreads();
     // Tiles are taken TS at a time (stream ts computes tile t0 + ts); the
     // gathers of the next NBUF - TS tiles stay in flight meanwhile.
 #pragma unroll
@@ -496,135 +629,18 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
       if (t0 + NBUF - 1 < ntiles) wait_vm<(NBUF - TS) * LPT>();
       else wait_vm<0>();
       __syncthreads();
-      bool cleared = false;
-#pragma unroll
-      for (int j = 0; j < TS; ++j) {
-        const int sl = (t0 + j) % NBUF;
-        if (t0 + j < ntiles && tbad[sl]) {   // rows without a key: clear them so 0 * garbage cannot poison O
-          cleared = true;
-          for (int i = tid; i < kKT * 16; i += NT) {
-            const int row = i >> 4;
-            if (!tvalid[sl][row]) *reinterpret_cast<i32x4*>(ring[sl] + row * kD + ((i & 15) << 3)) = i32x4{0, 0, 0, 0};
-          }
-        }
-      }
-      if (cleared) __syncthreads();   // uniform: tbad is read by every thread
       const int t = t0 + ts;
       if (t < ntiles) {   // uniform per wave
       const int slot = t % NBUF;
       uint16_t* tile = ring[slot];
       const int nt = (clen - t * kKT) < kKT ? (clen - t * kKT) : kKT;
 
-      // ---- S^T = K Q^T for 4 blocks of 16 keys: 8 independent accumulator
-      // chains (key block x head block) over the 4 d-chunks. Logits stay
-      // unscaled here; the scale enters the exponent below.
-      float s[HPW][4][4];
-      {
-        f32x4 acc[4][HPW];
+      bool holed = false;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int hb = 0; hb < HPW; ++hb) acc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < kD / 32; ++ks) {
-          Frag<uint16_t> a[4];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) a[kb].load(tile + swz(16 * kb + col, 4 * ks + g));
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int hb = 0; hb < HPW; ++hb) acc[kb][hb] = mma8(a[kb], qf[hb][ks], acc[kb][hb]);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-            for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = acc[kb][hb][rr];
-      }
-      if (nt < kKT || tbad[slot]) {   // uniform: only partial or holed tiles are masked
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int key = 16 * kb + 4 * g + rr;
-            if (!(key < nt && tvalid[slot][key])) {
-#pragma unroll
-              for (int hb = 0; hb < HPW; ++hb) s[hb][kb][rr] = -INFINITY;
-            }
-          }
-      }
-      // ---- online softmax (per head = per column), base-2 logits scale2 * s.
-      // Lazy rescaling: probabilities are taken against the running reference
-      // max m[hb] while no logit of the tile exceeds it by more than kLazy, so
-      // P, O and l grow by at most 2^kLazy (exact in float32, and bf16 keeps
-      // its relative precision); only a larger logit raises m (the column max
-      // over the 4 lane rows, by permlane swaps) and rescales O and l. The
-      // result O / l and the log-sum m + log2(l) do not depend on m.
-#pragma unroll
-      for (int hb = 0; hb < HPW; ++hb) {
-        float lmax = s[hb][0][0];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) lmax = fmaxf(lmax, s[hb][kb][rr]);
-        const float lm2 = lmax * scale2;
-        if (__ballot(lm2 > m[hb] + kLazy)) {   // wave-uniform
-          const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm2), __float_as_uint(lm2), false, false);
-          const float c1 = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
-          const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(c1), __float_as_uint(c1), false, false);
-          const float cmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
-          const float mnew = fmaxf(m[hb], cmax);
-          const float alpha = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mnew);
-          lsum[hb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
-          m[hb] = mnew;
-        }
-        const float negm = m[hb] == -INFINITY ? 0.f : -m[hb];
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[hb][kb][rr], scale2, negm));   // exp2(-inf) = 0
-            s[hb][kb][rr] = pv;
-            psum += pv;
-          }
-        lsum[hb] += psum;
-      }
-      // ---- O^T += V^T P^T. K-slot t of lane group g is key 4g+t (t < 4) or
-      // 16+4g+(t-4) (t >= 4) of the 32-key group; the transposed reads deliver
-      // exactly those keys for value column 16*db + col.
-      const int trow = 4 * g + (col >> 2);
-      const int tc = col & 3;
-#pragma unroll
-      for (int grp = 0; grp < 2; ++grp) {
-        Frag<uint16_t> pf[HPW];
-#pragma unroll
-        for (int hb = 0; hb < HPW; ++hb) {
-          pf[hb].v[0] = (int)cvt_pk_bf16(s[hb][2 * grp][0], s[hb][2 * grp][1]);
-          pf[hb].v[1] = (int)cvt_pk_bf16(s[hb][2 * grp][2], s[hb][2 * grp][3]);
-          pf[hb].v[2] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][0], s[hb][2 * grp + 1][1]);
-          pf[hb].v[3] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][2], s[hb][2 * grp + 1][3]);
-        }
-        const int r0 = 32 * grp + trow, r1 = r0 + 16;
-#pragma unroll
-        for (int db = 0; db < kD / 16; ++db) {
-          const int cch = 2 * db + (tc >> 1), half = (tc & 1) * 4;
-          const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(tile + swz(r0, cch) + half));
-          const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(tile + swz(r1, cch) + half));
-          Frag<uint16_t> va;
-          va.v = i32x4{(int)((uint16_t)lo4[0] | ((uint32_t)(uint16_t)lo4[1] << 16)),
-                       (int)((uint16_t)lo4[2] | ((uint32_t)(uint16_t)lo4[3] << 16)),
-                       (int)((uint16_t)hi4[0] | ((uint32_t)(uint16_t)hi4[1] << 16)),
-                       (int)((uint16_t)hi4[2] | ((uint32_t)(uint16_t)hi4[3] << 16))};
-#pragma unroll
-          for (int hb = 0; hb < HPW; ++hb) O[hb][db] = mma8(va, pf[hb], O[hb][db]);
-        }
-      }
+      for (int w = 0; w < NWT; ++w) holed |= tbadw[slot][w] != 0;
+      // slots without a key hold a finite row (the query's) and get probability 0
+      attn_tile16<HPW>(tile, nt < kKT || holed, [&](int key) { return key_src(t * kKT + key) != nullptr; },
+                       qf, scale2, m, lsum, O);
       }   // t < ntiles
       __syncthreads();   // the slots are refilled by later issue() calls
     }
@@ -737,20 +753,23 @@ static AttnShape pick_shape(int H) {
   return {nw, hpw};
 }
 
-// Key splits per (row, head group): a fixed function of the shapes, so the
-// merge order (and the result) never depends on timing. About one block per
-// compute unit, with at least kMinSplitKeys keys per split.
+// Key splits per (row, head group): a fixed function of the shapes (never of
+// timing), so the workspace query and the launch agree and the merge order is
+// fixed. About one block per compute unit, >= kMinSplitKeys keys per split.
 constexpr int64_t kMinSplitKeys = 128;
-int attn_splits(int64_t rows, int H, int64_t nk_max) {
+struct AttnPlan { int S; };
+static AttnPlan plan_attention(int64_t rows, int H, int64_t nk_max) {
   const AttnShape sh = pick_shape(H);
   const int64_t base = rows * (H / (16 * sh.nw * sh.hpw));
-  if (base >= 256) return 1;
+  if (base >= 256) return {1};
   const int64_t fill = cdiv(256, base);
   const int64_t by_keys = nk_max / kMinSplitKeys > 1 ? nk_max / kMinSplitKeys : 1;
   int64_t s = fill < by_keys ? fill : by_keys;
   if (s > 128) s = 128;
-  return (int)(s < 1 ? 1 : s);
+  return {(int)(s < 1 ? 1 : s)};
 }
+
+int attn_splits(int64_t rows, int H, int64_t nk_max) { return plan_attention(rows, H, nk_max).S; }
 
 size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max) {
   const int S = attn_splits(rows, H, nk_max);
@@ -810,7 +829,8 @@ hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void*
   const int64_t rows = B * Tq;
   if (rows == 0) return hipSuccess;
   const AttnShape sh = pick_shape(H);
-  const int S = attn_splits(rows, H, nk_max);
+  const AttnPlan pl = plan_attention(rows, H, nk_max);
+  const int S = pl.S;
   float* po = reinterpret_cast<float*>(ws);
   float* pml = po ? po + (size_t)rows * H * S * kD : nullptr;
   const dim3 grid((unsigned)rows, (unsigned)((H / (16 * sh.nw * sh.hpw)) * S));
