@@ -777,7 +777,8 @@ size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max) {
   return (size_t)rows * H * S * (kD + 2) * 4;
 }
 
-constexpr int kRing = 4;   // ring slots per block (bf16 path, one tile stream)
+constexpr int kRing = 2;   // ring slots per block (bf16 path, one tile stream): a small ring leaves LDS
+                           // for more resident blocks, which hides more latency than deeper prefetch
 constexpr int kRing2 = 6;  // ring slots with two tile streams (2 computed + 4 in flight)
 
 template <typename T, bool SPARSE, int NW, int HPW>
