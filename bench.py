@@ -257,6 +257,15 @@ def time_ops(torch, ops, iters, warmup=1):
     return {k: float(np.median(v)) for k, v in res.items()}
 
 
+def call_kernel_ms(torch, C, fn, kernel, max_launches=512):
+    """Sum of the device times of every launch of one library kernel in one call of fn."""
+    C.kernel_timer_start(kernel, max_launches)
+    fn()
+    torch.cuda.synchronize()
+    t = C.kernel_timer_read(max_launches)   # also stops the timer
+    return float(np.sum(t)) if t else None
+
+
 def attn_flops(n_keys, H, d=128):
     """QK and PV: 4 flops per (query, key, head, channel)."""
     return float(np.sum(n_keys, dtype=np.float64)) * H * d * 4
@@ -301,6 +310,7 @@ def prefill_csa(torch, C, syn, iters):
                                                   ws=ws_a, out=out)),
     ]
     t = time_ops(torch, ops, iters)
+    split = {kn: call_kernel_ms(torch, C, ops[2][1], kn) for kn in ("index_score", "topk")}
     p = np.arange(T, dtype=np.int64)
     n = np.minimum(N, (p + 1) // 4)
     keys = np.minimum(k, n) + np.minimum(p + 1, W)
@@ -309,6 +319,9 @@ def prefill_csa(torch, C, syn, iters):
             "ms": {kk: round(v, 4) for kk, v in t.items()}, "layer_ms": round(sum(t.values()), 4),
             "indexer_tflop": round(fl_i / 1e12, 4), "attn_tflop": round(fl_a / 1e12, 4),
             "indexer_tflop_s": round(fl_i / (t["indexer_topk"] * 1e-3) / 1e12, 2),
+            "indexer_split_ms": {kn: (None if v is None else round(v, 4)) for kn, v in split.items()},
+            "index_score_tflop_s": (None if not split["index_score"] else
+                                    round(fl_i / (split["index_score"] * 1e-3) / 1e12, 2)),
             "sparse_attn_tflop_s": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12, 2),
             "sparse_attn_frac_bf16_peak": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
@@ -380,6 +393,7 @@ def prefill_chunk(torch, C, syn, iters):
            ("dense_attn", lambda: C.dense_compressed_attn_fwd(qh, Eh, xh, win_start, sinkh, q_pos, 128, W, 1.0,
                                                               ws=ws_d, out=outh))]
     t = time_ops(torch, ops, iters)
+    split = {kn: call_kernel_ms(torch, C, ops[0][1], kn) for kn in ("index_score", "topk")}
     p = np.arange(L - Tq, L, dtype=np.int64)
     n = np.minimum(N, (p + 1) // 4)
     nh = np.minimum(NH, (p + 1) // 128)
@@ -389,6 +403,9 @@ def prefill_chunk(torch, C, syn, iters):
     return {"workload": "csa_hca_prefill_chunk_8192q_1m_ctx", "queries": Tq, "context": L, "heads": H,
             "ms": {kk: round(v, 4) for kk, v in t.items()}, "pair_ms": round(sum(t.values()), 4),
             "indexer_tflop": round(fl_i / 1e12, 3), "indexer_tflop_s": round(fl_i / (t["indexer_topk"] * 1e-3) / 1e12, 2),
+            "indexer_split_ms": {kn: (None if v is None else round(v, 4)) for kn, v in split.items()},
+            "index_score_tflop_s": (None if not split["index_score"] else
+                                    round(fl_i / (split["index_score"] * 1e-3) / 1e12, 2)),
             "sparse_attn_tflop_s": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12, 2),
             "dense_attn_tflop_s": round(fl_d / (t["dense_attn"] * 1e-3) / 1e12, 2),
             "dense_attn_frac_bf16_peak": round(fl_d / (t["dense_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}

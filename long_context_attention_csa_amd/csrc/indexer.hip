@@ -47,7 +47,7 @@ constexpr int kHistBins = 1 << kHistBits;
 constexpr int kCandCap = 8192;            // candidates held in LDS
 constexpr int kMaxK = 2048;
 constexpr int kGroup = 16;                // entries per group maximum
-constexpr int kGroupFactor = 4;           // group path when groups >= 4k
+constexpr int kGroupFactor = 2;           // group path when groups >= 2k
 
 // ------------------------------------------------------------------ operand loads
 // Per-format A/B operand of one 16x16 MFMA tile, for one lane:
