@@ -25,10 +25,12 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags. The indexer's MFMA results feed VALU math at once:
-# the VGPR form of the MFMA saves an accumulator-register read per element.
+# Per-source extra flags. The indexer's and the attention's MFMA results feed
+# VALU math at once (weighted ReLU, softmax, rescaling): the VGPR form of the
+# MFMA saves an accumulator-register copy per element.
 EXTRA = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 
