@@ -171,7 +171,7 @@ csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w,
  *   x_win  [B, T_win, d] of t;  win_start int32 [B] (position of row 0)
  *   sink   float32 [H], or NULL for no sink
  *   q_pos  int32 [B, Tq];  out [B, Tq, H, d] of t;  lse NULL or float32 [B, Tq, H]
- *   d == 128; H a multiple of 16, <= 256; 1 <= k <= 4096; window >= 0.
+ *   d == 128; H a multiple of 16, <= 256; 1 <= k <= 4096; window >= 0; B*Tq < 2^31.
  * Accumulation is float32; a query with no keys and no sink gives o = 0.
  */
 size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, int32_t k,
@@ -187,7 +187,7 @@ csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, co
  * entry (j < n(p), dense, no selection), plus the window and the sink
  * (cf-1.com write-up §3.2, §3.3). Same formula and layouts as
  * sparse_attn_fwd with idx = 0..n(p)-1.
- *   ratio >= 1 defines n(p).
+ *   ratio >= 1 defines n(p); B*Tq < 2^31.
  */
 size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t d,
                                  int32_t window);

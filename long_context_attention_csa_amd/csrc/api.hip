@@ -194,6 +194,8 @@ static csa_status check_attn_common(const char* fn, const void* q, const void* k
   CSA_REQUIRE(d == 128, CSA_ERR_UNSUPPORTED, "%s: d %d (only 128)", fn, d);
   CSA_REQUIRE(H >= 16 && H <= 256 && H % 16 == 0, CSA_ERR_UNSUPPORTED, "%s: H %d (multiple of 16, <= 256)", fn, H);
   if (B * Tq == 0) return CSA_OK;
+  CSA_REQUIRE(B <= INT32_MAX / Tq, CSA_ERR_SHAPE, "%s: B*Tq = %lld x %lld must be < 2^31", fn, (long long)B,
+              (long long)Tq);
   CSA_REQUIRE(q && q_pos && win_start && out, CSA_ERR_NULL, "%s: NULL tensor", fn);
   CSA_REQUIRE(N == 0 || kv, CSA_ERR_NULL, "%s: kv is NULL", fn);
   CSA_REQUIRE(T_win == 0 || x_win, CSA_ERR_NULL, "%s: x_win is NULL", fn);

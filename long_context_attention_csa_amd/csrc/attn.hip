@@ -338,12 +338,44 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
 //  * ds_read_b64_tr_b16 reads the V^T fragments of the P*V product
 //    transposed out of the same row-major tile, so no transposed copy is built.
 // Tiles are 64 rows x 256 B; each row's 16-byte chunk c is stored at position
-// c ^ (row & 7), which spreads both the QK fragment reads (16 rows, same chunk)
-// and the transposed reads (16 rows, 32 bytes) over all LDS banks. A lane of
-// a gather instruction fetches exactly the chunk its LDS slot must hold.
+// c ^ (row & SWM). With SWM = 15, sixteen consecutive rows put any given chunk
+// at sixteen different positions, so the K fragment reads (16 rows, one chunk
+// each) and the transposed V reads (4 rows x 32 bytes per 16 lanes) spread
+// over all LDS banks. A lane of a gather instruction fetches exactly the
+// chunk its LDS slot must hold; blocks of fewer than 4 waves use SWM = 7
+// (rows 8 apart share positions, a 2-way conflict on the K reads), which
+// keeps a lane's source chunk the same for all its gathers of a tile and so
+// saves the registers those kernels are short of.
 constexpr int kSelChunk = 1024;     // selected indices staged in LDS at a time
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kD + ((chunk ^ (row & 7)) << 3); }
+// Per-lane byte offsets of a wave's reads of one tile (the same for every
+// tile). K fragment (key block kb, d-step ks) of lane (g, col): row 16 kb + col,
+// chunk 4 ks + g, at byte kofs + ((64 ks) ^ kx) + 4096 kb. Transposed V read
+// (key half grp, 16-key half hi, d block db): row 32 grp + 16 hi + trow with
+// trow = 4 g + col / 4, 8 bytes of chunk 2 db + (col & 3) / 2, at byte
+// vofs + ((32 db) ^ vx) + 8192 grp + 4096 hi.
+struct TileLanes {
+  uint32_t kofs, kx, vofs, vx;
+  __device__ __forceinline__ TileLanes(int lane, int swm) {
+    const int g = lane >> 4, col = lane & 15;
+    kofs = col * 256 + 16 * ((g ^ col) & 3);
+    kx = 64 * ((col & swm) >> 2);
+    const int trow = 4 * g + (col >> 2), tc = col & 3;
+    vofs = trow * 256 + 16 * (((tc >> 1) ^ trow) & 1) + 8 * (tc & 1);
+    vx = 32 * ((trow & swm) >> 1);
+  }
+};
+
+typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Hides a value from the optimiser, so that constant offsets added to it are
+// not reassociated into separately hoisted registers.
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ i32x4 lds_read_b128(uint32_t a) { return *(lds_i32x4*)(size_t)a; }
+__device__ __forceinline__ s16x4 lds_read_tr16(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a);
+}
 
 // One global_load_lds_dwordx4: each lane's 16 bytes at src go to LDS address
 // lds_base + 16 * lane. Written as asm so that the compiler does not treat it
@@ -362,7 +394,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N_OUT & 15) | ((N_OUT >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -378,12 +409,11 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // row `key` holds a key; other rows get probability 0 (their LDS rows must
 // hold finite values).
 template <int HPW, typename KeyOk>
-__device__ __forceinline__ void attn_tile16(const uint16_t* tile, bool masked, KeyOk key_ok,
+__device__ __forceinline__ void attn_tile16(uint32_t tb, const TileLanes& tl, bool masked, KeyOk key_ok,
                                             const Frag<uint16_t> (&qf)[HPW][kD / 32], float scale2,
                                             float (&m)[HPW], float (&lsum)[HPW], f32x4 (&O)[HPW][kD / 16]) {
   constexpr float kLazy = 8.f;   // headroom of the lazily raised running max (base 2)
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, col = lane & 15;
+  const int g = (threadIdx.x & 63) >> 4;
   // ---- S^T = K Q^T for 4 blocks of 16 keys: 8 independent accumulator
   // chains (key block x head block) over the 4 d-chunks. Logits stay
   // unscaled here; the scale enters the exponent below.
@@ -396,9 +426,11 @@ __device__ __forceinline__ void attn_tile16(const uint16_t* tile, bool masked, K
       for (int hb = 0; hb < HPW; ++hb) acc[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kD / 32; ++ks) {
+      uint32_t ka = (((uint32_t)(64 * ks)) ^ tl.kx) + (tb + tl.kofs);
+      opaque(ka);   // keeps 4096 kb in the reads' offset field
       Frag<uint16_t> a[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) a[kb].load(tile + swz(16 * kb + col, 4 * ks + g));
+      for (int kb = 0; kb < 4; ++kb) a[kb].v = lds_read_b128(ka + 4096 * kb);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -451,22 +483,26 @@ __device__ __forceinline__ void attn_tile16(const uint16_t* tile, bool masked, K
       m[hb] = mnew;
     }
     const float negm = m[hb] == -INFINITY ? 0.f : -m[hb];
-    float psum = 0.f;
+    float ps[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(s[hb][kb][rr], scale2, negm));   // exp2(-inf) = 0
         s[hb][kb][rr] = pv;
-        psum += pv;
+        ps[rr & 1] += pv;
       }
-    lsum[hb] += psum;
+    lsum[hb] += ps[0] + ps[1];
   }
   // ---- O^T += V^T P^T. K-slot t of lane group g is key 4g+t (t < 4) or
   // 16+4g+(t-4) (t >= 4) of the 32-key group; the transposed reads deliver
   // exactly those keys for value column 16*db + col.
-  const int trow = 4 * g + (col >> 2);
-  const int tc = col & 3;
+  uint32_t va[kD / 16];
+#pragma unroll
+  for (int db = 0; db < kD / 16; ++db) {
+    va[db] = (((uint32_t)(32 * db)) ^ tl.vx) + (tb + tl.vofs);
+    opaque(va[db]);   // keeps 8192 grp + 4096 in the reads' offset field
+  }
 #pragma unroll
   for (int grp = 0; grp < 2; ++grp) {
     Frag<uint16_t> pf[HPW];
@@ -477,20 +513,16 @@ __device__ __forceinline__ void attn_tile16(const uint16_t* tile, bool masked, K
       pf[hb].v[2] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][0], s[hb][2 * grp + 1][1]);
       pf[hb].v[3] = (int)cvt_pk_bf16(s[hb][2 * grp + 1][2], s[hb][2 * grp + 1][3]);
     }
-    const int r0 = 32 * grp + trow, r1 = r0 + 16;
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db) {
-      const int cch = 2 * db + (tc >> 1), half = (tc & 1) * 4;
-      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(tile + swz(r0, cch) + half));
-      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)(tile + swz(r1, cch) + half));
+      const s16x4 lo4 = lds_read_tr16(va[db] + 8192 * grp);
+      const s16x4 hi4 = lds_read_tr16(va[db] + 8192 * grp + 4096);
       // the 4 + 4 transposed bf16 values already sit in dword order
       const i32x2 l2 = __builtin_bit_cast(i32x2, lo4), h2 = __builtin_bit_cast(i32x2, hi4);
-      Frag<uint16_t> va;
-      va.v = i32x4{l2[0], l2[1], h2[0], h2[1]};
+      Frag<uint16_t> vf;
+      vf.v = i32x4{l2[0], l2[1], h2[0], h2[1]};
 #pragma unroll
-      for (int hb = 0; hb < HPW; ++hb) O[hb][db] = mma8(va, pf[hb], O[hb][db]);
+      for (int hb = 0; hb < HPW; ++hb) O[hb][db] = mma8(vf, pf[hb], O[hb][db]);
     }
   }
 }
@@ -509,17 +541,36 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   __shared__ __align__(16) uint16_t ring[NBUF][kKT * kD];
   __shared__ int tbadw[NBUF][NWT];   // per wave: its gathers of the slot's tile hit rows without a key
   __shared__ int sidx[SPARSE ? kSelChunk : 1];
+  constexpr int QH = NW * HPW * 16;                // query rows (heads) of the block
+  constexpr int QPT = QH * 16 / NT;                // 16-byte query gathers per thread
+  static_assert(QPT * NT == QH * 16, "query rows split evenly over the threads");
+  // two tile streams (few rows, short key ranges): the query goes through LDS
+  __shared__ __align__(16) uint16_t qs[TS > 1 ? QH * kD : 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0 .. NWT-1: gathers
   const int hw = wv % NW, ts = wv / NW;                      // head wave, tile stream
   const int g = lane >> 4, col = lane & 15;
-  const int64_t r = blockIdx.x;
+  constexpr int SWM = NWT >= 4 ? 15 : 7;          // chunk swizzle mask of the tiles
+  const TileLanes tl(lane, SWM);
+  // rows < 2^31: 32-bit row arithmetic, so that both scalar loads below are
+  // issued together (a 64-bit division would put a branch between them)
+  const int32_t r32 = blockIdx.x, b32 = r32 / (int32_t)Tq;
+  const int64_t r = r32, b = b32;
   const int hg = blockIdx.y / S, sp = blockIdx.y % S;
-  const int64_t b = r / Tq;
-  const int64_t p = q_pos[r];
-  const int64_t n_sel = SPARSE ? (int64_t)k : visible(p, ratio, N);
-  const int64_t w0 = win_start[b];
+  if constexpr (TS > 1) {
+    // the query gathers go first: their addresses need no loaded value
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int qrow = (j * NWT + wv) * 4 + (lane >> 4);
+      gather_lds16(q + (r * H + hg * QH + qrow) * kD + (((lane & 15) ^ (qrow & SWM)) << 3),
+                   (uint32_t)(uintptr_t)(qs + (j * NWT + wv) * 4 * kD));
+    }
+  }
+  const int32_t w0_32 = win_start[b32];
+  const int32_t p32 = q_pos[r32];
+  const int64_t p = p32, w0 = w0_32;
+  const int64_t n_sel = SPARSE ? (int64_t)k : visible(p32, ratio, N);
   int64_t lo = p - window + 1;
   if (lo < 0) lo = 0;
   if (lo < w0) lo = w0;
@@ -531,33 +582,45 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   const int64_t kbeg = (int64_t)sp * chunk;
   const int64_t kend = (kbeg + chunk) < nk ? (kbeg + chunk) : nk;
 
-  const int h0 = hg * (NW * 16 * HPW) + hw * 16 * HPW;
+  const int h0 = hg * QH + hw * 16 * HPW;
+  // With two tile streams (short key ranges per block) the query rows go to
+  // LDS by the same asynchronous gathers as the keys, issued first so that the
+  // first wait on key tiles covers them, and the waves read their fragments
+  // from there: no vector load that the compiler tracks (and would wait for,
+  // draining the key pipeline) precedes the first tile. With one stream the
+  // fragments are loaded directly and waited for before the first gather.
   Frag<uint16_t> qf[HPW][kD / 32];
+  if constexpr (TS == 1) {
 #pragma unroll
-  for (int hb = 0; hb < HPW; ++hb) {
-    const uint16_t* qrow = q + (r * H + h0 + 16 * hb + col) * kD;
+    for (int hb = 0; hb < HPW; ++hb) {
+      const uint16_t* qrow = q + (r * H + h0 + 16 * hb + col) * kD;
 #pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) qf[hb][ks].load(qrow + 32 * ks + 8 * g);
+      for (int ks = 0; ks < kD / 32; ++ks) qf[hb][ks].load(qrow + 32 * ks + 8 * g);
+    }
+    if (!SPARSE) wait_vm<0>();   // the sparse path waits after its index staging
   }
+  auto load_q = [&]() {
+    if constexpr (TS > 1) {
+#pragma unroll
+      for (int hb = 0; hb < HPW; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < kD / 32; ++ks)
+          qf[hb][ks].v = lds_read_b128((uint32_t)(uintptr_t)qs + (hw * HPW + hb) * 4096 + tl.kofs + ((64u * ks) ^ tl.kx));
+    }
+  };
   // Logits are kept in base 2 (log2(e) folded into the scale) so each
   // probability is one v_exp_f32.
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
   const float scale2 = scale * kLog2e;
-  const bool has_sink = (sink != nullptr) && sp == 0 && ts == 0;
   float m[HPW], lsum[HPW];
   f32x4 O[HPW][kD / 16];
 #pragma unroll
   for (int hb = 0; hb < HPW; ++hb) {
-    m[hb] = has_sink ? sink[h0 + 16 * hb + col] * kLog2e : -INFINITY;
-    lsum[hb] = (has_sink && g == 0) ? 1.f : 0.f;
+    m[hb] = -INFINITY;
+    lsum[hb] = 0.f;
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // The gathers are invisible to the compiler's wait counting, so the query
-  // loads must be complete before the first gather is issued (a wait placed
-  // at their first use could not count the gathers behind them). The sparse
-  // path waits after its index staging below, which covers both.
-  if (!SPARSE) wait_vm<0>();
   const uint16_t* dummy = q + r * H * kD;   // a finite row for slots without a key
   const uint16_t* kvb = kv + b * N * kD;
   const uint16_t* xwb = x_win + b * T_win * kD;
@@ -573,6 +636,7 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
       }
       wait_vm<0>();   // every thread: the query and index loads are done before any gather
       __syncthreads();
+      if (c0 == kbeg) load_q();
     }
     const int ntiles = (clen + kKT - 1) / kKT;
     // Gather instruction j of this lane: tile row grow[j] (4 rows per wave
@@ -581,7 +645,7 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
       grow[j] = (j * NWT + wv) * 4 + (lane >> 4);
-      gcol[j] = ((lane & 15) ^ (grow[j] & 7)) << 3;
+      gcol[j] = ((lane & 15) ^ (grow[j] & SWM)) << 3;
     }
     // key kk of the section: its row, or null when the slot holds no key
     auto key_src = [&](int kk) -> const uint16_t* {
@@ -621,6 +685,13 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
 #pragma unroll
     for (int t = 0; t < NBUF - TS; ++t)
       if (t < ntiles) issue(t);
+    if (!SPARSE && TS > 1 && c0 == kbeg) {
+      // the query gathers are older than the key gathers just issued
+      if (ntiles >= NBUF - TS) wait_vm<(NBUF - TS) * LPT>();
+      else wait_vm<0>();
+      __syncthreads();
+      load_q();
+    }
 
     for (int t0 = 0; t0 < ntiles; t0 += TS) {
 #pragma unroll
@@ -632,19 +703,20 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
       const int t = t0 + ts;
       if (t < ntiles) {   // uniform per wave
       const int slot = t % NBUF;
-      uint16_t* tile = ring[slot];
+      const uint32_t tb = (uint32_t)(uintptr_t)ring[slot];
       const int nt = (clen - t * kKT) < kKT ? (clen - t * kKT) : kKT;
 
       bool holed = false;
 #pragma unroll
       for (int w = 0; w < NWT; ++w) holed |= tbadw[slot][w] != 0;
       // slots without a key hold a finite row (the query's) and get probability 0
-      attn_tile16<HPW>(tile, nt < kKT || holed, [&](int key) { return key_src(t * kKT + key) != nullptr; },
+      attn_tile16<HPW>(tb, tl, nt < kKT || holed, [&](int key) { return key_src(t * kKT + key) != nullptr; },
                        qf, scale2, m, lsum, O);
       }   // t < ntiles
       __syncthreads();   // the slots are refilled by later issue() calls
     }
   }
+  wait_vm<0>();   // a block without keys still has its query gathers in flight
 
   if constexpr (TS > 1) {
     // Stream 1 hands (O, m, lsum) to stream 0 through the (now idle) ring, in
@@ -681,6 +753,21 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
     }
   }
 
+  if (sink != nullptr && sp == 0) {
+    // The sink is one more logit (value 0) of split 0: it joins the
+    // denominator, with the running max raised to it when larger.
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+      const float ms = sink[h0 + 16 * hb + col] * kLog2e;
+      const float mm = fmaxf(m[hb], ms);
+      const float a0 = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mm);
+      lsum[hb] = lsum[hb] * a0 + (g == 0 ? __builtin_amdgcn_exp2f(ms - mm) : 0.f);
+      m[hb] = mm;
+#pragma unroll
+      for (int db = 0; db < kD / 16; ++db) O[hb][db] *= a0;
+    }
+  }
+
 #pragma unroll
   for (int hb = 0; hb < HPW; ++hb) {
     float l = lsum[hb];
@@ -697,11 +784,16 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
       }
       if (lse && g == 0) lse[r * H + head] = l > 0.f ? (m[hb] + __log2f(l)) * kLn2 : -INFINITY;
     } else {
+      // Partial result of this split: its own softmax average O / l in bf16
+      // (the merge takes a convex combination of the split averages, so
+      // their rounding stays within that of the bf16 output) and (m, l).
       const int64_t pi = (r * H + head) * S + sp;
-      float* po = part_o + pi * kD;
+      uint16_t* po = reinterpret_cast<uint16_t*>(part_o) + pi * kD;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
       for (int db = 0; db < kD / 16; ++db)
-        *reinterpret_cast<float4*>(po + 16 * db + 4 * g) = make_float4(O[hb][db][0], O[hb][db][1], O[hb][db][2], O[hb][db][3]);
+        *reinterpret_cast<uint2*>(po + 16 * db + 4 * g) =
+            make_uint2(cvt_pk_bf16(O[hb][db][0] * inv, O[hb][db][1] * inv), cvt_pk_bf16(O[hb][db][2] * inv, O[hb][db][3] * inv));
       if (g == 0) {
         part_ml[2 * pi] = m[hb] * kLn2;   // the merge works in natural-log units
         part_ml[2 * pi + 1] = l;
@@ -712,9 +804,11 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
 
 // Merge of S partial results per (row, head), in split order. 256 threads =
 // 8 (row, head) pairs x 32 lanes x 4 channels; loads are unrolled so the S
-// partials of a pair are in flight together.
-template <typename T>
-__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+// partials of a pair are in flight together. Partials are unnormalised float
+// sums (PT = float) or bf16 split averages O / l (PT = uint16_t); (m, l) are
+// float, m in natural-log units.
+template <typename T, typename PT>
+__global__ __launch_bounds__(256) void k_attn_merge(const PT* __restrict__ part_o, const float* __restrict__ part_ml,
                                                     int64_t RH, int S, T* __restrict__ out, float* __restrict__ lse) {
   const int64_t rh = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int d0 = (threadIdx.x & 31) * 4;
@@ -728,10 +822,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   if (mx != -INFINITY) {
 #pragma unroll 8
     for (int sp = 0; sp < S; ++sp) {
-      const float f = __expf(ml[2 * sp] - mx);
-      l = fmaf(ml[2 * sp + 1], f, l);
-      const float4 v = *reinterpret_cast<const float4*>(part_o + (rh * S + sp) * kD + d0);
-      o[0] = fmaf(v.x, f, o[0]); o[1] = fmaf(v.y, f, o[1]); o[2] = fmaf(v.z, f, o[2]); o[3] = fmaf(v.w, f, o[3]);
+      const float e = __expf(ml[2 * sp] - mx);
+      float v[4], f;
+      if constexpr (sizeof(PT) == 2) {
+        f = e * ml[2 * sp + 1];   // weight of the split average
+        l += f;
+        const uint2 u = *reinterpret_cast<const uint2*>(part_o + (rh * S + sp) * kD + d0);
+        v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+        v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        f = e;
+        l = fmaf(ml[2 * sp + 1], e, l);
+        const float4 u = *reinterpret_cast<const float4*>(part_o + (rh * S + sp) * kD + d0);
+        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+      }
+      o[0] = fmaf(v[0], f, o[0]); o[1] = fmaf(v[1], f, o[1]); o[2] = fmaf(v[2], f, o[2]); o[3] = fmaf(v[3], f, o[3]);
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -849,8 +954,11 @@ hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void*
   if (e != hipSuccess || S == 1) return e;
   const int64_t RH = rows * H;
   timer_before(CSA_KID_ATTN_MERGE, st);
-  if (t == CSA_BF16) k_attn_merge<uint16_t><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(po, pml, RH, S, (uint16_t*)out, lse);
-  else k_attn_merge<float><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(po, pml, RH, S, (float*)out, lse);
+  if (t == CSA_BF16)   // the bf16 kernels leave bf16 split averages
+    k_attn_merge<uint16_t, uint16_t><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(
+        reinterpret_cast<const uint16_t*>(po), pml, RH, S, (uint16_t*)out, lse);
+  else
+    k_attn_merge<float, float><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(po, pml, RH, S, (float*)out, lse);
   e = hipGetLastError();
   timer_after(CSA_KID_ATTN_MERGE, st);
   return e;
