@@ -387,6 +387,13 @@ __device__ __forceinline__ void gather_lds16(const void* src, uint32_t lds_base)
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
 }
 
+// The same with a wave-uniform base address (in scalar registers) and a
+// 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void gather_lds16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
 template <int N_OUT>
 __device__ __forceinline__ void wait_vm() {
   // s_waitcnt vmcnt(N_OUT), leaving expcnt and lgkmcnt unconstrained
@@ -622,6 +629,8 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
     for (int db = 0; db < kD / 16; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const uint16_t* dummy = q + r * H * kD;   // a finite row for slots without a key
+  // entry byte offsets fit 32 bits (and entry 0 exists)
+  const bool offs32 = N >= 1 && N <= ((int64_t)1 << 24);
   const uint16_t* kvb = kv + b * N * kD;
   const uint16_t* xwb = x_win + b * T_win * kD;
 
@@ -669,6 +678,17 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
 #pragma unroll
         for (int j = 0; j < LPT; ++j)
           gather_lds16(tb + grow[j] * kD + gcol[j], (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
+      } else if (SPARSE && offs32 && kk0 + kKT <= clen && t0k + kKT <= n_sel) {
+        // 64 selected entries: byte offsets from the batch's first entry (an
+        // entry outside [0, N) reads entry 0 and is marked)
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) {
+          const int32_t e = sidx[kk0 + grow[j]];
+          const bool ok = (uint32_t)e < (uint32_t)N;
+          bad |= !ok;
+          gather_lds16_s(kvb, (ok ? (uint32_t)e * (uint32_t)(kD * 2) : 0u) + (uint32_t)gcol[j] * 2u,
+                         (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
@@ -778,10 +798,10 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
       const float inv = l > 0.f ? 1.f / l : 0.f;
       uint16_t* orow = out + (r * H + head) * kD;
 #pragma unroll
-      for (int db = 0; db < kD / 16; ++db) {
-        const float v[4] = {O[hb][db][0] * inv, O[hb][db][1] * inv, O[hb][db][2] * inv, O[hb][db][3] * inv};
-        Elem<uint16_t>::store4(orow + 16 * db + 4 * g, v);
-      }
+      for (int db = 0; db < kD / 16; ++db)   // round to nearest even (v_cvt_pk_bf16_f32)
+        *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) =
+            make_uint2(cvt_pk_bf16(O[hb][db][0] * inv, O[hb][db][1] * inv),
+                       cvt_pk_bf16(O[hb][db][2] * inv, O[hb][db][3] * inv));
       if (lse && g == 0) lse[r * H + head] = l > 0.f ? (m[hb] + __log2f(l)) * kLn2 : -INFINITY;
     } else {
       // Partial result of this split: its own softmax average O / l in bf16
@@ -803,46 +823,67 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
 }
 
 // Merge of S partial results per (row, head), in split order. 256 threads =
-// 8 (row, head) pairs x 32 lanes x 4 channels; loads are unrolled so the S
-// partials of a pair are in flight together. Partials are unnormalised float
-// sums (PT = float) or bf16 split averages O / l (PT = uint16_t); (m, l) are
-// float, m in natural-log units.
+// 8 (row, head) pairs x 32 lanes x 4 channels. The splits are taken in
+// chunks of CH whose loads are all issued before any is used (one memory
+// round trip per chunk); a chunk is folded into the running (max, sum, O)
+// in split order. Partials are unnormalised float sums (PT = float) or
+// bf16 split averages O / l (PT = uint16_t); (m, l) are float, m in
+// natural-log units.
 template <typename T, typename PT>
 __global__ __launch_bounds__(256) void k_attn_merge(const PT* __restrict__ part_o, const float* __restrict__ part_ml,
                                                     int64_t RH, int S, T* __restrict__ out, float* __restrict__ lse) {
+  constexpr int CH = sizeof(PT) == 2 ? 32 : 16;
   const int64_t rh = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
   const int d0 = (threadIdx.x & 31) * 4;
   if (rh >= RH) return;
-  const float* ml = part_ml + 2 * rh * S;
-  float mx = -INFINITY;
-#pragma unroll 8
-  for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, ml[2 * sp]);
-  float l = 0.f;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml) + rh * S;
+  float M = -INFINITY, l = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};
-  if (mx != -INFINITY) {
-#pragma unroll 8
-    for (int sp = 0; sp < S; ++sp) {
-      const float e = __expf(ml[2 * sp] - mx);
-      float v[4], f;
+  for (int c0 = 0; c0 < S; c0 += CH) {
+    const int n = S - c0 < CH ? S - c0 : CH;
+    float2 mv[CH];
+    float v[CH][4];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      mv[j] = j < n ? ml[c0 + j] : make_float2(-INFINITY, 0.f);
       if constexpr (sizeof(PT) == 2) {
-        f = e * ml[2 * sp + 1];   // weight of the split average
+        const uint2 u = j < n ? *reinterpret_cast<const uint2*>(part_o + (rh * S + c0 + j) * kD + d0) : make_uint2(0, 0);
+        v[j][0] = __uint_as_float(u.x << 16); v[j][1] = __uint_as_float(u.x & 0xffff0000u);
+        v[j][2] = __uint_as_float(u.y << 16); v[j][3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+        const float4 u = j < n ? *reinterpret_cast<const float4*>(part_o + (rh * S + c0 + j) * kD + d0)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j][0] = u.x; v[j][1] = u.y; v[j][2] = u.z; v[j][3] = u.w;
+      }
+    }
+    float cm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) cm = fmaxf(cm, mv[j].x);
+    if (cm == -INFINITY) continue;   // uniform per pair
+    const float mn = fmaxf(M, cm);
+    const float a = M == -INFINITY ? 0.f : __expf(M - mn);
+    l *= a;
+    o[0] *= a; o[1] *= a; o[2] *= a; o[3] *= a;
+    M = mn;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float e = mv[j].x == -INFINITY ? 0.f : __expf(mv[j].x - M);
+      float f;
+      if constexpr (sizeof(PT) == 2) {
+        f = e * mv[j].y;   // weight of the split average
         l += f;
-        const uint2 u = *reinterpret_cast<const uint2*>(part_o + (rh * S + sp) * kD + d0);
-        v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-        v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
       } else {
         f = e;
-        l = fmaf(ml[2 * sp + 1], e, l);
-        const float4 u = *reinterpret_cast<const float4*>(part_o + (rh * S + sp) * kD + d0);
-        v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+        l = fmaf(mv[j].y, e, l);
       }
-      o[0] = fmaf(v[0], f, o[0]); o[1] = fmaf(v[1], f, o[1]); o[2] = fmaf(v[2], f, o[2]); o[3] = fmaf(v[3], f, o[3]);
+      o[0] = fmaf(v[j][0], f, o[0]); o[1] = fmaf(v[j][1], f, o[1]);
+      o[2] = fmaf(v[j][2], f, o[2]); o[3] = fmaf(v[j][3], f, o[3]);
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-  Elem<T>::store4(out + rh * kD + d0, v);
-  if (lse && d0 == 0) lse[rh] = l > 0.f ? mx + __logf(l) : -INFINITY;
+  const float r[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+  Elem<T>::store4(out + rh * kD + d0, r);
+  if (lse && d0 == 0) lse[rh] = l > 0.f ? M + __logf(l) : -INFINITY;
 }
 
 // ------------------------------------------------------------------ host side
