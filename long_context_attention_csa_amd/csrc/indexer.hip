@@ -1087,14 +1087,6 @@ static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N) {
   p.QB = Tq >= 4 ? 4 : 1;
   p.groups_per_batch = cdiv(Tq, p.QB);
   p.groups = B * p.groups_per_batch;
-  // Enough blocks to cover the chip several times: split entries when groups are few.
-  const int64_t want_blocks = 2048;
-  int64_t chunks = cdiv(want_blocks, p.groups);
-  const int64_t max_chunks = cdiv(N, 256);
-  if (chunks > max_chunks) chunks = max_chunks;
-  if (chunks < 1) chunks = 1;
-  p.chunk_entries = cdiv(cdiv(N, chunks), 64) * 64;
-  if (p.chunk_entries < 64) p.chunk_entries = 64;
   // Score buffer budget per pass: 1 GiB.
   const int64_t budget = (int64_t)1 << 30;
   const int64_t row_bytes = (N > 0 ? N : 1) * 4 + ((N + kGroup - 1) / kGroup) * 4;
@@ -1104,6 +1096,15 @@ static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N) {
   if (gpp > p.groups) gpp = p.groups;
   p.groups_per_pass = gpp;
   p.max_rows_per_pass = gpp * p.QB;
+  // Enough blocks per pass to cover the chip several times: split the
+  // entries when a pass has few query groups.
+  const int64_t want_blocks = 2048;
+  int64_t chunks = cdiv(want_blocks, gpp);
+  const int64_t max_chunks = cdiv(N, 256);
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks < 1) chunks = 1;
+  p.chunk_entries = cdiv(cdiv(N, chunks), 64) * 64;
+  if (p.chunk_entries < 64) p.chunk_entries = 64;
   return p;
 }
 
