@@ -1117,11 +1117,12 @@ size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N) {
   return rows * (size_t)N * 4 + rows * (size_t)groups_of(N) * 4 + 256;
 }
 
-// Batch shape of the key stream per format and queries per block (from a
-// sweep on MI355X at the 262k/1M-context decode shapes: deeper batching or
-// double buffering lowered occupancy without raising bandwidth).
+// Batch shape of the key stream per format and queries per block (from
+// sweeps on MI355X at the 262k/1M-context decode shapes and at the 65536-token
+// and 8192-query prefill shapes: deeper batching or double buffering lowered
+// occupancy without raising bandwidth, except 2 batches with 4 queries).
 template <int FMT, int QB> struct ScoreCfg {
-  static constexpr int UB = (FMT == CSA_FP4_E2M1 || QB > 1) ? 1 : 4;
+  static constexpr int UB = QB > 1 ? 2 : ((FMT == CSA_FP4_E2M1) ? 1 : 4);
   static constexpr bool DBUF = false;
 };
 
