@@ -1075,6 +1075,323 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float* __res
   write_sorted(sm, k, n, out);
 }
 
+// ------------------------------------------------------------------ short rows
+// Rows of n <= kSmallN scores (used for a whole launch when N <= kSmallN, e.g.
+// prefill rows over the compressed entries of a 64k-token sequence): one
+// 256-thread block per row; thread t keeps the order keys of entries
+// [64 t, 64 t + 64) in registers, so the row is read once. Keys are taken
+// relative to the row's smallest key (u = key - min, same order), and a 13-bit
+// histogram covers the top 13 significant bits of the row's span, so a row
+// whose scores lie close together still spreads over the bins (few
+// same-address LDS atomics). The histogram gives the bucket d1 of the k-th
+// largest key. Usual case (at most kSmallList keys in d1): one sweep marks the
+// keys above d1 in a per-thread 64-bit mask and lists the keys of d1 as
+// (u, inverted index) composites; a list key is chosen iff fewer than need of
+// the list's composites exceed it. Otherwise a second histogram over the next
+// 13 bits of the keys in d1 narrows the bucket, whose keys are ranked as
+// composites (at most kSmallCand) or, for heavy ties, bisected over the
+// remaining low bits of u (at most 6) and the inverted index. The chosen
+// entries form a bitmap (one 64-bit word per thread); one block scan places
+// them, staged in LDS and written out in order: ascending indices. Same total
+// order (score descending, index ascending) as the general kernel.
+constexpr int kSmallThreads = 256;
+constexpr int kSmallPer = 64;
+constexpr int64_t kSmallN = (int64_t)kSmallThreads * kSmallPer;   // 16384
+constexpr int kSmallBits = 13;
+constexpr int kSmallBins = 1 << kSmallBits;
+constexpr int kSmallCand = 512;
+constexpr int kSmallList = 256;
+
+struct SmallSmem {
+  uint32_t hist[kSmallBins + 64];   // + one spare bin per lane for entries past the row's end
+  unsigned long long cand[kSmallCand];
+  unsigned long long bits[kSmallThreads];   // chosen entries: bit j of word t is entry 64 t + j
+  uint32_t wsum[kSmallThreads / 64];
+  uint32_t wmin[kSmallThreads / 64], wmax[kSmallThreads / 64];
+  uint32_t bin, need, ncand;
+  unsigned long long thresh;
+};
+
+// Block-wide exclusive prefix of v (thread order) and total; one barrier.
+__device__ __forceinline__ uint32_t small_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(v);
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  uint32_t add = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kSmallThreads / 64; ++i) {
+    const uint32_t x = wsum[i];
+    add += i < wv ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  return add + incl - v;
+}
+
+__device__ __forceinline__ void small_clear(SmallSmem& sm) {
+  uint4* h = reinterpret_cast<uint4*>(sm.hist);
+#pragma unroll
+  for (int i = 0; i < kSmallBins / 4 / kSmallThreads; ++i) h[threadIdx.x + i * kSmallThreads] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Bucket of the target-th largest element of sm.hist (bins scanned from the
+// top): sets sm.bin and sm.need (target minus the count in higher bins).
+// Thread t sums bins [top - 32, top), top = kSmallBins - 32 t.
+__device__ __forceinline__ void small_find(SmallSmem& sm, uint32_t target) {
+  constexpr int BPT = kSmallBins / kSmallThreads;   // 32 bins per thread
+  constexpr int G = BPT / 4;                        // groups of 4 bins
+  const int top = kSmallBins - BPT * (int)threadIdx.x;
+  const uint4* h = reinterpret_cast<const uint4*>(sm.hist + top - BPT);
+  uint32_t gs[G], mine = 0;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const uint4 v = h[i];
+    gs[i] = (v.x + v.y) + (v.z + v.w);
+    mine += gs[i];
+  }
+  uint32_t total;
+  const uint32_t excl = small_scan(mine, sm.wsum, total);
+  if (excl < target && excl + mine >= target) {
+    // the group (from the top) that holds the target, then the bin in it
+    uint32_t above = excl;
+    int gi = 0;
+    bool done = false;
+#pragma unroll
+    for (int i = G - 1; i >= 0; --i) {
+      const bool hit = !done && above + gs[i] >= target;
+      gi = hit ? i : gi;
+      done = done || hit;
+      above += done ? 0u : gs[i];
+    }
+    const uint4 v = h[gi];
+    const uint32_t c[4] = {v.w, v.z, v.y, v.x};
+    uint32_t bin = 0, nd = 0;
+    done = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool hit = !done && above + c[q] >= target;
+      bin = hit ? (uint32_t)(top - BPT + 4 * gi + 3 - q) : bin;
+      nd = hit ? target - above : nd;
+      done = done || hit;
+      above += c[q];
+    }
+    sm.bin = bin;
+    sm.need = nd;
+  }
+  __syncthreads();
+}
+
+// The value passes through an empty asm statement: the compiler cannot reuse
+// per-entry masks derived from it across passes (which would hold 64 lane
+// masks in scalar registers and spill them).
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Pins a mask built bit by bit: the OR chain stays sequential (a balanced OR
+// tree would hold all 64 bits in registers at once).
+__device__ __forceinline__ void pin_mask(unsigned long long& t) {
+  uint32_t lo = (uint32_t)t, hi = (uint32_t)(t >> 32);
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  t = ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+__global__ __launch_bounds__(kSmallThreads) void k_topk_small(const float* __restrict__ sbase, int64_t srow0,
+                                                              int64_t row0, const int32_t* __restrict__ q_pos,
+                                                              int64_t N, int ratio, int k,
+                                                              int32_t* __restrict__ idx_out) {
+  __shared__ SmallSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t r = row0 + blockIdx.x;
+  const int n = (int)visible(q_pos[r], ratio, N);   // <= kSmallN
+  int32_t* out = idx_out + r * (int64_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kSmallThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* srow = sbase + (r - srow0) * N;
+  const int base = tid * kSmallPer;
+  const int nv = n - base < 0 ? 0 : (n - base > kSmallPer ? kSmallPer : n - base);
+  uint32_t key[kSmallPer];
+  uint32_t tmax = 0u, tinv = 0u;   // largest key and largest ~key (= ~smallest key) of the thread
+  if (nv == kSmallPer && (reinterpret_cast<uintptr_t>(srow + base) & 15) == 0) {
+#pragma unroll
+    for (int j = 0; j < kSmallPer; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(srow + base + j);
+      key[j] = order_key(v.x); key[j + 1] = order_key(v.y); key[j + 2] = order_key(v.z); key[j + 3] = order_key(v.w);
+    }
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) { tmax = max(tmax, key[j]); tinv = max(tinv, ~key[j]); }
+  } else if (nv > 0) {
+    // entries past the row's end repeat its last entry: the range is unchanged
+    // and every later pass skips them (j >= nv)
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) key[j] = order_key(srow[base + min(j, nv - 1)]);
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) { tmax = max(tmax, key[j]); tinv = max(tinv, ~key[j]); }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) key[j] = 0u;
+  }
+  small_clear(sm);
+  tmax = wave_umax(tmax);
+  tinv = wave_umax(tinv);
+  if (lane == 0) { sm.wmax[wv] = tmax; sm.wmin[wv] = tinv; }
+  if (tid == 0) sm.ncand = 0u;
+  __syncthreads();
+  uint32_t kmax = 0u, kinv = 0u;
+#pragma unroll
+  for (int i = 0; i < kSmallThreads / 64; ++i) { kmax = max(kmax, sm.wmax[i]); kinv = max(kinv, sm.wmin[i]); }
+  const uint32_t kmin = ~kinv;
+#pragma unroll
+  for (int j = 0; j < kSmallPer; ++j) key[j] -= kmin;   // u = key - kmin (order kept for the valid keys)
+  const uint32_t span = kmax - kmin;
+  const int bits = span ? 32 - __clz(span) : 0;
+  const int s1 = bits > kSmallBits ? bits - kSmallBits : 0;   // u >> s1 < kSmallBins
+  const int s2 = s1 > kSmallBits ? s1 - kSmallBits : 0;       // <= 6
+  const int w2 = s1 - s2;                                     // bits of the second histogram in use
+  // Each pass below takes its own copies of the loop-invariant values
+  // (fresh), so no per-entry mask or shifted key is kept from one pass to the
+  // next.
+  const unsigned long long valid = nv >= kSmallPer ? ~0ull : ((1ull << nv) - 1ull);
+  if (nv > 0) {  // pass 1
+    const int nvp = fresh(nv), sp = fresh(s1);
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) atomicAdd(&sm.hist[j < nvp ? key[j] >> sp : kSmallBins + lane], 1u);
+  }
+  __syncthreads();
+  small_find(sm, (uint32_t)k);
+  const uint32_t d1 = sm.bin, need1 = sm.need;
+  const uint32_t cnt1 = sm.hist[d1];
+  unsigned long long take = 0;   // bit j: entry base + j is chosen
+  if (cnt1 <= (uint32_t)kSmallList) {
+    if (nv > 0) {
+      const int nvp = fresh(nv), sp = fresh(s1);
+#pragma unroll
+      for (int j = 0; j < kSmallPer; ++j) {
+        const uint32_t bj = key[j] >> sp;
+        take |= (unsigned long long)(bj > d1) << j;
+        if (j < nvp && bj == d1) sm.cand[atomicAdd(&sm.ncand, 1u)] = composite(key[j], base + j);
+        if ((j & 7) == 7) pin_mask(take);
+      }
+    }
+    sm.bits[tid] = take & valid;
+    __syncthreads();
+    if ((uint32_t)tid < cnt1) {
+      const unsigned long long v = sm.cand[tid];
+      uint32_t rank = 0;
+      for (uint32_t e = 0; e < cnt1; ++e) rank += sm.cand[e] > v ? 1u : 0u;
+      if (rank < need1) {
+        const int i = composite_index(v);
+        atomicOr(&sm.bits[i >> 6], 1ull << (i & 63));
+      }
+    }
+    __syncthreads();
+    take = sm.bits[tid];
+  } else {
+    small_clear(sm);
+    __syncthreads();
+    {  // pass 2: the next bits of the keys of bucket d1
+      const int nvp = fresh(nv), sp = fresh(s1), sq = fresh(s2);
+#pragma unroll
+      for (int j = 0; j < kSmallPer; ++j)
+        if (j < nvp && (key[j] >> sp) == d1) atomicAdd(&sm.hist[(key[j] >> sq) & (kSmallBins - 1)], 1u);
+    }
+    __syncthreads();
+    small_find(sm, need1);
+    // bucket pre of u >> s2; need >= 1 of its keys are taken
+    const uint32_t pre = (d1 << w2) | (sm.bin & ((1u << w2) - 1u)), need = sm.need;
+    uint32_t ceq = 0;
+    {
+      const int nvp = fresh(nv), sq = fresh(s2);
+#pragma unroll
+      for (int j = 0; j < kSmallPer; ++j) ceq += (j < nvp && (key[j] >> sq) == pre) ? 1u : 0u;
+    }
+    uint32_t ncand;
+    uint32_t pos = small_scan(ceq, sm.wsum, ncand);
+    uint32_t thu, thi;   // threshold (u, index): taken iff u > thu, or u == thu and index <= thi
+    if (ncand <= (uint32_t)kSmallCand) {
+      if (ceq) {
+        const int nvp = fresh(nv), sq = fresh(s2);
+#pragma unroll
+        for (int j = 0; j < kSmallPer; ++j)
+          if (j < nvp && (key[j] >> sq) == pre) sm.cand[pos++] = composite(key[j], base + j);
+      }
+      __syncthreads();
+      for (uint32_t c = tid; c < ncand; c += kSmallThreads) {
+        const unsigned long long v = sm.cand[c];
+        uint32_t rank = 0;
+        for (uint32_t e = 0; e < ncand; ++e) rank += sm.cand[e] > v ? 1u : 0u;
+        if (rank == need - 1) sm.thresh = v;   // composites are distinct: exactly one
+      }
+      __syncthreads();
+      thu = (uint32_t)(sm.thresh >> 32);
+      thi = 0xffffffffu - (uint32_t)sm.thresh;
+    } else {
+      // Heavy ties: bisection over x = (low s2 bits of u, 16383 - index), which
+      // orders the bucket's keys like their composites.
+      uint32_t t = 0;
+      for (int bt = s2 + 13; bt >= 0; --bt) {
+        const uint32_t c = t | (1u << bt);
+        const int nvp = fresh(nv), sq = fresh(s2);
+        const uint32_t lowm = (1u << sq) - 1u;
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kSmallPer; ++j) {
+          const uint32_t x = ((key[j] & lowm) << 14) | (uint32_t)(kSmallN - 1 - (base + j));
+          cnt += (j < nvp && (key[j] >> sq) == pre && x >= c) ? 1u : 0u;
+        }
+        uint32_t tot;
+        (void)small_scan(cnt, sm.wsum, tot);
+        __syncthreads();   // wsum is rewritten by the next round
+        if (tot >= need) t = c;
+      }
+      thu = (pre << s2) | (t >> 14);
+      thi = (uint32_t)(kSmallN - 1) - (t & (uint32_t)(kSmallN - 1));
+    }
+    // taken: keys above the threshold key, and ties of it up to its index
+    // (every key above bucket pre is above thu, which lies in the bucket)
+#pragma unroll
+    for (int j = 0; j < kSmallPer; ++j) {
+      take |= (unsigned long long)(key[j] > thu || (key[j] == thu && (uint32_t)(base + j) <= thi)) << j;
+      if ((j & 7) == 7) pin_mask(take);
+    }
+    take &= valid;
+  }
+  // Output: the chosen entries in index order (exactly k of them).
+  uint32_t total;
+  uint32_t o = small_scan((uint32_t)__popcll(take), sm.wsum, total);
+  if (k <= kSmallBins) {
+    uint32_t* stage = sm.hist;   // free once every thread has passed the scan
+    while (take) {
+      const int j = __builtin_ctzll(take);
+      stage[o++] = (uint32_t)(base + j);
+      take &= take - 1;
+    }
+    __syncthreads();
+    if ((k & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+      for (int i = 4 * tid; i < k; i += 4 * kSmallThreads)
+        *reinterpret_cast<uint4*>(out + i) = *reinterpret_cast<const uint4*>(stage + i);
+    } else {
+      for (int i = tid; i < k; i += kSmallThreads) out[i] = (int32_t)stage[i];
+    }
+  } else {
+    while (take) {
+      const int j = __builtin_ctzll(take);
+      out[o++] = base + j;
+      take &= take - 1;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 struct IndexPlan {
@@ -1220,7 +1537,11 @@ hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const flo
       if (e != hipSuccess) return e;
     }
     timer_before(CSA_KID_TOPK, s);
-    k_topk_select<<<dim3((unsigned)(rhi - rlo)), kTopkThreads, 0, s>>>(sb, sr0, gb, gr0, rlo, q_pos, N, ratio, k, idx_out);
+    if (N <= kSmallN)   // every row is short: one 256-thread block per row
+      k_topk_small<<<dim3((unsigned)(rhi - rlo)), kSmallThreads, 0, s>>>(sb, sr0, rlo, q_pos, N, ratio, k, idx_out);
+    else
+      k_topk_select<<<dim3((unsigned)(rhi - rlo)), kTopkThreads, 0, s>>>(sb, sr0, gb, gr0, rlo, q_pos, N, ratio, k,
+                                                                        idx_out);
     hipError_t e = hipGetLastError();
     timer_after(CSA_KID_TOPK, s);
     if (e != hipSuccess) return e;

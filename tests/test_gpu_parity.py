@@ -298,6 +298,31 @@ def test_indexer_heavy_ties_overflow_path():
     assert np.array_equal(got[0], np.arange(k)) and np.array_equal(got[1], np.arange(k))
 
 
+def test_indexer_short_rows_heavy_ties():
+    """N <= 16384 (one 256-thread block per row): all scores equal, so the
+    threshold bucket holds every entry and the bisection branch runs; a second
+    row takes three score values (ties at the threshold, bisection again); a
+    third takes 40 values (a few hundred ties, the candidate-list branch); a
+    fourth is short of k. Lowest indices win, as in the oracle."""
+    N, k = 12000, 400
+    q_i = np.zeros((1, 4, 4, 64), np.float32)
+    q_i[0, 1, :, 0] = 1.0
+    q_i[0, 2, :, 1] = 1.0
+    k_i = np.ones((1, N, 64), np.float32)
+    k_i[0, :, 0] = (np.arange(N) % 3).astype(np.float32)
+    k_i[0, :, 1] = (np.arange(N) % 40).astype(np.float32)
+    w = np.ones((1, 4, 4), np.float32)
+    q_pos = np.array([[4 * N, 4 * N, 4 * N, 4 * 200]], np.int32)
+    idx = C.indexer_topk(dev(q_i), None, dev(w), dev(k_i), None, "f32", dev(q_pos, torch.int32), 4, k, 64)
+    got = host(idx)[0]
+    assert np.array_equal(got[0], np.arange(k))
+    assert np.array_equal(got[1], np.arange(2, 3 * k, 3))
+    s2 = 4.0 * (np.arange(N) % 40)
+    assert np.array_equal(got[2], O.topk_select(s2[None], [N], k)[0])
+    nv = int(O.visible_entries(4 * 200, 4, N))
+    assert np.array_equal(got[3, :nv], np.arange(nv)) and np.all(got[3, nv:] == -1)
+
+
 def test_indexer_small_n_and_padding():
     N, k = 50, 64
     d = syn.csa_decode(24, B=1, N=N, H=16, H_I=8, d_I=64)
