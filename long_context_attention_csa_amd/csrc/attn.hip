@@ -366,39 +366,10 @@ struct TileLanes {
   }
 };
 
-typedef __attribute__((address_space(3))) const i32x4 lds_i32x4;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-// Hides a value from the optimiser, so that constant offsets added to it are
-// not reassociated into separately hoisted registers.
-__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ i32x4 lds_read_b128(uint32_t a) { return *(lds_i32x4*)(size_t)a; }
 __device__ __forceinline__ s16x4 lds_read_tr16(uint32_t a) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(size_t)a);
-}
-
-// One global_load_lds_dwordx4: each lane's 16 bytes at src go to LDS address
-// lds_base + 16 * lane. Written as asm so that the compiler does not treat it
-// as an LDS store: it would otherwise drain every outstanding load before
-// each later LDS access or barrier (it cannot tell the ring slots apart),
-// which serialises the gather pipeline. Completion is tracked explicitly with
-// wait_vm() followed by a barrier before a slot is read. No register outputs.
-__device__ __forceinline__ void gather_lds16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
-}
-
-// The same with a wave-uniform base address (in scalar registers) and a
-// 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void gather_lds16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory", "m0");
-}
-
-template <int N_OUT>
-__device__ __forceinline__ void wait_vm() {
-  // s_waitcnt vmcnt(N_OUT), leaving expcnt and lgkmcnt unconstrained
-  static_assert(N_OUT >= 0 && N_OUT < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N_OUT & 15) | ((N_OUT >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));

@@ -506,6 +506,163 @@ __global__ __launch_bounds__(256) void k_index_score_dec(
   }
 }
 
+// ------------------------------------------------------------------ prefill score kernel (fp8)
+// fp8 keys with d_I = 128, four consecutive queries of one sequence per block
+// of four waves, one query per wave (so only that query's operands and
+// weights stay in registers). The block streams its entry range through an
+// LDS ring of kPfDepth stages of 64 entries (8 KB of key rows plus 64 float
+// scales), filled by global_load_lds: wave w copies rows 16w .. 16w + 15 of
+// each stage (two dwordx4 loads) and their scales (one dword load, 16 lanes),
+// so every wave has the same number of loads per stage in flight. Within a
+// 128-byte row, 16-byte chunk c is stored at position c ^ ((row >> 1) & 7):
+// the 16 rows read by the 16 lanes of one B-operand load then fall on 16
+// distinct bank groups.
+//
+// Each wave scores all 64 entries of a stage for its query: 4 tiles x HB
+// head blocks of v_mfma_scale_f32_16x16x128_f8f6f4, the weighted ReLU head
+// sum in registers and one reduce-scatter that leaves lane l with entry
+// base + l. Its score row segment (one 256-byte store) and group maxima are
+// stored one stage later, so a store is never the last memory operation
+// before a wait: waits count only loads issued after the awaited stage,
+// which also covers every earlier store (vmcnt counts both). Blocks run the
+// longest rows (last query groups) first.
+constexpr int kPfStage = 64;
+constexpr int kPfDepth = 4;
+constexpr int kPfRowB = 128;
+constexpr int kPfLoads = 3;   // loads per stage per wave
+
+template <int HB>
+__global__ __launch_bounds__(256) void k_index_score_pf(
+    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
+    int64_t Tq, int64_t N, int H_I, int ratio, int64_t group0, int64_t groups_per_batch,
+    int64_t chunk_entries, float* __restrict__ sbase, int64_t srow0, float* __restrict__ gbase, int64_t grow0) {
+  __shared__ __align__(16) uint8_t ring[kPfDepth][kPfStage * kPfRowB];
+  __shared__ __align__(16) float sring[kPfDepth][kPfStage];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int g = lane >> 4, col = lane & 15;
+  const int64_t grp = group0 + (int64_t)(gridDim.y - 1 - blockIdx.y);
+  const int64_t b = grp / groups_per_batch;
+  const int64_t t0 = (grp % groups_per_batch) * 4;
+  const int nq = (int)((Tq - t0) < 4 ? (Tq - t0) : 4);
+  int64_t nmax = 0, nvw = 0;
+#pragma unroll
+  for (int qi = 0; qi < 4; ++qi) {
+    const int64_t n = qi < nq ? visible(q_pos[b * Tq + t0 + qi], ratio, N) : 0;
+    nmax = n > nmax ? n : nmax;
+    nvw = qi == wv ? n : nvw;
+  }
+  const int64_t e_begin = (int64_t)blockIdx.x * chunk_entries;
+  if (e_begin >= nmax) return;
+  const int64_t e_end = (e_begin + chunk_entries) < nmax ? (e_begin + chunk_entries) : nmax;
+  const int S = (int)((e_end - e_begin + kPfStage - 1) / kPfStage);
+  const bool live_q = wv < nq;
+  const int64_t r = b * Tq + t0 + (live_q ? wv : 0);
+
+  // query operands (A: head = lane % 16 of head block hb, K bytes [32g, 32g + 32))
+  // and weights with the query's row scale folded in; padded heads are zero
+  i32x8 qa[HB];
+  float wq[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int hrow = hb * 16 + col;
+    const bool live = hrow < H_I;
+    const uint8_t* qrow = q_idx + (r * H_I + (live ? hrow : 0)) * kPfRowB + 32 * g;
+    const i32x4 x0 = *reinterpret_cast<const i32x4*>(qrow);
+    const i32x4 x1 = *reinterpret_cast<const i32x4*>(qrow + 16);
+    qa[hb] = live ? i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]} : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int h = hb * 16 + 4 * g + rr;
+      const int hs = h < H_I ? h : 0;
+      const float wv_ = w[r * H_I + hs] * q_scale[r * H_I + hs];
+      wq[hb][rr] = h < H_I ? wv_ : 0.f;
+    }
+  }
+  wait_vm<0>();   // the operand loads above are complete before the ring's loads start
+
+  const uint8_t* kb = k_idx + b * N * kPfRowB;
+  const float* ksb = k_scale + b * N;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[0][0];
+  const uint32_t sring0 = (uint32_t)(uintptr_t)&sring[0][0];
+  // Stage loads: rows past N - 1 read row N - 1 (scores of entries past the
+  // visible count are never stored).
+  const int rA = 16 * wv + (lane >> 3);          // row of the first load, +8 for the second
+  const uint32_t cA = (uint32_t)((lane & 7) ^ ((rA >> 1) & 7));
+  const uint32_t cB = (uint32_t)((lane & 7) ^ (((rA + 8) >> 1) & 7));
+  auto issue = [&](int st) {
+    const int64_t e0 = e_begin + (int64_t)kPfStage * st;
+    const int64_t eb = e0 < N - 1 ? e0 : N - 1;                     // uniform
+    const int lim = (int)((N - 1 - eb) < (kPfStage - 1) ? (N - 1 - eb) : (kPfStage - 1));
+    const uint8_t* sb = kb + eb * kPfRowB;
+    const uint32_t slot = ring0 + (uint32_t)(st % kPfDepth) * (kPfStage * kPfRowB);
+    const uint32_t ra = (uint32_t)(rA < lim ? rA : lim), rb = (uint32_t)(rA + 8 < lim ? rA + 8 : lim);
+    gather_lds16_s(sb, ra * kPfRowB + 16u * cA, slot + (uint32_t)(16 * wv) * kPfRowB);
+    gather_lds16_s(sb, rb * kPfRowB + 16u * cB, slot + (uint32_t)(16 * wv + 8) * kPfRowB);
+    if (lane < 16) {
+      const int rs = 16 * wv + lane;
+      gather_lds4_s(ksb + eb, 4u * (uint32_t)(rs < lim ? rs : lim),
+                    sring0 + (uint32_t)(st % kPfDepth) * (kPfStage * 4) + (uint32_t)(64 * wv));
+    }
+  };
+#pragma unroll
+  for (int st = 0; st < kPfDepth - 1; ++st)
+    if (st < S) issue(st);
+
+  // B-operand LDS offsets of this lane (tile t adds 16 * 128 * t):
+  // row col, chunks 2g and 2g + 1, swizzled by (col >> 1) & 7
+  const uint32_t sw = (uint32_t)((col >> 1) & 7);
+  const uint32_t ob0 = (uint32_t)col * kPfRowB + 16u * ((2u * g) ^ sw);
+  const uint32_t ob1 = (uint32_t)col * kPfRowB + 16u * ((2u * g + 1u) ^ sw);
+  const int64_t G = (N + kGroup - 1) / kGroup;
+  float* srow = sbase + (r - srow0) * N;
+  float* grow = gbase + (r - grow0) * G;
+  float prev_s = 0.f, prev_g = 0.f;
+  int64_t prev_e = -1;
+  auto store_prev = [&]() {
+    if (live_q && prev_e >= 0) {
+      if (prev_e + lane < nvw) srow[prev_e + lane] = prev_s;
+      if (col == 0 && prev_e + 16 * g < nvw) grow[(prev_e + 16 * g) / kGroup] = prev_g;
+    }
+  };
+  for (int st = 0; st < S; ++st) {
+    if (st + kPfDepth - 2 < S) wait_vm<(kPfDepth - 2) * kPfLoads>();
+    else if (st + 1 < S) wait_vm<kPfLoads>();
+    else wait_vm<0>();
+    __syncthreads();   // stage st is in LDS; every wave is done with stage st - 1
+    if (st + kPfDepth - 1 < S) issue(st + kPfDepth - 1);
+    store_prev();
+    if (live_q) {
+      uint32_t kslot = ring0 + (uint32_t)(st % kPfDepth) * (kPfStage * kPfRowB);
+      opaque(kslot);
+      float part[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const i32x4 b0 = lds_read_b128(kslot + ob0 + 2048u * t);
+        const i32x4 b1 = lds_read_b128(kslot + ob1 + 2048u * t);
+        const i32x8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        float pt = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hb], bv, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                             0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) pt = fmaf(wq[hb][rr], relu_bits(acc[rr]), pt);
+        }
+        part[t] = pt;
+      }
+      const float kscale = sring[st % kPfDepth][lane];
+      const float sc = reduce_scatter4(part[0], part[1], part[2], part[3]) * kscale;
+      const int64_t e0 = e_begin + (int64_t)kPfStage * st;
+      prev_s = sc;
+      prev_g = max_row16(e0 + lane < nvw ? sc : -INFINITY);
+      prev_e = e0;
+    }
+  }
+  store_prev();
+}
+
 // ------------------------------------------------------------------ block helpers
 
 // Inclusive scan across the block of one value per thread (kTopkThreads
@@ -1478,10 +1635,32 @@ static void dispatch_hb(int HB, dim3 grid, hipStream_t s, const void* q, const v
   }
 }
 
+static void launch_score_pf(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
+                            const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
+                            int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb,
+                            int64_t gr0) {
+  const auto* q8 = static_cast<const uint8_t*>(q);
+  const auto* k8 = static_cast<const uint8_t*>(kk);
+  const auto* qsf = static_cast<const float*>(qs);
+  const auto* ksf = static_cast<const float*>(ks);
+  switch (HB) {
+    case 1: k_index_score_pf<1><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 2: k_index_score_pf<2><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 3: k_index_score_pf<3><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    default: k_index_score_pf<4><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+  }
+}
+
 template <int FMT>
 static void dispatch_fmt(int DI, int QB, int HB, dim3 grid, hipStream_t s, const void* q, const void* qs,
                          const float* w, const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N,
                          int H_I, int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
+  if constexpr (FMT == CSA_FP8_E4M3) {
+    if (DI == 128 && QB == 4) {
+      launch_score_pf(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+      return;
+    }
+  }
   if (DI == 128) {
     if (QB == 4) dispatch_hb<FMT, 128, 4>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
     else dispatch_hb<FMT, 128, 1>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
