@@ -506,39 +506,53 @@ __global__ __launch_bounds__(256) void k_index_score_dec(
   }
 }
 
-// ------------------------------------------------------------------ prefill score kernel (fp8)
-// fp8 keys with d_I = 128, four consecutive queries of one sequence per block
-// of four waves, one query per wave (so only that query's operands and
+// ------------------------------------------------------------------ prefill score kernel (fp8 / fp4)
+// Quantised keys with d_I = 128, four consecutive queries of one sequence per
+// block of four waves, one query per wave (so only that query's operands and
 // weights stay in registers). The block streams its entry range through an
-// LDS ring of kPfDepth stages of 64 entries (8 KB of key rows plus 64 float
-// scales), filled by global_load_lds: wave w copies rows 16w .. 16w + 15 of
-// each stage (two dwordx4 loads) and their scales (one dword load, 16 lanes),
-// so every wave has the same number of loads per stage in flight. Within a
-// 128-byte row, 16-byte chunk c is stored at position c ^ ((row >> 1) & 7):
-// the 16 rows read by the 16 lanes of one B-operand load then fall on 16
-// distinct bank groups.
+// LDS ring of kPfDepth stages of 64 entries (key rows plus one 32-bit scale
+// word per entry: the fp8 row scale, or the four E8M0 block scales of an fp4
+// row), filled by global_load_lds: wave w copies rows 16w .. 16w + 15 of each
+// stage (fp8: two dwordx4 loads, fp4: one) and their scale words (one dword
+// load, 16 lanes), so every wave has the same number of loads per stage in
+// flight. Within a row, 16-byte chunk c is stored at position
+// c ^ ((row >> 1) & 7) (fp8, 128-byte rows) or c ^ ((row >> 2) & 3) (fp4,
+// 64-byte rows): the 16 rows read by the 16 lanes of one B-operand load then
+// fall on 16 distinct bank groups.
 //
 // Each wave scores all 64 entries of a stage for its query: 4 tiles x HB
-// head blocks of v_mfma_scale_f32_16x16x128_f8f6f4, the weighted ReLU head
-// sum in registers and one reduce-scatter that leaves lane l with entry
-// base + l. Its score row segment (one 256-byte store) and group maxima are
-// stored one stage later, so a store is never the last memory operation
-// before a wait: waits count only loads issued after the awaited stage,
-// which also covers every earlier store (vmcnt counts both). Blocks run the
-// longest rows (last query groups) first.
+// head blocks of v_mfma_scale_f32_16x16x128_f8f6f4 (fp4: the E8M0 block
+// scales of query and key go to the instruction's scale operands), the
+// weighted ReLU head sum in registers and one reduce-scatter that leaves lane
+// l with entry base + l. Its score row segment (one 256-byte store) and group
+// maxima are stored one stage later, so a store is never the last memory
+// operation before a wait: waits count only loads issued after the awaited
+// stage, which also covers every earlier store (vmcnt counts both). Blocks run
+// the longest rows (last query groups) first.
 constexpr int kPfStage = 64;
 constexpr int kPfDepth = 4;
-constexpr int kPfRowB = 128;
-constexpr int kPfLoads = 3;   // loads per stage per wave
 
-template <int HB>
+template <int FMT> struct PfCfg;
+template <> struct PfCfg<CSA_FP8_E4M3> {
+  static constexpr int RB = 128;   // bytes per key row
+  static constexpr int LOADS = 3;  // loads per stage per wave
+};
+template <> struct PfCfg<CSA_FP4_E2M1> {
+  static constexpr int RB = 64;
+  static constexpr int LOADS = 2;
+};
+
+template <int FMT, int HB>
 __global__ __launch_bounds__(256) void k_index_score_pf(
-    const uint8_t* __restrict__ q_idx, const float* __restrict__ q_scale, const float* __restrict__ w,
-    const uint8_t* __restrict__ k_idx, const float* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
+    const uint8_t* __restrict__ q_idx, const void* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_idx, const void* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
     int64_t Tq, int64_t N, int H_I, int ratio, int64_t group0, int64_t groups_per_batch,
     int64_t chunk_entries, float* __restrict__ sbase, int64_t srow0, float* __restrict__ gbase, int64_t grow0) {
-  __shared__ __align__(16) uint8_t ring[kPfDepth][kPfStage * kPfRowB];
-  __shared__ __align__(16) float sring[kPfDepth][kPfStage];
+  constexpr bool F4 = FMT == CSA_FP4_E2M1;
+  constexpr int RB = PfCfg<FMT>::RB, LOADS = PfCfg<FMT>::LOADS;
+  constexpr int SB = kPfStage * RB;   // key bytes per stage
+  __shared__ __align__(16) uint8_t ring[kPfDepth][SB];
+  __shared__ __align__(16) uint32_t sring[kPfDepth][kPfStage];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, col = lane & 15;
@@ -560,46 +574,66 @@ __global__ __launch_bounds__(256) void k_index_score_pf(
   const bool live_q = wv < nq;
   const int64_t r = b * Tq + t0 + (live_q ? wv : 0);
 
-  // query operands (A: head = lane % 16 of head block hb, K bytes [32g, 32g + 32))
-  // and weights with the query's row scale folded in; padded heads are zero
+  // Query operands (A: head = lane % 16 of head block hb; fp8: K bytes
+  // [32g, 32g + 32), fp4: K elements [32g, 32g + 32) = bytes [16g, 16g + 16)
+  // with their E8M0 block scale) and weights (fp8: the query's row scale
+  // folded in); padded heads are zero.
   i32x8 qa[HB];
+  int qs8[HB];
   float wq[HB][4];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int hrow = hb * 16 + col;
     const bool live = hrow < H_I;
-    const uint8_t* qrow = q_idx + (r * H_I + (live ? hrow : 0)) * kPfRowB + 32 * g;
-    const i32x4 x0 = *reinterpret_cast<const i32x4*>(qrow);
-    const i32x4 x1 = *reinterpret_cast<const i32x4*>(qrow + 16);
-    qa[hb] = live ? i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]} : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    const int64_t qr = r * H_I + (live ? hrow : 0);
+    if constexpr (F4) {
+      const i32x4 x0 = *reinterpret_cast<const i32x4*>(q_idx + qr * RB + 16 * g);
+      qa[hb] = live ? i32x8{x0[0], x0[1], x0[2], x0[3], 0, 0, 0, 0} : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      const int sc = reinterpret_cast<const uint8_t*>(q_scale)[qr * 4 + g];
+      qs8[hb] = live ? sc : 127;
+    } else {
+      const uint8_t* qrow = q_idx + qr * RB + 32 * g;
+      const i32x4 x0 = *reinterpret_cast<const i32x4*>(qrow);
+      const i32x4 x1 = *reinterpret_cast<const i32x4*>(qrow + 16);
+      qa[hb] = live ? i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]} : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      qs8[hb] = 127;
+    }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int h = hb * 16 + 4 * g + rr;
       const int hs = h < H_I ? h : 0;
-      const float wv_ = w[r * H_I + hs] * q_scale[r * H_I + hs];
+      float wv_ = w[r * H_I + hs];
+      if constexpr (!F4) wv_ *= reinterpret_cast<const float*>(q_scale)[r * H_I + hs];
       wq[hb][rr] = h < H_I ? wv_ : 0.f;
     }
   }
   wait_vm<0>();   // the operand loads above are complete before the ring's loads start
 
-  const uint8_t* kb = k_idx + b * N * kPfRowB;
-  const float* ksb = k_scale + b * N;
+  const uint8_t* kb = k_idx + b * N * RB;
+  const uint32_t* ksb = reinterpret_cast<const uint32_t*>(k_scale) + b * N;
   const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[0][0];
   const uint32_t sring0 = (uint32_t)(uintptr_t)&sring[0][0];
   // Stage loads: rows past N - 1 read row N - 1 (scores of entries past the
-  // visible count are never stored).
-  const int rA = 16 * wv + (lane >> 3);          // row of the first load, +8 for the second
-  const uint32_t cA = (uint32_t)((lane & 7) ^ ((rA >> 1) & 7));
-  const uint32_t cB = (uint32_t)((lane & 7) ^ (((rA + 8) >> 1) & 7));
+  // visible count are never stored). One dwordx4 load covers 1 KB: 8 rows
+  // (fp8) or 16 rows (fp4).
+  constexpr int RPL = 1024 / RB;                 // rows per load
+  constexpr int CPR = RB / 16;                   // chunks per row
+  const int rA = 16 * wv + lane / CPR;           // row of the first load (+8 for the second, fp8)
+  auto swz = [](int row) { return F4 ? ((row >> 2) & 3) : ((row >> 1) & 7); };
+  const uint32_t cA = (uint32_t)((lane % CPR) ^ swz(rA));
+  const uint32_t cB = (uint32_t)((lane % CPR) ^ swz(rA + 8));
   auto issue = [&](int st) {
     const int64_t e0 = e_begin + (int64_t)kPfStage * st;
     const int64_t eb = e0 < N - 1 ? e0 : N - 1;                     // uniform
     const int lim = (int)((N - 1 - eb) < (kPfStage - 1) ? (N - 1 - eb) : (kPfStage - 1));
-    const uint8_t* sb = kb + eb * kPfRowB;
-    const uint32_t slot = ring0 + (uint32_t)(st % kPfDepth) * (kPfStage * kPfRowB);
-    const uint32_t ra = (uint32_t)(rA < lim ? rA : lim), rb = (uint32_t)(rA + 8 < lim ? rA + 8 : lim);
-    gather_lds16_s(sb, ra * kPfRowB + 16u * cA, slot + (uint32_t)(16 * wv) * kPfRowB);
-    gather_lds16_s(sb, rb * kPfRowB + 16u * cB, slot + (uint32_t)(16 * wv + 8) * kPfRowB);
+    const uint8_t* sb = kb + eb * RB;
+    const uint32_t slot = ring0 + (uint32_t)(st % kPfDepth) * SB;
+    const uint32_t ra = (uint32_t)(rA < lim ? rA : lim);
+    gather_lds16_s(sb, ra * RB + 16u * cA, slot + (uint32_t)(16 * wv) * RB);
+    if constexpr (!F4) {
+      const uint32_t rb = (uint32_t)(rA + 8 < lim ? rA + 8 : lim);
+      gather_lds16_s(sb, rb * RB + 16u * cB, slot + (uint32_t)(16 * wv + RPL) * RB);
+    }
     if (lane < 16) {
       const int rs = 16 * wv + lane;
       gather_lds4_s(ksb + eb, 4u * (uint32_t)(rs < lim ? rs : lim),
@@ -610,11 +644,12 @@ __global__ __launch_bounds__(256) void k_index_score_pf(
   for (int st = 0; st < kPfDepth - 1; ++st)
     if (st < S) issue(st);
 
-  // B-operand LDS offsets of this lane (tile t adds 16 * 128 * t):
-  // row col, chunks 2g and 2g + 1, swizzled by (col >> 1) & 7
-  const uint32_t sw = (uint32_t)((col >> 1) & 7);
-  const uint32_t ob0 = (uint32_t)col * kPfRowB + 16u * ((2u * g) ^ sw);
-  const uint32_t ob1 = (uint32_t)col * kPfRowB + 16u * ((2u * g + 1u) ^ sw);
+  // B-operand LDS offsets of this lane (tile t adds 16 * RB * t): row col;
+  // fp8: chunks 2g and 2g + 1, fp4: chunk g; swizzled as stored
+  const uint32_t sw = (uint32_t)swz(col);
+  const uint32_t ob0 = F4 ? (uint32_t)col * RB + 16u * ((uint32_t)g ^ sw)
+                          : (uint32_t)col * RB + 16u * ((2u * g) ^ sw);
+  const uint32_t ob1 = (uint32_t)col * RB + 16u * ((2u * g + 1u) ^ sw);
   const int64_t G = (N + kGroup - 1) / kGroup;
   float* srow = sbase + (r - srow0) * N;
   float* grow = gbase + (r - grow0) * G;
@@ -627,33 +662,48 @@ __global__ __launch_bounds__(256) void k_index_score_pf(
     }
   };
   for (int st = 0; st < S; ++st) {
-    if (st + kPfDepth - 2 < S) wait_vm<(kPfDepth - 2) * kPfLoads>();
-    else if (st + 1 < S) wait_vm<kPfLoads>();
+    if (st + kPfDepth - 2 < S) wait_vm<(kPfDepth - 2) * LOADS>();
+    else if (st + 1 < S) wait_vm<LOADS>();
     else wait_vm<0>();
     __syncthreads();   // stage st is in LDS; every wave is done with stage st - 1
     if (st + kPfDepth - 1 < S) issue(st + kPfDepth - 1);
     store_prev();
     if (live_q) {
-      uint32_t kslot = ring0 + (uint32_t)(st % kPfDepth) * (kPfStage * kPfRowB);
+      uint32_t kslot = ring0 + (uint32_t)(st % kPfDepth) * SB;
       opaque(kslot);
+      uint32_t sslot = sring0 + (uint32_t)(st % kPfDepth) * (kPfStage * 4);
       float part[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const i32x4 b0 = lds_read_b128(kslot + ob0 + 2048u * t);
-        const i32x4 b1 = lds_read_b128(kslot + ob1 + 2048u * t);
-        const i32x8 bv = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        i32x8 bv;
+        int ks8 = 127;
+        if constexpr (F4) {
+          const i32x4 b0 = lds_read_b128(kslot + ob0 + (uint32_t)(16 * RB * t));
+          bv = i32x8{b0[0], b0[1], b0[2], b0[3], 0, 0, 0, 0};
+          const uint32_t sw4 = *(__attribute__((address_space(3))) const uint32_t*)(size_t)(sslot + 4u * (16 * t + col));
+          ks8 = (int)((sw4 >> (8 * g)) & 0xffu);
+        } else {
+          const i32x4 b0 = lds_read_b128(kslot + ob0 + (uint32_t)(16 * RB * t));
+          const i32x4 b1 = lds_read_b128(kslot + ob1 + (uint32_t)(16 * RB * t));
+          bv = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        }
         float pt = 0.f;
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
-          const f32x4 acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hb], bv, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                                             0, 0, 0, 127, 0, 127);
+          f32x4 acc;
+          if constexpr (F4)
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hb], bv, f32x4{0.f, 0.f, 0.f, 0.f}, 4, 4, 0,
+                                                                   qs8[hb], 0, ks8);
+          else
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hb], bv, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                   127, 0, 127);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) pt = fmaf(wq[hb][rr], relu_bits(acc[rr]), pt);
         }
         part[t] = pt;
       }
-      const float kscale = sring[st % kPfDepth][lane];
-      const float sc = reduce_scatter4(part[0], part[1], part[2], part[3]) * kscale;
+      float sc = reduce_scatter4(part[0], part[1], part[2], part[3]);
+      if constexpr (!F4) sc *= __uint_as_float(sring[st % kPfDepth][lane]);
       const int64_t e0 = e_begin + (int64_t)kPfStage * st;
       prev_s = sc;
       prev_g = max_row16(e0 + lane < nvw ? sc : -INFINITY);
@@ -1635,19 +1685,18 @@ static void dispatch_hb(int HB, dim3 grid, hipStream_t s, const void* q, const v
   }
 }
 
+template <int FMT>
 static void launch_score_pf(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
                             const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
                             int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb,
                             int64_t gr0) {
   const auto* q8 = static_cast<const uint8_t*>(q);
   const auto* k8 = static_cast<const uint8_t*>(kk);
-  const auto* qsf = static_cast<const float*>(qs);
-  const auto* ksf = static_cast<const float*>(ks);
   switch (HB) {
-    case 1: k_index_score_pf<1><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    case 2: k_index_score_pf<2><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    case 3: k_index_score_pf<3><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    default: k_index_score_pf<4><<<grid, 256, 0, s>>>(q8, qsf, w, k8, ksf, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 1: k_index_score_pf<FMT, 1><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 2: k_index_score_pf<FMT, 2><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 3: k_index_score_pf<FMT, 3><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    default: k_index_score_pf<FMT, 4><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
   }
 }
 
@@ -1655,9 +1704,9 @@ template <int FMT>
 static void dispatch_fmt(int DI, int QB, int HB, dim3 grid, hipStream_t s, const void* q, const void* qs,
                          const float* w, const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N,
                          int H_I, int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
-  if constexpr (FMT == CSA_FP8_E4M3) {
+  if constexpr (FMT == CSA_FP8_E4M3 || FMT == CSA_FP4_E2M1) {
     if (DI == 128 && QB == 4) {
-      launch_score_pf(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+      launch_score_pf<FMT>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
       return;
     }
   }

@@ -237,21 +237,24 @@ def test_indexer_exact_grid_prefill(fmt, d_I, H_I):
     assert np.array_equal(host(idx), want)
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
 @pytest.mark.parametrize("H_I", [19, 64])
-def test_indexer_exact_grid_prefill_batched(H_I):
-    """fp8 keys, d_I = 128, two sequences whose positions differ (the second is
+def test_indexer_exact_grid_prefill_batched(fmt, H_I):
+    """fp8 / fp4 keys, d_I = 128, two sequences whose positions differ (the second is
     shifted so its late rows see every entry), a query count that leaves a
     partial last group of queries, padded head blocks when H_I < 64: exact
     scores on the visible entries and bit-exact indices."""
     B, T, d_I, k = 2, 1001, 128, 96
     N = 260
-    q_i = syn.integers(51, (B, T, H_I, d_I), -4, 4)
-    k_i = syn.integers(52, (B, N, d_I), -4, 4)
+    if fmt == "fp4":
+        q_i, k_i = syn.fp4_grid(51, (B, T, H_I, d_I)), syn.fp4_grid(52, (B, N, d_I))
+    else:
+        q_i, k_i = syn.integers(51, (B, T, H_I, d_I), -4, 4), syn.integers(52, (B, N, d_I), -4, 4)
     w = syn.grid_weights(53, (B, T, H_I))
     q_pos = np.stack([np.arange(T), np.arange(T) + 37]).astype(np.int32)
-    _print("indexer grid prefill batched", H_I)
-    qc, qs, kc, ks = _grid_operands("fp8", q_i, k_i)
-    idx, sc = C.indexer_topk(qc, qs, dev(w), kc, ks, "fp8", dev(q_pos, torch.int32), 4, k, d_I, want_scores=True)
+    _print("indexer grid prefill batched", fmt, H_I)
+    qc, qs, kc, ks = _grid_operands(fmt, q_i, k_i)
+    idx, sc = C.indexer_topk(qc, qs, dev(w), kc, ks, fmt, dev(q_pos, torch.int32), 4, k, d_I, want_scores=True)
     scores, want = _oracle_topk(q_i, w, k_i, q_pos, 4, k)
     got_s = host(sc)
     vis = np.isfinite(scores)
