@@ -536,6 +536,19 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   const int32_t r32 = blockIdx.x, b32 = r32 / (int32_t)Tq;
   const int64_t r = r32, b = b32;
   const int hg = blockIdx.y / S, sp = blockIdx.y % S;
+  // Selected indices [c0, c0 + cnt) of the row copied to LDS, one dword per
+  // lane, all copies in flight together (slots past the selected entries
+  // belong to window keys and are never read).
+  auto stage_sel = [&](int64_t c0, int cnt) {
+    const int32_t* isrc = idx + r * k + c0;
+    for (int j = 0; j * NT < cnt; ++j) {
+      const int i = j * NT + wv * 64 + lane;
+      if (i < cnt) gather_lds4_s(isrc, 4u * (uint32_t)i, (uint32_t)(uintptr_t)(sidx + j * NT + wv * 64));
+    }
+  };
+  // With one split the first section starts at the row's first selected
+  // entry whatever the query position: its indices need no loaded value.
+  if (SPARSE && S == 1) stage_sel(0, k < kSelChunk ? k : kSelChunk);
   if constexpr (TS > 1) {
     // the query gathers go first: their addresses need no loaded value
 #pragma unroll
@@ -610,10 +623,9 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   for (int64_t c0 = kbeg; c0 < kend; c0 += kSelChunk) {
     const int clen = (int)((kend - c0) < kSelChunk ? (kend - c0) : kSelChunk);
     if (SPARSE) {
-      for (int i = tid; i < clen; i += NT) {
-        const int64_t ki = c0 + i;
-        sidx[i] = ki < n_sel ? idx[r * k + ki] : -1;
-      }
+      // The section's selected indices go straight to LDS (with one split
+      // the first section's were issued at entry).
+      if (!(S == 1 && c0 == 0)) stage_sel(c0, (int)(n_sel - c0 < (int64_t)clen ? n_sel - c0 : (int64_t)clen));
       wait_vm<0>();   // every thread: the query and index loads are done before any gather
       __syncthreads();
       if (c0 == kbeg) load_q();
