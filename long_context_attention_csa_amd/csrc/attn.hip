@@ -805,8 +805,8 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   }
 }
 
-// Merge of S partial results per (row, head), in split order. 256 threads =
-// 8 (row, head) pairs x 32 lanes x 4 channels. The splits are taken in
+// Merge of S partial results per (row, head), in split order. 32 lanes x 4
+// channels per (row, head) pair, blockDim / 32 pairs per block. The splits are taken in
 // chunks of CH whose loads are all issued before any is used (one memory
 // round trip per chunk); a chunk is folded into the running (max, sum, O)
 // in split order. Partials are unnormalised float sums (PT = float) or
@@ -816,7 +816,7 @@ template <typename T, typename PT>
 __global__ __launch_bounds__(256) void k_attn_merge(const PT* __restrict__ part_o, const float* __restrict__ part_ml,
                                                     int64_t RH, int S, T* __restrict__ out, float* __restrict__ lse) {
   constexpr int CH = sizeof(PT) == 2 ? 32 : 16;
-  const int64_t rh = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int64_t rh = (int64_t)blockIdx.x * (blockDim.x >> 5) + (threadIdx.x >> 5);
   const int d0 = (threadIdx.x & 31) * 4;
   if (rh >= RH) return;
   const float2* ml = reinterpret_cast<const float2*>(part_ml) + rh * S;
@@ -906,6 +906,14 @@ size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max) {
   return (size_t)rows * H * S * (kD + 2) * 4;
 }
 
+// (row, head) pairs per merge block: 2 to 8, about 512 blocks (the few pairs
+// of a decode step spread over more compute units than 8 per block allow)
+static int merge_pairs(int64_t RH) {
+  int p = 2;
+  while (p < 8 && RH / (2 * p) >= 512) p *= 2;
+  return p;
+}
+
 constexpr int kRing = 2;   // ring slots per block (bf16 path, one tile stream): a small ring leaves LDS
                            // for more resident blocks, which hides more latency than deeper prefetch
 constexpr int kRing2 = 6;  // ring slots with two tile streams (2 computed + 4 in flight)
@@ -979,10 +987,10 @@ hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void*
   const int64_t RH = rows * H;
   timer_before(CSA_KID_ATTN_MERGE, st);
   if (t == CSA_BF16)   // the bf16 kernels leave bf16 split averages
-    k_attn_merge<uint16_t, uint16_t><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(
+    k_attn_merge<uint16_t, uint16_t><<<dim3((unsigned)cdiv(RH, merge_pairs(RH))), 32 * merge_pairs(RH), 0, st>>>(
         reinterpret_cast<const uint16_t*>(po), pml, RH, S, (uint16_t*)out, lse);
   else
-    k_attn_merge<float, float><<<dim3((unsigned)cdiv(RH, 8)), 256, 0, st>>>(po, pml, RH, S, (float*)out, lse);
+    k_attn_merge<float, float><<<dim3((unsigned)cdiv(RH, merge_pairs(RH))), 32 * merge_pairs(RH), 0, st>>>(po, pml, RH, S, (float*)out, lse);
   e = hipGetLastError();
   timer_after(CSA_KID_ATTN_MERGE, st);
   return e;
