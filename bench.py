@@ -18,7 +18,7 @@ library's kernel timer), the CPU oracle timed on a bounded sample, and extra
 workloads (CSA decode at 262k context; prefill TFLOP/s) under "extras".
 
 Usage: python bench.py [--steps K] [--warmup W]
-                       [--extras decode4,prefill_csa,prefill_hca,prefill_chunk|none]
+                       [--extras decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk|none]
 """
 from __future__ import annotations
 
@@ -326,6 +326,64 @@ def prefill_csa(torch, C, syn, iters):
             "sparse_attn_frac_bf16_peak": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
 
+def decode_append(torch, C, syn, iters):
+    """Decode-time cache maintenance of the 1M-context layer pair, B = 8: each
+    step appends one token per sequence to the CSA KV cache (bf16 entries), the
+    CSA indexer-key cache (fp4 entries + E8M0 scales) and the HCA cache (bf16),
+    through their state rings. The positions end a 128-token block, so every
+    call writes a CSA entry and an HCA entry (the most work a step can do)."""
+    dev, bf = "cuda", torch.bfloat16
+    B, L, W = 8, 1 << 20, 128
+    N, NH = L // 4, L // 128
+    s = 5000
+    rows = [syn.normal_device(s + i, (B, W), dev, bf) for i in range(10)]
+    pos = torch.full((B,), L - 1, dtype=torch.int32, device=dev)
+    E = torch.empty(B, N, W, dtype=bf, device=dev)
+    KI = torch.empty(B, N, W // 2, dtype=torch.uint8, device=dev)
+    KIs = torch.empty(B, N, W // 32, dtype=torch.uint8, device=dev)
+    EH = torch.empty(B, NH, W, dtype=bf, device=dev)
+    st_kv = syn.normal_device(s + 20, (B, 8, 4, W), dev, bf)
+    st_ix = syn.normal_device(s + 21, (B, 8, 4, W), dev, bf)
+    st_h = syn.normal_device(s + 22, (B, 128, 2, W), dev, bf)
+    ops = [
+        ("csa_kv", lambda: C.csa_compress_append(*rows[0:4], pos, st_kv, E, None, 4)),
+        ("csa_index_keys_fp4", lambda: C.csa_compress_append(*rows[4:8], pos, st_ix, KI, KIs, 4)),
+        ("hca", lambda: C.hca_compress_append(rows[8], rows[9], pos, st_h, EH, 128)),
+    ]
+    # device time per op and per step: 50 steps captured in one graph,
+    # replayed (a single call is shorter than its host-side launch path, and a
+    # graph replay has a fixed cost of its own)
+    per_graph, reps = 50, 10
+    def graph_us(fns):
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                for f in fns:
+                    f()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * per_graph) * 1e3
+    t = {name: graph_us([f]) for name, f in ops}
+    step = graph_us([f for _, f in ops])
+    # bytes a step touches: ring rows read (CSA 7 earlier tokens x 4 streams,
+    # HCA 127 tokens x 2 streams), the new rows read and written to the ring,
+    # the entries written
+    rb = W * 2
+    byts = B * (2 * (7 * 4 + 4 + 4) * rb + (127 * 2 + 2 + 2) * rb + rb + W // 2 + W // 32 + rb)
+    return {"workload": "decode_append_pair_1m_ctx", "batch": B, "context": L,
+            "us": {k: round(v, 2) for k, v in t.items()}, "step_us": round(step, 2), "step_bytes": byts,
+            "timing": "hip graph replay"}
+
+
 def prefill_hca(torch, C, syn, iters):
     """Single HCA layer prefill, bf16, T = 131,072: 128:1 compression to 1024
     entries, then dense attention (64 heads) over all visible entries plus the
@@ -419,8 +477,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
-    ap.add_argument("--extras", default="decode4,prefill_csa,prefill_hca,prefill_chunk",
-                    help="comma list of decode4,prefill_csa,prefill_hca,prefill_chunk or 'none'")
+    ap.add_argument("--extras", default="decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk",
+                    help="comma list of decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk or 'none'")
     ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -496,7 +554,8 @@ def main():
             "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in kt4.items()}}
         del st4
         torch.cuda.empty_cache()
-    for key, fn in (("prefill_csa", prefill_csa), ("prefill_hca", prefill_hca), ("prefill_chunk", prefill_chunk)):
+    for key, fn in (("decode_append", decode_append), ("prefill_csa", prefill_csa), ("prefill_hca", prefill_hca),
+                    ("prefill_chunk", prefill_chunk)):
         if key in wanted:
             r = fn(torch, C, syn, args.prefill_iters)
             log(f"[bench] {r['workload']}: {r}")

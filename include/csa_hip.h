@@ -121,6 +121,51 @@ csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B,
                         int32_t width, int32_t ratio, void* out, csa_dtype out_t, void* stream);
 
 /*
+ * csa_compress_append — decode-time step of the CSA compressor (cf-1.com
+ * write-up §4.4: the KV cache keeps a state cache of recent uncompressed
+ * tokens beside the compressed entries; §3.1: entry j is made from stream A
+ * of block j and stream B of block j-1). For each sequence b, the new token's
+ * rows at absolute position pos[b] go into the sequence's state ring; when
+ * the token completes block j = (pos[b]+1)/ratio - 1 (and j < N_cap), entry
+ * j is computed exactly as csa_compress computes it (same device code: the
+ * same bits) and written to row j of the sequence's cache.
+ *   c_a, c_b, z_a, z_b  [B, width] of in_t: the new token of each sequence
+ *   pos       int32 [B]: its position; a negative position skips the sequence
+ *   state     [B, 2*ratio, 4, width] of in_t, caller-owned and persistent:
+ *             tokens t of the last 2*ratio positions at slot t % (2*ratio),
+ *             streams in the order c_a, c_b, z_a, z_b. Before the first
+ *             append of a sequence starting at position p0 > 0, slots of the
+ *             2*ratio - 1 tokens before p0 must hold those tokens (appending
+ *             them, with their outputs discarded, does it).
+ *   out       [B, N_cap, width] of out_t (and out_scale as in csa_compress:
+ *             [B, N_cap] float32 for fp8, [B, N_cap, width/32] uint8 for fp4)
+ *   width 64 or 128; ratio 1..128. Sequences of one call must be distinct.
+ */
+csa_status csa_compress_append(const void* c_a, const void* c_b, const void* z_a, const void* z_b,
+                               csa_dtype in_t, int64_t B, int32_t width, int32_t ratio, const int32_t* pos,
+                               void* state, int64_t N_cap, void* out, csa_dtype out_t, void* out_scale,
+                               void* stream);
+
+/*
+ * hca_compress_append — decode-time step of the HCA compressor (cf-1.com
+ * write-up §4.4 state cache; §3.2: one entry per 128 tokens). The new token
+ * (rows of c and z) at position pos[b] goes into the sequence's ring of the
+ * last ratio tokens; when it completes block j = (pos[b]+1)/ratio - 1 (and
+ * j < N_cap), entry j is computed exactly as hca_compress computes it and
+ * written to row j of the sequence's cache.
+ *   c, z   [B, width] of in_t (CSA_F32 or CSA_BF16)
+ *   pos    int32 [B]; a negative position skips the sequence
+ *   state  [B, ratio, 2, width] of in_t, caller-owned and persistent: token t
+ *          at slot t % ratio, streams c, z. Block j's first ratio - 1 tokens
+ *          must have been appended (or written there) before its last one.
+ *   out    [B, N_cap, width] of out_t (CSA_F32 or CSA_BF16)
+ *   width 64 or 128; ratio 1..4096.
+ */
+csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int64_t B, int32_t width,
+                               int32_t ratio, const int32_t* pos, void* state, int64_t N_cap, void* out,
+                               csa_dtype out_t, void* stream);
+
+/*
  * indexer_topk — lightning-indexer scores and per-query top-k selection
  * (cf-1.com write-up §3.1: each query picks its top-k compressed entries
  * through the lightning indexer; §2.4: k = 512 or 1024; §3.4: low-rank,

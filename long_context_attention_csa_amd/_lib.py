@@ -31,6 +31,10 @@ SIGNATURES = {
     "csa_quantize_rows": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _P, ctypes.c_int, _P, _P]),
     "csa_compress": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, ctypes.c_int, _P, _P]),
     "hca_compress": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I64, _I32, _I32, _P, ctypes.c_int, _P]),
+    "csa_compress_append": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, _I64, _I32, _I32, _P, _P, _I64, _P,
+                                           ctypes.c_int, _P, _P]),
+    "hca_compress_append": (ctypes.c_int, [_P, _P, ctypes.c_int, _I64, _I32, _I32, _P, _P, _I64, _P, ctypes.c_int,
+                                           _P]),
     "indexer_topk_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32, ctypes.c_int]),
     "indexer_topk": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _I32, _I32, _I32,
                                     _I32, _P, _P, _P, _SZ, _P]),

@@ -13,6 +13,10 @@ hipError_t launch_csa_compress(const void*, const void*, const void*, const void
                                int, void*, csa_dtype, void*, hipStream_t);
 hipError_t launch_hca_compress(const void*, const void*, csa_dtype, int64_t, int64_t, int, int, void*, csa_dtype,
                                hipStream_t);
+hipError_t launch_csa_append(const void*, const void*, const void*, const void*, csa_dtype, int64_t, int, int,
+                             const int32_t*, void*, int64_t, void*, csa_dtype, void*, hipStream_t);
+hipError_t launch_hca_append(const void*, const void*, csa_dtype, int64_t, int, int, const int32_t*, void*, int64_t,
+                             void*, csa_dtype, hipStream_t);
 hipError_t launch_quantize_rows(const void*, csa_dtype, int64_t, int, void*, csa_dtype, void*, hipStream_t);
 size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N);
 hipError_t launch_indexer_topk(const void*, const void*, const float*, const void*, const void*, csa_dtype,
@@ -145,6 +149,48 @@ csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B,
   CSA_REQUIRE(c && z && out, CSA_ERR_NULL, "hca_compress: NULL tensor");
   return hip_status(launch_hca_compress(c, z, in_t, B, T, width, ratio, out, out_t, (hipStream_t)stream),
                     "hca_compress");
+}
+
+csa_status csa_compress_append(const void* c_a, const void* c_b, const void* z_a, const void* z_b,
+                               csa_dtype in_t, int64_t B, int32_t width, int32_t ratio, const int32_t* pos,
+                               void* state, int64_t N_cap, void* out, csa_dtype out_t, void* out_scale,
+                               void* stream) {
+  g_last_error.clear();
+  CSA_REQUIRE(is_dtype(in_t) && is_dtype(out_t), CSA_ERR_UNSUPPORTED, "csa_compress_append: unknown dtype");
+  CSA_REQUIRE(is_float(in_t), CSA_ERR_UNSUPPORTED, "csa_compress_append: input must be CSA_F32 or CSA_BF16");
+  CSA_REQUIRE(B >= 0 && N_cap >= 0, CSA_ERR_SHAPE, "csa_compress_append: B=%lld N_cap=%lld", (long long)B,
+              (long long)N_cap);
+  CSA_REQUIRE(B <= INT32_MAX, CSA_ERR_SHAPE, "csa_compress_append: B=%lld (< 2^31)", (long long)B);
+  CSA_REQUIRE(width == 64 || width == 128, CSA_ERR_UNSUPPORTED, "csa_compress_append: width %d (64 or 128)", width);
+  CSA_REQUIRE(ratio >= 1 && ratio <= 128, CSA_ERR_SHAPE, "csa_compress_append: ratio %d (1..128)", ratio);
+  if (is_float(out_t))
+    CSA_REQUIRE(out_scale == nullptr, CSA_ERR_SHAPE, "csa_compress_append: out_scale must be NULL for a float output");
+  if (B == 0) return CSA_OK;
+  CSA_REQUIRE(c_a && c_b && z_a && z_b && pos && state && out, CSA_ERR_NULL, "csa_compress_append: NULL tensor");
+  CSA_REQUIRE(is_float(out_t) || out_scale, CSA_ERR_NULL, "csa_compress_append: out_scale required for %s output",
+              out_t == CSA_FP8_E4M3 ? "fp8" : "fp4");
+  return hip_status(launch_csa_append(c_a, c_b, z_a, z_b, in_t, B, width, ratio, pos, state, N_cap, out, out_t,
+                                      out_scale, (hipStream_t)stream),
+                    "csa_compress_append");
+}
+
+csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int64_t B, int32_t width,
+                               int32_t ratio, const int32_t* pos, void* state, int64_t N_cap, void* out,
+                               csa_dtype out_t, void* stream) {
+  g_last_error.clear();
+  CSA_REQUIRE(is_dtype(in_t) && is_dtype(out_t), CSA_ERR_UNSUPPORTED, "hca_compress_append: unknown dtype");
+  CSA_REQUIRE(is_float(in_t) && is_float(out_t), CSA_ERR_UNSUPPORTED,
+              "hca_compress_append: input and output must be CSA_F32 or CSA_BF16");
+  CSA_REQUIRE(B >= 0 && N_cap >= 0, CSA_ERR_SHAPE, "hca_compress_append: B=%lld N_cap=%lld", (long long)B,
+              (long long)N_cap);
+  CSA_REQUIRE(B <= INT32_MAX, CSA_ERR_SHAPE, "hca_compress_append: B=%lld (< 2^31)", (long long)B);
+  CSA_REQUIRE(width == 64 || width == 128, CSA_ERR_UNSUPPORTED, "hca_compress_append: width %d (64 or 128)", width);
+  CSA_REQUIRE(ratio >= 1 && ratio <= 4096, CSA_ERR_SHAPE, "hca_compress_append: ratio %d (1..4096)", ratio);
+  if (B == 0) return CSA_OK;
+  CSA_REQUIRE(c && z && pos && state && out, CSA_ERR_NULL, "hca_compress_append: NULL tensor");
+  return hip_status(launch_hca_append(c, z, in_t, B, width, ratio, pos, state, N_cap, out, out_t,
+                                      (hipStream_t)stream),
+                    "hca_compress_append");
 }
 
 size_t indexer_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t k,

@@ -100,6 +100,46 @@ def hca_compress(c, z, ratio: int = 128, out_fmt: str | None = None):
     return out
 
 
+def csa_append_state(B: int, width: int, ratio: int = 4, dtype=torch.bfloat16, device="cuda"):
+    """A zeroed state ring for csa_compress_append: [B, 2*ratio, 4, width]."""
+    return torch.zeros(B, 2 * ratio, 4, width, dtype=dtype, device=device)
+
+
+def hca_append_state(B: int, width: int, ratio: int = 128, dtype=torch.bfloat16, device="cuda"):
+    """A zeroed state ring for hca_compress_append: [B, ratio, 2, width]."""
+    return torch.zeros(B, ratio, 2, width, dtype=dtype, device=device)
+
+
+def csa_compress_append(c_a, c_b, z_a, z_b, pos, state, out, out_scale=None, ratio: int = 4):
+    """Decode-time CSA compressor step: new token rows [B, width] at positions pos
+    (int32 [B]); updates state [B, 2*ratio, 4, width] and, for sequences whose
+    token completes a block, writes that entry into out [B, N_cap, width] (and
+    out_scale for fp8/fp4 caches)."""
+    _contig(c_a, c_b, z_a, z_b, pos, state, out, out_scale)
+    in_t = _float_dtype(c_a)
+    B, width = c_a.shape
+    N_cap = out.shape[1]
+    if out.dtype == torch.uint8:
+        fmt = CSA_FP8_E4M3 if out.shape[2] == width else CSA_FP4_E2M1
+    else:
+        fmt = _float_dtype(out)
+    check("csa_compress_append", lib().csa_compress_append(_ptr(c_a), _ptr(c_b), _ptr(z_a), _ptr(z_b), in_t, B, width,
+                                                           ratio, _ptr(pos), _ptr(state), N_cap, _ptr(out), fmt,
+                                                           _ptr(out_scale), _stream()))
+
+
+def hca_compress_append(c, z, pos, state, out, ratio: int = 128):
+    """Decode-time HCA compressor step: new token rows [B, width] at positions pos;
+    updates state [B, ratio, 2, width] and writes completed entries into out
+    [B, N_cap, width]."""
+    _contig(c, z, pos, state, out)
+    in_t = _float_dtype(c)
+    B, width = c.shape
+    check("hca_compress_append", lib().hca_compress_append(_ptr(c), _ptr(z), in_t, B, width, ratio, _ptr(pos),
+                                                           _ptr(state), out.shape[1], _ptr(out), _float_dtype(out),
+                                                           _stream()))
+
+
 def indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt: str) -> int:
     return int(lib().indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, FMT[fmt]))
 
