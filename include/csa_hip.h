@@ -166,6 +166,22 @@ csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int
                                csa_dtype out_t, void* stream);
 
 /*
+ * csa_set_batch_invariant / csa_get_batch_invariant — batch-invariant mode
+ * (cf-1.com write-up §4.3: the kernel library is batch-invariant and
+ * deterministic). Process-wide switch, off by default. When on, the
+ * attention calls (sparse_attn_fwd, dense_compressed_attn_fwd) plan their key
+ * splits and tile streams from one sequence's query count Tq instead of the
+ * batch's B*Tq, so each sequence's output and LSE are the same bits whatever
+ * else is in the batch (the indexer and the compressors already compute each
+ * row on its own). Decode batches then use the split count of a single
+ * sequence. The workspace-size queries follow the mode: query them after
+ * setting it, and do not change it between a query and the call it sizes.
+ * Every result is deterministic in both modes.
+ */
+csa_status csa_set_batch_invariant(int32_t on);
+int32_t csa_get_batch_invariant(void);
+
+/*
  * indexer_topk — lightning-indexer scores and per-query top-k selection
  * (cf-1.com write-up §3.1: each query picks its top-k compressed entries
  * through the lightning indexer; §2.4: k = 512 or 1024; §3.4: low-rank,

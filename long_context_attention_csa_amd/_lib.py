@@ -44,6 +44,8 @@ SIGNATURES = {
     "dense_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
     "dense_compressed_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32,
                                                  _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "csa_set_batch_invariant": (ctypes.c_int, [_I32]),
+    "csa_get_batch_invariant": (_I32, []),
     "csa_kernel_timer_start": (ctypes.c_int, [_I32, _I32]),
     "csa_kernel_timer_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32]),
 }

@@ -22,7 +22,9 @@ size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N);
 hipError_t launch_indexer_topk(const void*, const void*, const float*, const void*, const void*, csa_dtype,
                                const int32_t*, int64_t, int64_t, int64_t, int, int, int, int, int32_t*, float*, void*,
                                hipStream_t);
-size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max);
+size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max);
+void set_batch_invariant(int on);
+int batch_invariant();
 hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void* kv, const int32_t* idx,
                             const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                             int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio,
@@ -193,6 +195,14 @@ csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int
                     "hca_compress_append");
 }
 
+csa_status csa_set_batch_invariant(int32_t on) {
+  g_last_error.clear();
+  set_batch_invariant(on);
+  return CSA_OK;
+}
+
+int32_t csa_get_batch_invariant(void) { return batch_invariant(); }
+
 size_t indexer_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t k,
                                    csa_dtype qk_t) {
   (void)H_I; (void)d_I; (void)k; (void)qk_t;
@@ -251,7 +261,7 @@ static csa_status check_attn_common(const char* fn, const void* q, const void* k
 size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, int32_t k, int32_t window) {
   (void)d;
   if (B <= 0 || Tq <= 0 || H <= 0) return 0;
-  return attn_ws_bytes(B * Tq, H, (int64_t)k + window);
+  return attn_ws_bytes(B, Tq, H, (int64_t)k + window);
 }
 
 csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
@@ -277,7 +287,7 @@ csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, co
 size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t d, int32_t window) {
   (void)d;
   if (B <= 0 || Tq <= 0 || H <= 0) return 0;
-  return attn_ws_bytes(B * Tq, H, N + window);
+  return attn_ws_bytes(B, Tq, H, N + window);
 }
 
 csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* x_win, const int32_t* win_start,

@@ -24,6 +24,8 @@
 // triples are merged in a fixed order, so results are deterministic.
 #include "common.hpp"
 
+#include <atomic>
+
 namespace csa {
 
 constexpr int kKT = 64;            // keys per tile
@@ -898,12 +900,20 @@ static AttnPlan plan_attention(int64_t rows, int H, int64_t nk_max) {
   return {(int)(s < 1 ? 1 : s)};
 }
 
+// Batch-invariant mode: the split count and the tile-stream choice are
+// planned from one sequence's rows (Tq) instead of the whole batch (B * Tq),
+// so a sequence's result does not depend on what else is in the batch.
+static std::atomic<int> g_batch_invariant{0};
+void set_batch_invariant(int on) { g_batch_invariant.store(on ? 1 : 0); }
+int batch_invariant() { return g_batch_invariant.load(); }
+static int64_t plan_rows(int64_t B, int64_t Tq) { return g_batch_invariant.load() ? Tq : B * Tq; }
+
 int attn_splits(int64_t rows, int H, int64_t nk_max) { return plan_attention(rows, H, nk_max).S; }
 
-size_t attn_ws_bytes(int64_t rows, int H, int64_t nk_max) {
-  const int S = attn_splits(rows, H, nk_max);
+size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max) {
+  const int S = attn_splits(plan_rows(B, Tq), H, nk_max);
   if (S == 1) return 0;
-  return (size_t)rows * H * S * (kD + 2) * 4;
+  return (size_t)(B * Tq) * H * S * (kD + 2) * 4;
 }
 
 // (row, head) pairs per merge block: 2 to 8, about 512 blocks (the few pairs
@@ -922,10 +932,10 @@ template <typename T, bool SPARSE, int NW, int HPW>
 static void launch_attn_t(dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                           const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                           int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
-                          int S, void* out, float* lse, float* po, float* pml) {
+                          int S, bool two_streams, void* out, float* lse, float* po, float* pml) {
   if constexpr (sizeof(T) == 2) {
     // Few rows (decode): two tile streams per block, two waves per SIMD.
-    if (grid.x * grid.y <= 1024)
+    if (two_streams)
       k_attn16<SPARSE, NW, HPW, kRing2, 2><<<grid, NW * 2 * 64, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)x_win, win_start, sink, q_pos, Tq, N, T_win,
           H, k, window, ratio, scale, S, (uint16_t*)out, lse, po, pml);
@@ -944,11 +954,11 @@ template <typename T, bool SPARSE>
 static void launch_attn_sh(AttnShape sh, dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                            const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                            int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
-                           int S, void* out, float* lse, float* po, float* pml) {
+                           int S, bool two_streams, void* out, float* lse, float* po, float* pml) {
 #define CSA_ATTN_CASE(NW_, HPW_)                                                                               \
   if (sh.nw == NW_ && sh.hpw == HPW_) {                                                                        \
     launch_attn_t<T, SPARSE, NW_, HPW_>(grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, \
-                                        k, window, ratio, scale, S, out, lse, po, pml);                        \
+                                        k, window, ratio, scale, S, two_streams, out, lse, po, pml);           \
     return;                                                                                                    \
   }
   CSA_ATTN_CASE(4, 2)
@@ -967,19 +977,22 @@ hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void*
   const int64_t rows = B * Tq;
   if (rows == 0) return hipSuccess;
   const AttnShape sh = pick_shape(H);
-  const AttnPlan pl = plan_attention(rows, H, nk_max);
+  const int64_t prow = plan_rows(B, Tq);
+  const AttnPlan pl = plan_attention(prow, H, nk_max);
   const int S = pl.S;
+  // two tile streams when the planned grid is small (few rows: decode)
+  const bool two_streams = prow * (H / (16 * sh.nw * sh.hpw)) * S <= 1024;
   float* po = reinterpret_cast<float*>(ws);
   float* pml = po ? po + (size_t)rows * H * S * kD : nullptr;
   const dim3 grid((unsigned)rows, (unsigned)((H / (16 * sh.nw * sh.hpw)) * S));
   const int kid = sparse ? CSA_KID_SPARSE_ATTN : CSA_KID_DENSE_ATTN;
   timer_before(kid, st);
   if (t == CSA_BF16) {
-    if (sparse) launch_attn_sh<uint16_t, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
-    else launch_attn_sh<uint16_t, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
+    if (sparse) launch_attn_sh<uint16_t, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
+    else launch_attn_sh<uint16_t, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
   } else {
-    if (sparse) launch_attn_sh<float, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
-    else launch_attn_sh<float, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, out, lse, po, pml);
+    if (sparse) launch_attn_sh<float, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
+    else launch_attn_sh<float, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
   }
   hipError_t e = hipGetLastError();
   timer_after(kid, st);

@@ -140,6 +140,15 @@ def hca_compress_append(c, z, pos, state, out, ratio: int = 128):
                                                            _stream()))
 
 
+def set_batch_invariant(on: bool) -> None:
+    """Batch-invariant mode of the attention calls (process-wide)."""
+    check("csa_set_batch_invariant", lib().csa_set_batch_invariant(1 if on else 0))
+
+
+def batch_invariant() -> bool:
+    return bool(lib().csa_get_batch_invariant())
+
+
 def indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt: str) -> int:
     return int(lib().indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, FMT[fmt]))
 

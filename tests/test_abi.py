@@ -109,3 +109,35 @@ def test_timer_validation():
     lib = _lib.lib()
     assert lib.csa_kernel_timer_start(0, 4) == SHAPE
     assert lib.csa_kernel_timer_start(4, 0) == SHAPE
+
+
+def test_append_validation():
+    lib = _lib.lib()
+    # width 96 unsupported; ratio 0; fp8 cache without its scale; NULL state
+    assert lib.csa_compress_append(P, P, P, P, 1, 2, 96, 4, P, P, 10, P, 1, None, None) == UNSUP
+    assert lib.csa_compress_append(P, P, P, P, 1, 2, 128, 0, P, P, 10, P, 1, None, None) == SHAPE
+    assert lib.csa_compress_append(P, P, P, P, 1, 2, 128, 4, P, P, 10, P, 2, None, None) == NULL
+    assert lib.csa_compress_append(P, P, P, P, 1, 2, 128, 4, P, None, 10, P, 1, None, None) == NULL
+    assert lib.csa_compress_append(P, P, P, P, 1, 0, 128, 4, None, None, 10, None, 1, None, None) == OK
+    assert lib.hca_compress_append(P, P, 1, 2, 128, 128, P, P, 10, P, 2, None) == UNSUP   # fp8 output
+    assert lib.hca_compress_append(P, P, 1, 2, 128, 0, P, P, 10, P, 1, None) == SHAPE
+    assert lib.hca_compress_append(P, P, 1, 2, 128, 128, None, P, 10, P, 1, None) == NULL
+
+
+def test_batch_invariant_switch():
+    """Host logic of the batch-invariant mode: the switch, and the attention
+    workspace of a decode batch that plans each sequence's splits alone."""
+    from long_context_attention_csa_amd import ops
+    assert not ops.batch_invariant()
+    default8 = ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128)
+    one = ops.dense_attn_workspace_size(1, 1, 8192, 128, 128, 128)
+    ops.set_batch_invariant(True)
+    try:
+        assert ops.batch_invariant()
+        assert ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128) == 8 * one
+        assert ops.sparse_attn_workspace_size(8, 1, 128, 128, 1024, 128) == \
+            8 * ops.sparse_attn_workspace_size(1, 1, 128, 128, 1024, 128)
+    finally:
+        ops.set_batch_invariant(False)
+    assert not ops.batch_invariant()
+    assert ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128) == default8
