@@ -275,6 +275,16 @@ def index_flops(n_vis, H_I, d_I):
     return float(np.sum(n_vis, dtype=np.float64)) * H_I * d_I * 2
 
 
+def bf16_score_variant(torch, C, iters, call, ws_bytes):
+    """Indexer with bfloat16 index scores on the same operands: op time and the
+    score / top-k kernel split (ms). Not part of the layer time."""
+    ws_b = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
+    fn = lambda: call(ws_b)
+    t = time_ops(torch, [("indexer_topk_bf16_scores", fn)], iters)["indexer_topk_bf16_scores"]
+    split = {kn: call_kernel_ms(torch, C, fn, kn) for kn in ("index_score", "topk")}
+    return {"ms": round(t, 4), "split_ms": {kn: (None if v is None else round(v, 4)) for kn, v in split.items()}}
+
+
 def prefill_csa(torch, C, syn, iters):
     """Single CSA layer prefill, bf16, T = 65,536: compress (KV and fp8 indexer
     keys), indexer top-512 over 16,384 entries (64 heads x 128, fp8), sparse
@@ -311,6 +321,9 @@ def prefill_csa(torch, C, syn, iters):
     ]
     t = time_ops(torch, ops, iters)
     split = {kn: call_kernel_ms(torch, C, ops[2][1], kn) for kn in ("index_score", "topk")}
+    bf = bf16_score_variant(torch, C, iters, lambda ws_b: C.indexer_topk(
+        qi, qs, w, st["KI"][0], st["KI"][1], "fp8", q_pos, 4, k, d_I, ws=ws_b, idx_out=st["idx"], bf16_scores=True),
+        C.indexer_topk_workspace_size(1, T, N, H_I, d_I, k, "fp8", bf16_scores=True))
     p = np.arange(T, dtype=np.int64)
     n = np.minimum(N, (p + 1) // 4)
     keys = np.minimum(k, n) + np.minimum(p + 1, W)
@@ -323,7 +336,8 @@ def prefill_csa(torch, C, syn, iters):
             "index_score_tflop_s": (None if not split["index_score"] else
                                     round(fl_i / (split["index_score"] * 1e-3) / 1e12, 2)),
             "sparse_attn_tflop_s": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12, 2),
-            "sparse_attn_frac_bf16_peak": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            "sparse_attn_frac_bf16_peak": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "indexer_bf16_scores": bf}
 
 
 def decode_append(torch, C, syn, iters):
@@ -452,6 +466,9 @@ def prefill_chunk(torch, C, syn, iters):
                                                               ws=ws_d, out=outh))]
     t = time_ops(torch, ops, iters)
     split = {kn: call_kernel_ms(torch, C, ops[0][1], kn) for kn in ("index_score", "topk")}
+    bf = bf16_score_variant(torch, C, iters, lambda ws_b: C.indexer_topk(
+        qi, qs, w, kc, ks, "fp4", q_pos, 4, k, d_I, ws=ws_b, idx_out=idx, bf16_scores=True),
+        C.indexer_topk_workspace_size(1, Tq, N, H_I, d_I, k, "fp4", bf16_scores=True))
     p = np.arange(L - Tq, L, dtype=np.int64)
     n = np.minimum(N, (p + 1) // 4)
     nh = np.minimum(NH, (p + 1) // 128)
@@ -466,7 +483,8 @@ def prefill_chunk(torch, C, syn, iters):
                                     round(fl_i / (split["index_score"] * 1e-3) / 1e12, 2)),
             "sparse_attn_tflop_s": round(fl_a / (t["sparse_attn"] * 1e-3) / 1e12, 2),
             "dense_attn_tflop_s": round(fl_d / (t["dense_attn"] * 1e-3) / 1e12, 2),
-            "dense_attn_frac_bf16_peak": round(fl_d / (t["dense_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            "dense_attn_frac_bf16_peak": round(fl_d / (t["dense_attn"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "indexer_bf16_scores": bf}
 
 
 # ----------------------------------------------------------------------------- main

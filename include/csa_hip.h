@@ -216,6 +216,31 @@ csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w,
                         void* stream);
 
 /*
+ * indexer_topk_bf16_scores — indexer_topk with bfloat16 index scores
+ * (cf-1.com write-up §4.4: quantising the index scores from FP32 to BF16
+ * halves the selector's score traffic at a small recall cost).
+ * Each score I(p,s) is accumulated in float32 exactly as in indexer_topk,
+ * then rounded once to bfloat16 (round to nearest, ties to even); the
+ * selection runs on the rounded values under the same total order (score
+ * descending, index ascending; -0 equals +0), so entries whose float32
+ * scores differ but round to the same bfloat16 value tie and the lower
+ * index wins. Arguments, layouts, limits and errors are those of
+ * indexer_topk, except:
+ *   score_out  NULL, or bfloat16 bits uint16 [B, Tq, N]: the rounded scores
+ *              (entries >= n(p) are left untouched)
+ *   the workspace is the one indexer_topk_bf16_scores_workspace_size
+ *   returns (smaller than indexer_topk's for long rows).
+ */
+size_t indexer_topk_bf16_scores_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I,
+                                               int32_t d_I, int32_t k, csa_dtype qk_t);
+csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, const float* w,
+                                    const void* k_idx, const void* k_scale, csa_dtype qk_t,
+                                    const int32_t* q_pos, int64_t B, int64_t Tq, int64_t N,
+                                    int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
+                                    int32_t* idx_out, uint16_t* score_out, void* ws,
+                                    size_t ws_bytes, void* stream);
+
+/*
  * sparse_attn_fwd — CSA core attention over the selected compressed entries,
  * the uncompressed window and the sink (cf-1.com write-up §3.1, §3.3;
  * yfxerp.com write-up §3 sliding_window 128, attention_sink).

@@ -38,6 +38,9 @@ SIGNATURES = {
     "indexer_topk_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32, ctypes.c_int]),
     "indexer_topk": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _I32, _I32, _I32,
                                     _I32, _P, _P, _P, _SZ, _P]),
+    "indexer_topk_bf16_scores_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32, ctypes.c_int]),
+    "indexer_topk_bf16_scores": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _I32, _I32,
+                                                _I32, _I32, _P, _P, _P, _SZ, _P]),
     "sparse_attn_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
                                        _I32, _I32, _F, _P, _P, _P, _SZ, _P]),

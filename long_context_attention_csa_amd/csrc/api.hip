@@ -18,10 +18,10 @@ hipError_t launch_csa_append(const void*, const void*, const void*, const void*,
 hipError_t launch_hca_append(const void*, const void*, csa_dtype, int64_t, int, int, const int32_t*, void*, int64_t,
                              void*, csa_dtype, hipStream_t);
 hipError_t launch_quantize_rows(const void*, csa_dtype, int64_t, int, void*, csa_dtype, void*, hipStream_t);
-size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N);
+size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes);
 hipError_t launch_indexer_topk(const void*, const void*, const float*, const void*, const void*, csa_dtype,
-                               const int32_t*, int64_t, int64_t, int64_t, int, int, int, int, int32_t*, float*, void*,
-                               hipStream_t);
+                               const int32_t*, int64_t, int64_t, int64_t, int, int, int, int, int32_t*, void*, bool,
+                               void*, hipStream_t);
 size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max);
 void set_batch_invariant(int on);
 int batch_invariant();
@@ -207,7 +207,43 @@ size_t indexer_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I
                                    csa_dtype qk_t) {
   (void)H_I; (void)d_I; (void)k; (void)qk_t;
   if (B <= 0 || Tq <= 0 || N < 0) return 0;
-  return indexer_ws_bytes(B, Tq, N);
+  return indexer_ws_bytes(B, Tq, N, 4);
+}
+
+size_t indexer_topk_bf16_scores_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I,
+                                               int32_t k, csa_dtype qk_t) {
+  (void)H_I; (void)d_I; (void)k; (void)qk_t;
+  if (B <= 0 || Tq <= 0 || N < 0) return 0;
+  return indexer_ws_bytes(B, Tq, N, 2);
+}
+
+static csa_status indexer_common(const char* fn, const void* q_idx, const void* q_scale, const float* w,
+                                 const void* k_idx, const void* k_scale, csa_dtype qk_t, const int32_t* q_pos,
+                                 int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
+                                 int32_t* idx_out, void* score_out, bool bf16, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  CSA_REQUIRE(is_dtype(qk_t), CSA_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)qk_t);
+  CSA_REQUIRE(B >= 0 && Tq >= 0 && N >= 0 && N < (int64_t(1) << 30) && B * Tq < (int64_t(1) << 31), CSA_ERR_SHAPE,
+              "%s: B=%lld Tq=%lld N=%lld", fn, (long long)B, (long long)Tq, (long long)N);
+  CSA_REQUIRE(H_I >= 1 && H_I <= 64, CSA_ERR_UNSUPPORTED, "%s: H_I %d (1..64)", fn, H_I);
+  CSA_REQUIRE(d_I == 64 || d_I == 128, CSA_ERR_UNSUPPORTED, "%s: d_I %d (64 or 128)", fn, d_I);
+  CSA_REQUIRE(k >= 1 && k <= 2048, CSA_ERR_SHAPE, "%s: k %d (1..2048)", fn, k);
+  CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "%s: ratio %d", fn, ratio);
+  const bool quant = qk_t == CSA_FP8_E4M3 || qk_t == CSA_FP4_E2M1;
+  CSA_REQUIRE(quant || (q_scale == nullptr && k_scale == nullptr), CSA_ERR_SHAPE,
+              "%s: q_scale/k_scale must be NULL for float operands", fn);
+  if (B * Tq == 0) return CSA_OK;
+  CSA_REQUIRE(q_idx && w && q_pos && idx_out, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  CSA_REQUIRE(N == 0 || k_idx, CSA_ERR_NULL, "%s: k_idx is NULL", fn);
+  CSA_REQUIRE(!quant || (q_scale && (N == 0 || k_scale)), CSA_ERR_NULL, "%s: scales required", fn);
+  CSA_REQUIRE(((uintptr_t)q_idx & 15) == 0 && ((uintptr_t)k_idx & 15) == 0 && ((uintptr_t)k_scale & 3) == 0,
+              CSA_ERR_SHAPE, "%s: q_idx and k_idx must be 16-byte aligned, k_scale 4-byte aligned", fn);
+  const size_t need = bf16 ? indexer_topk_bf16_scores_workspace_size(B, Tq, N, H_I, d_I, k, qk_t)
+                           : indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, qk_t);
+  CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  return hip_status(launch_indexer_topk(q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio, k,
+                                        idx_out, score_out, bf16, ws, (hipStream_t)stream),
+                    fn);
 }
 
 csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
@@ -215,27 +251,18 @@ csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w, 
                         int64_t N, int32_t H_I, int32_t d_I, int32_t ratio, int32_t k, int32_t* idx_out,
                         float* score_out, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  CSA_REQUIRE(is_dtype(qk_t), CSA_ERR_UNSUPPORTED, "indexer_topk: unknown dtype %d", (int)qk_t);
-  CSA_REQUIRE(B >= 0 && Tq >= 0 && N >= 0 && N < (int64_t(1) << 30) && B * Tq < (int64_t(1) << 31), CSA_ERR_SHAPE,
-              "indexer_topk: B=%lld Tq=%lld N=%lld", (long long)B, (long long)Tq, (long long)N);
-  CSA_REQUIRE(H_I >= 1 && H_I <= 64, CSA_ERR_UNSUPPORTED, "indexer_topk: H_I %d (1..64)", H_I);
-  CSA_REQUIRE(d_I == 64 || d_I == 128, CSA_ERR_UNSUPPORTED, "indexer_topk: d_I %d (64 or 128)", d_I);
-  CSA_REQUIRE(k >= 1 && k <= 2048, CSA_ERR_SHAPE, "indexer_topk: k %d (1..2048)", k);
-  CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "indexer_topk: ratio %d", ratio);
-  const bool quant = qk_t == CSA_FP8_E4M3 || qk_t == CSA_FP4_E2M1;
-  CSA_REQUIRE(quant || (q_scale == nullptr && k_scale == nullptr), CSA_ERR_SHAPE,
-              "indexer_topk: q_scale/k_scale must be NULL for float operands");
-  if (B * Tq == 0) return CSA_OK;
-  CSA_REQUIRE(q_idx && w && q_pos && idx_out, CSA_ERR_NULL, "indexer_topk: NULL tensor");
-  CSA_REQUIRE(N == 0 || k_idx, CSA_ERR_NULL, "indexer_topk: k_idx is NULL");
-  CSA_REQUIRE(!quant || (q_scale && (N == 0 || k_scale)), CSA_ERR_NULL, "indexer_topk: scales required");
-  CSA_REQUIRE(((uintptr_t)q_idx & 15) == 0 && ((uintptr_t)k_idx & 15) == 0 && ((uintptr_t)k_scale & 3) == 0,
-              CSA_ERR_SHAPE, "indexer_topk: q_idx and k_idx must be 16-byte aligned, k_scale 4-byte aligned");
-  const size_t need = indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, qk_t);
-  CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "indexer_topk: workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(launch_indexer_topk(q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio, k,
-                                        idx_out, score_out, ws, (hipStream_t)stream),
-                    "indexer_topk");
+  return indexer_common("indexer_topk", q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio,
+                        k, idx_out, score_out, false, ws, ws_bytes, stream);
+}
+
+csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
+                                    const void* k_scale, csa_dtype qk_t, const int32_t* q_pos, int64_t B,
+                                    int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
+                                    int32_t* idx_out, uint16_t* score_out, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  g_last_error.clear();
+  return indexer_common("indexer_topk_bf16_scores", q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I,
+                        d_I, ratio, k, idx_out, score_out, true, ws, ws_bytes, stream);
 }
 
 static csa_status check_attn_common(const char* fn, const void* q, const void* kv, const void* x_win,

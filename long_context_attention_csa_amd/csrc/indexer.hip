@@ -49,6 +49,41 @@ constexpr int kMaxK = 2048;
 constexpr int kGroup = 16;                // entries per group maximum
 constexpr int kGroupFactor = 2;           // group path when groups >= 2k
 
+// ------------------------------------------------------------------ score storage
+// Scores are stored as float32, or (the bf16-score variant) as bf16: the
+// float32 score rounded to nearest even once, before anything uses it, so
+// group maxima, stored scores and the selection all see the same value.
+template <typename SC> struct ScoreT;
+template <> struct ScoreT<float> {
+  __device__ __forceinline__ static float round(float v) { return v; }
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct ScoreT<uint16_t> {
+  __device__ __forceinline__ static float round(float v) { return __uint_as_float((uint32_t)f32_to_bf16(v) << 16); }
+  __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
+  __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) {
+    p[i] = (uint16_t)(__float_as_uint(v) >> 16);   // v is already a bf16 value
+  }
+};
+// 8 consecutive scores from a 16-byte aligned address (float: two float4
+// loads, bf16: one).
+template <typename SC>
+__device__ __forceinline__ void load_scores8(const SC* p, float* v) {
+  if constexpr (sizeof(SC) == 4) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ operand loads
 // Per-format A/B operand of one 16x16 MFMA tile, for one lane:
 //   row/col index = lane % 16, K-group g = lane / 16.
@@ -175,12 +210,12 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
 // grid.x: entry chunk (chunk_entries entries each), grid.y: query group
 // (QB consecutive queries of one sequence), 256 threads (4 waves).
 // Group gy covers rows row_lo(gy) .. ; row r writes scores at sbase + (r - srow0) * N.
-template <int FMT, int DI, int HB, int QB, int UB, bool DBUF>
+template <int FMT, int DI, int HB, int QB, int UB, bool DBUF, typename SC>
 __global__ __launch_bounds__(256) void k_index_score(
     const void* __restrict__ q_idx, const void* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k_idx, const void* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
     int64_t Tq, int64_t N, int H_I, int ratio, int64_t group0, int64_t groups_per_batch,
-    int64_t chunk_entries, float* __restrict__ sbase, int64_t srow0, float* __restrict__ gbase, int64_t grow0) {
+    int64_t chunk_entries, SC* __restrict__ sbase, int64_t srow0, float* __restrict__ gbase, int64_t grow0) {
   typedef typename Storage<FMT>::type ST;
   constexpr int RU = row_units<FMT, DI>();
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -280,11 +315,12 @@ __global__ __launch_bounds__(256) void k_index_score(
         }
         part = sum_xor16_32(part);
         if constexpr (FMT == CSA_FP8_E4M3) part *= ks[u];
+        part = ScoreT<SC>::round(part);
         const bool ok = e < nvis[qi];
         // group maximum over the 16 entries of this block (valid entries only)
         const float gm = max_row16(ok ? part : -INFINITY);
         const int64_t r = b * Tq + t0 + qi;
-        if (g == 0 && ok) sbase[(r - srow0) * N + e] = part;
+        if (g == 0 && ok) ScoreT<SC>::store(sbase, (r - srow0) * N + e, part);
         if (lane == 0 && e0 < nvis[qi]) gbase[(r - grow0) * G + e0 / kGroup] = gm;
       }
     }
@@ -368,11 +404,11 @@ __device__ __forceinline__ uint32_t transpose_rows_bytes(uint32_t w, int lane) {
   return __builtin_amdgcn_perm(b[1], b[0], ((lane >> 4) & 1) ? 0x07030501u : 0x06020400u);
 }
 
-template <int FMT, int HB, int NB, int DEPTH>
+template <int FMT, int HB, int NB, int DEPTH, typename SC>
 __global__ __launch_bounds__(256) void k_index_score_dec(
     const void* __restrict__ q_idx, const void* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k_idx, const void* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
-    int64_t Tq, int64_t N, int H_I, int ratio, int64_t row_begin, float* __restrict__ sbase, int64_t srow0,
+    int64_t Tq, int64_t N, int H_I, int ratio, int64_t row_begin, SC* __restrict__ sbase, int64_t srow0,
     float* __restrict__ gbase, int64_t grow0) {
   constexpr int DI = 128;
   constexpr int RB = FMT == CSA_FP4_E2M1 ? DI / 2 : DI;    // bytes per key row
@@ -491,17 +527,18 @@ __global__ __launch_bounds__(256) void k_index_score_dec(
     const float p3 = tile(d, st, std::integral_constant<int, 3>{});
     float s = reduce_scatter4(p0, p1, p2, p3);
     if constexpr (FMT == CSA_FP8_E4M3) s *= d.sc;
+    s = ScoreT<SC>::round(s);
     const bool ok = batch_base(i) + lane < nvis;
     out_s[i] = s;
     out_g[i] = max_row16(ok ? s : -INFINITY);
   }
   const int64_t G = (N + kGroup - 1) / kGroup;
-  float* srow = sbase + (r - srow0) * N;
+  SC* srow = sbase + (r - srow0) * N;
   float* grow = gbase + (r - grow0) * G;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int64_t e0 = batch_base(i);
-    if (e0 + lane < nvis) srow[e0 + lane] = out_s[i];
+    if (e0 + lane < nvis) ScoreT<SC>::store(srow, e0 + lane, out_s[i]);
     if (col == 0 && e0 + 16 * g < nvis) grow[(e0 + 16 * g) / kGroup] = out_g[i];
   }
 }
@@ -542,12 +579,12 @@ template <> struct PfCfg<CSA_FP4_E2M1> {
   static constexpr int LOADS = 2;
 };
 
-template <int FMT, int HB>
+template <int FMT, int HB, typename SC>
 __global__ __launch_bounds__(256) void k_index_score_pf(
     const uint8_t* __restrict__ q_idx, const void* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ k_idx, const void* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
     int64_t Tq, int64_t N, int H_I, int ratio, int64_t group0, int64_t groups_per_batch,
-    int64_t chunk_entries, float* __restrict__ sbase, int64_t srow0, float* __restrict__ gbase, int64_t grow0) {
+    int64_t chunk_entries, SC* __restrict__ sbase, int64_t srow0, float* __restrict__ gbase, int64_t grow0) {
   constexpr bool F4 = FMT == CSA_FP4_E2M1;
   constexpr int RB = PfCfg<FMT>::RB, LOADS = PfCfg<FMT>::LOADS;
   constexpr int SB = kPfStage * RB;   // key bytes per stage
@@ -651,13 +688,13 @@ __global__ __launch_bounds__(256) void k_index_score_pf(
                           : (uint32_t)col * RB + 16u * ((2u * g) ^ sw);
   const uint32_t ob1 = (uint32_t)col * RB + 16u * ((2u * g + 1u) ^ sw);
   const int64_t G = (N + kGroup - 1) / kGroup;
-  float* srow = sbase + (r - srow0) * N;
+  SC* srow = sbase + (r - srow0) * N;
   float* grow = gbase + (r - grow0) * G;
   float prev_s = 0.f, prev_g = 0.f;
   int64_t prev_e = -1;
   auto store_prev = [&]() {
     if (live_q && prev_e >= 0) {
-      if (prev_e + lane < nvw) srow[prev_e + lane] = prev_s;
+      if (prev_e + lane < nvw) ScoreT<SC>::store(srow, prev_e + lane, prev_s);
       if (col == 0 && prev_e + 16 * g < nvw) grow[(prev_e + 16 * g) / kGroup] = prev_g;
     }
   };
@@ -704,6 +741,7 @@ __global__ __launch_bounds__(256) void k_index_score_pf(
       }
       float sc = reduce_scatter4(part[0], part[1], part[2], part[3]);
       if constexpr (!F4) sc *= __uint_as_float(sring[st % kPfDepth][lane]);
+      sc = ScoreT<SC>::round(sc);
       const int64_t e0 = e_begin + (int64_t)kPfStage * st;
       prev_s = sc;
       prev_g = max_row16(e0 + lane < nvw ? sc : -INFINITY);
@@ -947,19 +985,21 @@ __device__ void take_top_candidates(TopkSmem& sm, int ncand) {
 
 // Full-row path: 13-bit histogram of all n scores, take the higher buckets,
 // resolve the boundary bucket exactly. Leaves k indices in sm.sel.
-__device__ void select_full_row(TopkSmem& sm, const float* __restrict__ srow, int64_t n, int k) {
+template <typename SC>
+__device__ void select_full_row(TopkSmem& sm, const SC* __restrict__ srow, int64_t n, int k) {
   const int tid = threadIdx.x;
   for (int i = tid; i < kHistBins; i += kTopkThreads) sm.hist[i] = 0;
   if (tid == 0) { sm.nsel = 0; sm.ncand = 0; }
   __syncthreads();
 #pragma unroll 8
-  for (int64_t i = tid; i < n; i += kTopkThreads) atomicAdd(&sm.hist[order_key(srow[i]) >> (32 - kHistBits)], 1u);
+  for (int64_t i = tid; i < n; i += kTopkThreads)
+    atomicAdd(&sm.hist[order_key(ScoreT<SC>::load(srow, i)) >> (32 - kHistBits)], 1u);
   __syncthreads();
   find_bucket(sm, (uint32_t)k);
   const uint32_t d1 = sm.bin;
 #pragma unroll 8
   for (int64_t i = tid; i < n; i += kTopkThreads) {
-    const uint32_t key = order_key(srow[i]);
+    const uint32_t key = order_key(ScoreT<SC>::load(srow, i));
     const uint32_t d = key >> (32 - kHistBits);
     if (d > d1) {
       sm.sel[atomicAdd(&sm.nsel, 1)] = (int)i;
@@ -982,11 +1022,11 @@ __device__ void select_full_row(TopkSmem& sm, const float* __restrict__ srow, in
     // Bucket larger than the LDS list (heavy ties): select straight from the row.
     radix_threshold(sm, n, [&](int64_t i, bool& ok) {
       ok = true;
-      return composite(order_key(srow[i]), i);
+      return composite(order_key(ScoreT<SC>::load(srow, i)), i);
     });
     const unsigned long long th = sm.thresh;
     for (int64_t i = tid; i < n; i += kTopkThreads) {
-      const uint32_t key = order_key(srow[i]);
+      const uint32_t key = order_key(ScoreT<SC>::load(srow, i));
       if ((key >> (32 - kHistBits)) == d1 && composite(key, i) >= th) sm.sel[atomicAdd(&sm.nsel, 1)] = (int)i;
     }
     __syncthreads();
@@ -1071,7 +1111,8 @@ __device__ __forceinline__ float pick16(const float (&a)[16], int j) {
   return __uint_as_float(r);
 }
 
-__device__ bool select_by_groups(TopkSmem& sm, const float* __restrict__ srow, const float* __restrict__ grow,
+template <typename SC>
+__device__ bool select_by_groups(TopkSmem& sm, const SC* __restrict__ srow, const float* __restrict__ grow,
                                  int64_t n, int64_t m, int k, int32_t* __restrict__ out) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (m > (int64_t)kGPT * kTopkThreads) return false;
@@ -1160,23 +1201,17 @@ __device__ bool select_by_groups(TopkSmem& sm, const float* __restrict__ srow, c
     const int eb = ga + 1 < gb ? glist[ga + 1] * kGroup : ni;
     if (svec && ea + kGroup <= ni) {
 #pragma unroll
-      for (int j = 0; j < kGroup; j += 4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(srow + ea + j);
-        va[j] = t4.x; va[j + 1] = t4.y; va[j + 2] = t4.z; va[j + 3] = t4.w;
-      }
+      for (int j = 0; j < kGroup; j += 8) load_scores8(srow + ea + j, va + j);
     } else {
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) va[j] = ea + j < ni ? srow[ea + j] : -INFINITY;
+      for (int j = 0; j < kGroup; ++j) va[j] = ea + j < ni ? ScoreT<SC>::load(srow, ea + j) : -INFINITY;
     }
     if (svec && eb + kGroup <= ni) {
 #pragma unroll
-      for (int j = 0; j < kGroup; j += 4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(srow + eb + j);
-        vb[j] = t4.x; vb[j + 1] = t4.y; vb[j + 2] = t4.z; vb[j + 3] = t4.w;
-      }
+      for (int j = 0; j < kGroup; j += 8) load_scores8(srow + eb + j, vb + j);
     } else {
 #pragma unroll
-      for (int j = 0; j < kGroup; ++j) vb[j] = eb + j < ni ? srow[eb + j] : -INFINITY;
+      for (int j = 0; j < kGroup; ++j) vb[j] = eb + j < ni ? ScoreT<SC>::load(srow, eb + j) : -INFINITY;
     }
     uint32_t ma = 0, mb = 0;
 #pragma unroll
@@ -1258,7 +1293,8 @@ __device__ bool select_by_groups(TopkSmem& sm, const float* __restrict__ srow, c
 
 // One block per row of the current pass. Row r's scores live at
 // sbase + (r - srow0) * N and its group maxima at gbase + (r - grow0) * G.
-__global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float* __restrict__ sbase, int64_t srow0,
+template <typename SC>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_select(const SC* __restrict__ sbase, int64_t srow0,
                                                               const float* __restrict__ gbase, int64_t grow0,
                                                               int64_t row0, const int32_t* __restrict__ q_pos,
                                                               int64_t N, int ratio, int k, int32_t* __restrict__ idx_out) {
@@ -1272,7 +1308,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const float* __res
     return;
   }
   const int64_t G = (N + kGroup - 1) / kGroup;
-  const float* srow = sbase + (r - srow0) * N;
+  const SC* srow = sbase + (r - srow0) * N;
   const float* grow = gbase + (r - grow0) * G;
   const int64_t m = (n + kGroup - 1) / kGroup;
   if (m >= (int64_t)kGroupFactor * k && select_by_groups(sm, srow, grow, n, m, k, out)) return;
@@ -1411,7 +1447,22 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
   return v;
 }
 
-__global__ __launch_bounds__(kSmallThreads) void k_topk_small(const float* __restrict__ sbase, int64_t srow0,
+// Selection key of entry i (< kSmallN) with score v. float32 scores: the
+// order key itself (ties are resolved later by index). bf16 scores carry only
+// the high 16 bits of the order key, so the low 16 bits take 16383 - i: every
+// key is distinct and orders entries by (score descending, index ascending),
+// and equal bf16 scores, which are common, no longer pile into one histogram
+// bin (same-address LDS atomics serialise).
+template <typename SC>
+__device__ __forceinline__ uint32_t small_key(float v, int i) {
+  if constexpr (sizeof(SC) == 2)
+    return (order_key(v) & 0xffff0000u) | (uint32_t)(kSmallN - 1 - i);
+  else
+    return order_key(v);
+}
+
+template <typename SC>
+__global__ __launch_bounds__(kSmallThreads) void k_topk_small(const SC* __restrict__ sbase, int64_t srow0,
                                                               int64_t row0, const int32_t* __restrict__ q_pos,
                                                               int64_t N, int ratio, int k,
                                                               int32_t* __restrict__ idx_out) {
@@ -1424,16 +1475,18 @@ __global__ __launch_bounds__(kSmallThreads) void k_topk_small(const float* __res
     for (int i = tid; i < k; i += kSmallThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const float* srow = sbase + (r - srow0) * N;
+  const SC* srow = sbase + (r - srow0) * N;
   const int base = tid * kSmallPer;
   const int nv = n - base < 0 ? 0 : (n - base > kSmallPer ? kSmallPer : n - base);
   uint32_t key[kSmallPer];
   uint32_t tmax = 0u, tinv = 0u;   // largest key and largest ~key (= ~smallest key) of the thread
   if (nv == kSmallPer && (reinterpret_cast<uintptr_t>(srow + base) & 15) == 0) {
 #pragma unroll
-    for (int j = 0; j < kSmallPer; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(srow + base + j);
-      key[j] = order_key(v.x); key[j + 1] = order_key(v.y); key[j + 2] = order_key(v.z); key[j + 3] = order_key(v.w);
+    for (int j = 0; j < kSmallPer; j += 8) {
+      float v[8];
+      load_scores8(srow + base + j, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) key[j + i] = small_key<SC>(v[i], base + j + i);
     }
 #pragma unroll
     for (int j = 0; j < kSmallPer; ++j) { tmax = max(tmax, key[j]); tinv = max(tinv, ~key[j]); }
@@ -1441,7 +1494,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_topk_small(const float* __res
     // entries past the row's end repeat its last entry: the range is unchanged
     // and every later pass skips them (j >= nv)
 #pragma unroll
-    for (int j = 0; j < kSmallPer; ++j) key[j] = order_key(srow[base + min(j, nv - 1)]);
+    for (int j = 0; j < kSmallPer; ++j) {
+      const int i = base + min(j, nv - 1);
+      key[j] = small_key<SC>(ScoreT<SC>::load(srow, i), i);
+    }
 #pragma unroll
     for (int j = 0; j < kSmallPer; ++j) { tmax = max(tmax, key[j]); tinv = max(tinv, ~key[j]); }
   } else {
@@ -1606,14 +1662,14 @@ struct IndexPlan {
   int64_t groups_per_batch, groups, chunk_entries, groups_per_pass, max_rows_per_pass;
 };
 
-static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N) {
+static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N, int sbytes) {
   IndexPlan p;
   p.QB = Tq >= 4 ? 4 : 1;
   p.groups_per_batch = cdiv(Tq, p.QB);
   p.groups = B * p.groups_per_batch;
   // Score buffer budget per pass: 1 GiB.
   const int64_t budget = (int64_t)1 << 30;
-  const int64_t row_bytes = (N > 0 ? N : 1) * 4 + ((N + kGroup - 1) / kGroup) * 4;
+  const int64_t row_bytes = (N > 0 ? N : 1) * sbytes + ((N + kGroup - 1) / kGroup) * 4;
   int64_t gpp = budget / (row_bytes * p.QB);
   if (gpp < 1) gpp = 1;
   if (gpp > 65535) gpp = 65535;
@@ -1634,11 +1690,15 @@ static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N) {
 
 static int64_t groups_of(int64_t N) { return (N + kGroup - 1) / kGroup; }
 
-// Workspace: per pass, the scores [rows, N] and the group maxima [rows, G].
-size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N) {
-  const IndexPlan p = make_plan(B, Tq, N);
+// Workspace: per pass, the scores [rows, N] (sbytes each: 4 for float32, 2 for
+// bf16) and, from the next 256-byte boundary, the group maxima [rows, G].
+static size_t score_area(const IndexPlan& p, int64_t N, int sbytes) {
+  return ((size_t)p.max_rows_per_pass * (size_t)N * (size_t)sbytes + 255) / 256 * 256;
+}
+size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes) {
+  const IndexPlan p = make_plan(B, Tq, N, sbytes);
   const size_t rows = (size_t)p.max_rows_per_pass;
-  return rows * (size_t)N * 4 + rows * (size_t)groups_of(N) * 4 + 256;
+  return score_area(p, N, sbytes) + rows * (size_t)groups_of(N) * 4 + 256;
 }
 
 // Batch shape of the key stream per format and queries per block (from
@@ -1654,78 +1714,81 @@ template <int FMT, int QB> struct ScoreCfg {
 // (sweep at the 1M-context fp4 and 262k-context fp8 decode shapes).
 constexpr int kDecNB = 4, kDecDepth = 2;
 
-template <int FMT>
+template <int FMT, typename SC>
 static void launch_score_dec(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
                              const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
-                             int ratio, int64_t r0, float* sb, int64_t sr0, float* gb, int64_t gr0) {
+                             int ratio, int64_t r0, SC* sb, int64_t sr0, float* gb, int64_t gr0) {
   switch (HB) {
-    case 1: k_index_score_dec<FMT, 1, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
-    case 2: k_index_score_dec<FMT, 2, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
-    case 3: k_index_score_dec<FMT, 3, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
-    default: k_index_score_dec<FMT, 4, kDecNB, kDecDepth><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+    case 1: k_index_score_dec<FMT, 1, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+    case 2: k_index_score_dec<FMT, 2, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+    case 3: k_index_score_dec<FMT, 3, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
+    default: k_index_score_dec<FMT, 4, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
   }
 }
 
-template <int FMT, int DI, int HB, int QB>
+template <int FMT, int DI, int HB, int QB, typename SC>
 static void launch_score(dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w, const void* kk,
                          const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I, int ratio, int64_t g0,
-                         int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
-  k_index_score<FMT, DI, HB, QB, ScoreCfg<FMT, QB>::UB, ScoreCfg<FMT, QB>::DBUF><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+                         int64_t gpb, int64_t ce, SC* sb, int64_t sr0, float* gb, int64_t gr0) {
+  k_index_score<FMT, DI, HB, QB, ScoreCfg<FMT, QB>::UB, ScoreCfg<FMT, QB>::DBUF, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
 }
 
-template <int FMT, int DI, int QB>
+template <int FMT, int DI, int QB, typename SC>
 static void dispatch_hb(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
                         const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
-                        int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
+                        int ratio, int64_t g0, int64_t gpb, int64_t ce, SC* sb, int64_t sr0, float* gb, int64_t gr0) {
   switch (HB) {
-    case 1: launch_score<FMT, DI, 1, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    case 2: launch_score<FMT, DI, 2, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    case 3: launch_score<FMT, DI, 3, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    default: launch_score<FMT, DI, 4, QB>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 1: launch_score<FMT, DI, 1, QB, SC>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 2: launch_score<FMT, DI, 2, QB, SC>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 3: launch_score<FMT, DI, 3, QB, SC>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    default: launch_score<FMT, DI, 4, QB, SC>(grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
   }
 }
 
-template <int FMT>
+template <int FMT, typename SC>
 static void launch_score_pf(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
                             const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
-                            int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb,
+                            int ratio, int64_t g0, int64_t gpb, int64_t ce, SC* sb, int64_t sr0, float* gb,
                             int64_t gr0) {
   const auto* q8 = static_cast<const uint8_t*>(q);
   const auto* k8 = static_cast<const uint8_t*>(kk);
   switch (HB) {
-    case 1: k_index_score_pf<FMT, 1><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    case 2: k_index_score_pf<FMT, 2><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    case 3: k_index_score_pf<FMT, 3><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
-    default: k_index_score_pf<FMT, 4><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 1: k_index_score_pf<FMT, 1, SC><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 2: k_index_score_pf<FMT, 2, SC><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    case 3: k_index_score_pf<FMT, 3, SC><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
+    default: k_index_score_pf<FMT, 4, SC><<<grid, 256, 0, s>>>(q8, qs, w, k8, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0); break;
   }
 }
 
-template <int FMT>
+template <int FMT, typename SC>
 static void dispatch_fmt(int DI, int QB, int HB, dim3 grid, hipStream_t s, const void* q, const void* qs,
                          const float* w, const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N,
-                         int H_I, int ratio, int64_t g0, int64_t gpb, int64_t ce, float* sb, int64_t sr0, float* gb, int64_t gr0) {
+                         int H_I, int ratio, int64_t g0, int64_t gpb, int64_t ce, SC* sb, int64_t sr0, float* gb, int64_t gr0) {
   if constexpr (FMT == CSA_FP8_E4M3 || FMT == CSA_FP4_E2M1) {
     if (DI == 128 && QB == 4) {
-      launch_score_pf<FMT>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+      launch_score_pf<FMT, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
       return;
     }
   }
   if (DI == 128) {
-    if (QB == 4) dispatch_hb<FMT, 128, 4>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
-    else dispatch_hb<FMT, 128, 1>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+    if (QB == 4) dispatch_hb<FMT, 128, 4, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+    else dispatch_hb<FMT, 128, 1, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
   } else {
-    if (QB == 4) dispatch_hb<FMT, 64, 4>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
-    else dispatch_hb<FMT, 64, 1>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+    if (QB == 4) dispatch_hb<FMT, 64, 4, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
+    else dispatch_hb<FMT, 64, 1, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, g0, gpb, ce, sb, sr0, gb, gr0);
   }
 }
 
-hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
-                               const void* k_scale, csa_dtype fmt, const int32_t* q_pos, int64_t B, int64_t Tq,
-                               int64_t N, int H_I, int d_I, int ratio, int k, int32_t* idx_out, float* score_out,
-                               void* ws, hipStream_t s) {
-  if (B * Tq == 0) return hipSuccess;
-  const IndexPlan p = make_plan(B, Tq, N);
+template <typename SC>
+static hipError_t run_indexer(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
+                              const void* k_scale, csa_dtype fmt, const int32_t* q_pos, int64_t B, int64_t Tq,
+                              int64_t N, int H_I, int d_I, int ratio, int k, int32_t* idx_out, SC* score_out,
+                              void* ws, hipStream_t s) {
+  constexpr int SB = (int)sizeof(SC);
+  const IndexPlan p = make_plan(B, Tq, N, SB);
   const int HB = (H_I + 15) / 16;
+  // group maxima follow the pass's score rows in the workspace
+  float* gb = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + score_area(p, N, SB));
   for (int64_t g0 = 0; g0 < p.groups; g0 += p.groups_per_pass) {
     const int64_t g1 = (g0 + p.groups_per_pass) < p.groups ? (g0 + p.groups_per_pass) : p.groups;
     const int64_t rlo = (g0 / p.groups_per_batch) * Tq + (g0 % p.groups_per_batch) * p.QB;
@@ -1733,11 +1796,8 @@ hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const flo
     int64_t rhi = (glast / p.groups_per_batch) * Tq + (glast % p.groups_per_batch) * p.QB + p.QB;
     const int64_t bend = (glast / p.groups_per_batch + 1) * Tq;
     if (rhi > bend) rhi = bend;
-    float* sb = score_out ? score_out : reinterpret_cast<float*>(ws);
+    SC* sb = score_out ? score_out : reinterpret_cast<SC*>(ws);
     const int64_t sr0 = score_out ? 0 : rlo;
-    // group maxima live after the pass's score rows in the workspace (rows rlo..rhi)
-    // group maxima follow the pass's score rows in the workspace
-    float* gb = reinterpret_cast<float*>(ws) + (size_t)p.max_rows_per_pass * (size_t)N;
     const int64_t gr0 = rlo;
     const bool dec = p.QB == 1 && d_I == 128 && (fmt == CSA_FP8_E4M3 || fmt == CSA_FP4_E2M1);
     if (N > 0 && dec) {
@@ -1745,9 +1805,9 @@ hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const flo
       const dim3 grid((unsigned)cdiv(N, (int64_t)256 * kDecNB), (unsigned)(g1 - g0));
       timer_before(CSA_KID_INDEX_SCORE, s);
       if (fmt == CSA_FP8_E4M3)
-        launch_score_dec<CSA_FP8_E4M3>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
+        launch_score_dec<CSA_FP8_E4M3, SC>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
       else
-        launch_score_dec<CSA_FP4_E2M1>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
+        launch_score_dec<CSA_FP4_E2M1, SC>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
       hipError_t e = hipGetLastError();
       timer_after(CSA_KID_INDEX_SCORE, s);
       if (e != hipSuccess) return e;
@@ -1755,10 +1815,10 @@ hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const flo
       const dim3 grid((unsigned)cdiv(N, p.chunk_entries), (unsigned)(g1 - g0));
       timer_before(CSA_KID_INDEX_SCORE, s);
       switch (fmt) {
-        case CSA_FP8_E4M3: dispatch_fmt<CSA_FP8_E4M3>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
-        case CSA_FP4_E2M1: dispatch_fmt<CSA_FP4_E2M1>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
-        case CSA_BF16: dispatch_fmt<CSA_BF16>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
-        default: dispatch_fmt<CSA_F32>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
+        case CSA_FP8_E4M3: dispatch_fmt<CSA_FP8_E4M3, SC>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
+        case CSA_FP4_E2M1: dispatch_fmt<CSA_FP4_E2M1, SC>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
+        case CSA_BF16: dispatch_fmt<CSA_BF16, SC>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
+        default: dispatch_fmt<CSA_F32, SC>(d_I, p.QB, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, g0, p.groups_per_batch, p.chunk_entries, sb, sr0, gb, gr0); break;
       }
       hipError_t e = hipGetLastError();
       timer_after(CSA_KID_INDEX_SCORE, s);
@@ -1766,15 +1826,27 @@ hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const flo
     }
     timer_before(CSA_KID_TOPK, s);
     if (N <= kSmallN)   // every row is short: one 256-thread block per row
-      k_topk_small<<<dim3((unsigned)(rhi - rlo)), kSmallThreads, 0, s>>>(sb, sr0, rlo, q_pos, N, ratio, k, idx_out);
+      k_topk_small<SC><<<dim3((unsigned)(rhi - rlo)), kSmallThreads, 0, s>>>(sb, sr0, rlo, q_pos, N, ratio, k, idx_out);
     else
-      k_topk_select<<<dim3((unsigned)(rhi - rlo)), kTopkThreads, 0, s>>>(sb, sr0, gb, gr0, rlo, q_pos, N, ratio, k,
-                                                                        idx_out);
+      k_topk_select<SC><<<dim3((unsigned)(rhi - rlo)), kTopkThreads, 0, s>>>(sb, sr0, gb, gr0, rlo, q_pos, N, ratio,
+                                                                            k, idx_out);
     hipError_t e = hipGetLastError();
     timer_after(CSA_KID_TOPK, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
+                               const void* k_scale, csa_dtype fmt, const int32_t* q_pos, int64_t B, int64_t Tq,
+                               int64_t N, int H_I, int d_I, int ratio, int k, int32_t* idx_out, void* score_out,
+                               bool bf16_scores, void* ws, hipStream_t s) {
+  if (B * Tq == 0) return hipSuccess;
+  if (bf16_scores)
+    return run_indexer<uint16_t>(q_idx, q_scale, w, k_idx, k_scale, fmt, q_pos, B, Tq, N, H_I, d_I, ratio, k,
+                                 idx_out, static_cast<uint16_t*>(score_out), ws, s);
+  return run_indexer<float>(q_idx, q_scale, w, k_idx, k_scale, fmt, q_pos, B, Tq, N, H_I, d_I, ratio, k, idx_out,
+                            static_cast<float*>(score_out), ws, s);
 }
 
 }  // namespace csa

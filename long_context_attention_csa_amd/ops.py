@@ -149,15 +149,17 @@ def batch_invariant() -> bool:
     return bool(lib().csa_get_batch_invariant())
 
 
-def indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt: str) -> int:
-    return int(lib().indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, FMT[fmt]))
+def indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt: str, bf16_scores: bool = False) -> int:
+    fn = lib().indexer_topk_bf16_scores_workspace_size if bf16_scores else lib().indexer_topk_workspace_size
+    return int(fn(B, Tq, N, H_I, d_I, k, FMT[fmt]))
 
 
 def indexer_topk(q_idx, q_scale, w, k_idx, k_scale, fmt: str, q_pos, ratio: int, k: int, d_I: int,
-                 want_scores: bool = False, ws=None, idx_out=None):
+                 want_scores: bool = False, ws=None, idx_out=None, bf16_scores: bool = False):
     """Indexer scores and top-k. q_idx [B, Tq, H_I, d_I(/2 for fp4)], w [B, Tq, H_I] float32,
     k_idx [B, N, d_I(/2)], q_pos int32 [B, Tq]. Returns idx int32 [B, Tq, k]
-    (and the float32 scores [B, Tq, N] when want_scores)."""
+    (and the scores [B, Tq, N] when want_scores: float32, or bfloat16 when
+    bf16_scores, in which case selection also runs on the bfloat16-rounded scores)."""
     _contig(q_idx, q_scale, w, k_idx, k_scale, q_pos)
     f = FMT[fmt]
     B, Tq, H_I = q_idx.shape[:3]
@@ -165,11 +167,13 @@ def indexer_topk(q_idx, q_scale, w, k_idx, k_scale, fmt: str, q_pos, ratio: int,
     dev = q_idx.device
     if idx_out is None:
         idx_out = torch.empty(B, Tq, k, dtype=torch.int32, device=dev)
-    scores = torch.empty(B, Tq, N, dtype=torch.float32, device=dev) if want_scores else None
-    ws, nbytes = _workspace(indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt), dev, ws)
-    check("indexer_topk", lib().indexer_topk(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), f,
-                                             _ptr(q_pos), B, Tq, N, H_I, d_I, ratio, k, _ptr(idx_out), _ptr(scores),
-                                             _ptr(ws), nbytes, _stream()))
+    sdt = torch.bfloat16 if bf16_scores else torch.float32
+    scores = torch.empty(B, Tq, N, dtype=sdt, device=dev) if want_scores else None
+    ws, nbytes = _workspace(indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt, bf16_scores), dev, ws)
+    name = "indexer_topk_bf16_scores" if bf16_scores else "indexer_topk"
+    check(name, getattr(lib(), name)(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale), f,
+                                     _ptr(q_pos), B, Tq, N, H_I, d_I, ratio, k, _ptr(idx_out), _ptr(scores),
+                                     _ptr(ws), nbytes, _stream()))
     return (idx_out, scores) if want_scores else idx_out
 
 

@@ -116,6 +116,7 @@ def hca_compress(c, z, ratio: int = 128) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127  # largest finite bfloat16
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -308,6 +309,42 @@ def topk_select(scores, n_vis, k: int) -> np.ndarray:
         order = np.lexsort((np.arange(n), -s))   # primary: -score, secondary: index
         out[t] = np.sort(order[:k])
     return out
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value, ties to even; returns float64.
+
+    bfloat16 keeps float32's 8-bit exponent and 8 significant bits (7 stored),
+    so a normal value with exponent e sits on a grid of step 2**(e-7); below
+    2**-126 the grid step is fixed at 2**-133 (subnormals). NaN and infinities
+    pass through unchanged.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    fin = np.isfinite(x)
+    a = np.where(fin, np.abs(x), 0.0)
+    safe = np.where(a > 0, a, 1.0)
+    e = np.floor(np.log2(safe)).astype(np.int64)
+    # guard log2 rounding at exact powers of two
+    e = np.where(np.exp2(e.astype(np.float64)) > safe, e - 1, e)
+    e = np.where(np.exp2((e + 1).astype(np.float64)) <= safe, e + 1, e)
+    e = np.maximum(e, -126)
+    step = np.exp2((e - 7).astype(np.float64))
+    r = _round_half_even(a / step) * step
+    if (r > BF16_MAX).any():
+        raise ValueError("bf16_round overflow")
+    return np.where(fin & (a > 0), np.copysign(r, x), x)
+
+
+def topk_select_bf16(scores, n_vis, k: int) -> np.ndarray:
+    """Top-k selection on bfloat16 index scores.
+
+    [cf-1 §4.4]: the index scores are quantised from FP32 to BF16 before the
+    selector, which halves its score traffic at a small recall cost. Reading:
+    each score is rounded once (nearest, ties to even) and the selection of
+    ``topk_select`` runs on the rounded values, so scores that round to the
+    same value tie and the lower index wins.
+    """
+    return topk_select(bf16_round(scores), n_vis, k)
 
 
 # ---------------------------------------------------------------------------

@@ -80,6 +80,36 @@ def test_indexer_validation():
     assert call(args(B=0)) == OK
 
 
+def test_indexer_bf16_scores_validation():
+    """The bfloat16-score entry point validates like indexer_topk and stores two
+    bytes per score instead of four."""
+    lib = _lib.lib()
+    args = lambda **kw: dict(dict(q=P, qs=P, w=P, k=P, ks=P, fmt=2, pos=P, B=1, Tq=1, N=64, H=64, d=128, ratio=4,
+                                  kk=16, out=P, so=None, ws=P, wsb=1 << 40), **kw)
+    call = lambda a: lib.indexer_topk_bf16_scores(a["q"], a["qs"], a["w"], a["k"], a["ks"], a["fmt"], a["pos"],
+                                                  a["B"], a["Tq"], a["N"], a["H"], a["d"], a["ratio"], a["kk"],
+                                                  a["out"], a["so"], a["ws"], a["wsb"], None)
+    assert call(args(kk=0)) == SHAPE
+    assert call(args(H=65)) == UNSUP
+    assert call(args(qs=None)) == NULL
+    assert call(args(fmt=7)) == UNSUP
+    assert call(args(ws=None)) == WS
+    need = lib.indexer_topk_bf16_scores_workspace_size(1, 1, 64, 64, 128, 16, 2)
+    assert need > 0 and call(args(wsb=need - 1)) == WS
+    assert call(args(B=0)) == OK
+    assert lib.indexer_topk_bf16_scores_workspace_size(0, 1, 64, 64, 128, 16, 2) == 0
+    # rows that fit one pass of either variant: half the score bytes
+    small = (1, 64, 1 << 16, 64, 128, 512, 2)
+    f32 = lib.indexer_topk_workspace_size(*small)
+    b16 = lib.indexer_topk_bf16_scores_workspace_size(*small)
+    assert 0 < b16 < f32 and f32 - b16 == 64 * (1 << 16) * 2
+    # a pass's score buffer is capped (1 GiB): the bf16 variant fits twice the rows in about the same space
+    big = (1, 8192, 1 << 18, 64, 128, 1024, 2)
+    assert abs(lib.indexer_topk_bf16_scores_workspace_size(*big) - lib.indexer_topk_workspace_size(*big)) < 1 << 24
+    assert call(args(d=96)) == UNSUP
+    assert lib.csa_last_error().startswith(b"indexer_topk_bf16_scores:")
+
+
 def test_attention_validation():
     lib = _lib.lib()
     f = lib.sparse_attn_fwd

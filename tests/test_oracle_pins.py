@@ -293,6 +293,77 @@ def test_topk_signed_zero_is_a_tie():
     assert list(O.topk_select(s, [4], 2)[0]) == [0, 1]
 
 
+def test_bf16_round_matches_torch_rne():
+    """bfloat16 rounding against torch's float32 -> bfloat16 conversion (round to
+    nearest even), on random values, every exact midpoint of two neighbouring
+    bfloat16 values over several binades, and subnormals."""
+    g = np.random.default_rng(17)
+    v = np.concatenate([
+        g.standard_normal(200000) * 1e3, g.uniform(-1, 1, 100000),
+        g.standard_normal(50000) * 1e-39, g.standard_normal(50000) * 1e30,
+    ]).astype(np.float32)
+    bits = np.concatenate([np.arange(0x3F00, 0x4400), np.arange(0x0000, 0x0100), np.arange(0x7E00, 0x7F7F)])
+    vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, -mids, vals.astype(np.float32), np.float32([0.0, -0.0, np.inf, -np.inf])])
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(v)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    assert np.isnan(O.bf16_round(np.nan))
+
+
+def test_bf16_round_closed_forms():
+    # 8 significant bits: grid step 2^-7 in [1, 2), 2 in [256, 512)
+    assert O.bf16_round(1 + 2.0 ** -8) == 1.0                  # tie -> even (mantissa 0)
+    assert O.bf16_round(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6    # tie -> even (mantissa 2)
+    assert O.bf16_round(257.0) == 256.0 and O.bf16_round(259.0) == 260.0
+    assert O.bf16_round(-258.9) == -258.0
+    assert O.bf16_round(2.0 ** -133) == 2.0 ** -133 and O.bf16_round(2.0 ** -135) == 0.0
+
+
+def test_topk_bf16_merges_near_ties():
+    """[cf-1 §4.4] selection on BF16 scores: scores that round to the same
+    bfloat16 value tie, and the lower index wins."""
+    s = np.array([[256.0, 257.0, 100.0]])
+    assert list(O.topk_select(s, [3], 1)[0]) == [1]
+    assert list(O.topk_select_bf16(s, [3], 1)[0]) == [0]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_topk_bf16_brute_force(seed):
+    g = np.random.default_rng(100 + seed)
+    n_rows, N, k = 5, 48, 9
+    scores = g.integers(250, 262, size=(n_rows, N)).astype(np.float64) + g.uniform(0, 1, (n_rows, N))
+    n_vis = np.array([0, 5, 9, 30, 48])
+    rounded = torch.from_numpy(scores.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.topk_select_bf16(scores.astype(np.float32), n_vis, k)
+    for t in range(n_rows):
+        want = _topk_brute(rounded[t], n_vis[t], k)
+        assert list(got[t, :len(want)]) == want
+        assert np.all(got[t, len(want):] == -1)
+
+
+def test_bf16_selection_recall_on_synthetic_prefill():
+    """[cf-1 §4.4] BF16 index scores keep almost all of the FP32 selection
+    (the pages report 99.7% KV recall). On this synthetic workload the
+    recall of the BF16 selection against the exact one stays above 99%."""
+    T, H_I, d_I, k = 2048, 16, 64, 128
+    inp = syn.csa_prefill(3, T, 4, H_I, d_I, bf16=False)
+    k_i = syn.normal(77, (T // 4, d_I))
+    pos = np.arange(T)
+    sc = O.indexer_scores(inp["q_i"], inp["w"], k_i, pos, 4)
+    n_vis = O.visible_entries(pos, 4, T // 4)
+    a = O.topk_select(sc, n_vis, k)
+    b = O.topk_select_bf16(sc, n_vis, k)
+    hit = tot = 0
+    for t in range(T):
+        sa = set(a[t][a[t] >= 0].tolist())
+        hit += len(sa & set(b[t][b[t] >= 0].tolist()))
+        tot += len(sa)
+    assert hit / tot > 0.99
+
+
 # ---------------------------------------------------------------- attention
 
 def test_attention_ones_values_closed_form():
@@ -426,3 +497,4 @@ def test_layer_brute_force_T16(seed):
             ii = got["idx"][t]
             sel[t, ii[ii >= 0]] = True
         assert np.array_equal(sel, sel_ref)
+
