@@ -436,6 +436,89 @@ def dense_attn(q, kv, x_win, win_start: int, sink, q_pos, ratio: int, window: in
 
 
 # ---------------------------------------------------------------------------
+# Backward of the core attention ([cf-1 §4.3]: training runs a deterministic
+# attention backward; the pages give no formulas, so these are the gradients
+# of the forward definitions above)
+# ---------------------------------------------------------------------------
+
+
+def attend_bwd(q, keys, sink, dout, scale: float = 1.0):
+    """Gradients of ``attend`` for one query: o_h = sum_i P_hi key_i with
+    P_hi = e^{l_hi} / (e^{sink_h} + sum_j e^{l_hj}), l_hi = scale q_h . key_i.
+
+    Keys are also the values, so each key row collects both roles:
+      dP_hi  = dout_h . key_i              (value role)
+      D_h    = dout_h . o_h = sum_i P_hi dP_hi
+      dl_hi  = P_hi (dP_hi - D_h)          (softmax Jacobian; the sink is one
+                                            more softmax term with no value)
+      dq_h   = scale sum_i dl_hi key_i
+      dkey_i = sum_h (scale dl_hi q_h + P_hi dout_h)
+      dsink_h = -P_sink,h D_h,  P_sink,h = e^{sink_h} / (e^{sink_h} + sum_j e^{l_hj})
+
+    q, dout: [H, d]; keys: [n, d]; sink: [H]. Returns (dq [H, d], dkeys [n, d],
+    dsink [H]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.float64)
+    sink = np.asarray(sink, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    o, lse = attend(q, keys, sink, scale)
+    P = np.exp(scale * (q @ keys.T) - lse[:, None])                 # [H, n]
+    p_sink = np.exp(sink - lse)                                    # [H]
+    dP = dout @ keys.T                                             # [H, n]
+    D = np.sum(dout * o, axis=1)                                   # [H]
+    dl = P * (dP - D[:, None])
+    dq = scale * (dl @ keys)
+    dkeys = scale * (dl.T @ q) + P.T @ dout
+    dsink = -p_sink * D
+    return dq, dkeys, dsink
+
+
+def sparse_attn_bwd(q, kv, idx, x_win, win_start: int, sink, q_pos, dout, window: int = 128,
+                    scale: float = 1.0):
+    """Gradients of ``sparse_attn`` (same key sets, same readings).
+
+    Each selected entry and each window row collects the gradient of every
+    query that attends to it; the sink's gradient is summed over queries.
+    Returns (dq [Tq, H, d], dkv [N, d], dx_win [T_win, d], dsink [H]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kv = np.asarray(kv, dtype=np.float64)
+    x_win = np.asarray(x_win, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    Tq, H, d = q.shape
+    N = kv.shape[0]
+    dq = np.zeros_like(q)
+    dkv = np.zeros_like(kv)
+    dx_win = np.zeros_like(x_win)
+    dsink = np.zeros(H)
+    for t in range(Tq):
+        p = int(q_pos[t])
+        sel = np.asarray(idx[t], dtype=np.int64)
+        sel = sel[(sel >= 0) & (sel < N)]
+        rows = window_rows(p, window, win_start, x_win.shape[0]) - win_start
+        keys = np.concatenate([kv[sel], x_win[rows]], axis=0)
+        dq[t], dk, ds = attend_bwd(q[t], keys, sink, dout[t], scale)
+        np.add.at(dkv, sel, dk[:len(sel)])
+        np.add.at(dx_win, rows, dk[len(sel):])
+        dsink += ds
+    return dq, dkv, dx_win, dsink
+
+
+def dense_attn_bwd(q, kv, x_win, win_start: int, sink, q_pos, ratio: int, dout, window: int = 128,
+                   scale: float = 1.0):
+    """Gradients of ``dense_attn``: ``sparse_attn_bwd`` with every visible entry selected."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    N = np.asarray(kv).shape[0]
+    n_vis = visible_entries(q_pos, ratio, N)
+    kmax = int(n_vis.max()) if len(n_vis) else 0
+    idx = np.full((len(q_pos), max(kmax, 1)), -1, dtype=np.int64)
+    for t, n in enumerate(n_vis):
+        idx[t, :n] = np.arange(n)
+    return sparse_attn_bwd(q, kv, idx, x_win, win_start, sink, q_pos, dout, window, scale)
+
+
+# ---------------------------------------------------------------------------
 # Whole layers (one sequence)
 # ---------------------------------------------------------------------------
 

@@ -498,3 +498,110 @@ def test_layer_brute_force_T16(seed):
             sel[t, ii[ii >= 0]] = True
         assert np.array_equal(sel, sel_ref)
 
+
+# ---------------------------------------------------------------- attention backward
+
+def _sparse_case(seed, Tq=4, H=2, d=5, N=7, T_win=6, k=3, win_start=2):
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((Tq, H, d))
+    kv = g.standard_normal((N, d))
+    xw = g.standard_normal((T_win, d))
+    sink = g.standard_normal(H)
+    dout = g.standard_normal((Tq, H, d))
+    q_pos = np.array([2, 4, 7, 9][:Tq])
+    idx = np.array([[0, 3, -1], [1, 2, 6], [-1, -1, -1], [0, 5, 9]])[:Tq, :k]   # holes and an index >= N
+    return q, kv, idx, xw, win_start, sink, q_pos, dout
+
+
+def _num_grad(f, x, eps=1e-6):
+    """Central differences of the scalar f at x (float64), element by element."""
+    gr = np.zeros_like(x)
+    for i in np.ndindex(x.shape):
+        x0 = x[i]
+        x[i] = x0 + eps
+        fp = f()
+        x[i] = x0 - eps
+        fm = f()
+        x[i] = x0
+        gr[i] = (fp - fm) / (2 * eps)
+    return gr
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("window,scale", [(3, 0.7), (1, 1.0), (0, 1.3)])
+def test_sparse_attn_bwd_finite_differences(seed, window, scale):
+    """Gradients of L = sum(dout * o) against central differences of the
+    forward oracle: every input, with holes, an index past N, windows clipped
+    by the supplied rows, and a query with no selected entry."""
+    q, kv, idx, xw, w0, sink, q_pos, dout = _sparse_case(seed)
+    L = lambda: float(np.sum(dout * O.sparse_attn(q, kv, idx, xw, w0, sink, q_pos, window, scale)[0]))
+    dq, dkv, dxw, ds = O.sparse_attn_bwd(q, kv, idx, xw, w0, sink, q_pos, dout, window, scale)
+    for got, x in ((dq, q), (dkv, kv), (dxw, xw), (ds, sink)):
+        np.testing.assert_allclose(got, _num_grad(L, x), rtol=1e-6, atol=1e-8)
+
+
+def test_dense_attn_bwd_finite_differences():
+    g = np.random.default_rng(9)
+    Tq, H, d, N, T_win, ratio, W = 5, 3, 4, 4, 8, 2, 3
+    q, kv, xw = g.standard_normal((Tq, H, d)), g.standard_normal((N, d)), g.standard_normal((T_win, d))
+    sink, dout = g.standard_normal(H), g.standard_normal((Tq, H, d))
+    q_pos = np.array([0, 1, 4, 6, 7])
+    L = lambda: float(np.sum(dout * O.dense_attn(q, kv, xw, 0, sink, q_pos, ratio, W)[0]))
+    dq, dkv, dxw, ds = O.dense_attn_bwd(q, kv, xw, 0, sink, q_pos, ratio, dout, W)
+    for got, x in ((dq, q), (dkv, kv), (dxw, xw), (ds, sink)):
+        np.testing.assert_allclose(got, _num_grad(L, x), rtol=1e-6, atol=1e-8)
+
+
+def _sparse_attn_torch(q, kv, idx, xw, w0, sink, q_pos, window, scale):
+    """Mask formulation in torch: logits over every entry and every window row,
+    masked to the query's key set, with the sink as one more logit whose value
+    row is zero."""
+    Tq, H, d = q.shape
+    N, T_win = kv.shape[0], xw.shape[0]
+    keys = torch.cat([kv, xw], 0)                                    # [N + T_win, d]
+    mask = torch.zeros(Tq, N + T_win, dtype=torch.bool)
+    for t in range(Tq):
+        for e in idx[t]:
+            if 0 <= e < N:
+                mask[t, e] = True
+        p = int(q_pos[t])
+        for a in range(w0, w0 + T_win):
+            if p - window < a <= p:
+                mask[t, N + a - w0] = True
+    logits = scale * torch.einsum("thd,jd->thj", q, keys)
+    logits = logits.masked_fill(~mask[:, None, :], float("-inf"))
+    logits = torch.cat([logits, sink[None, :, None].expand(Tq, H, 1)], -1)
+    prob = torch.softmax(logits, -1)[..., :-1]
+    return torch.einsum("thj,jd->thd", prob, keys)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_sparse_attn_bwd_matches_torch_autograd(seed):
+    """Mid-size case against torch autograd (float64) through the mask formulation."""
+    g = np.random.default_rng(40 + seed)
+    Tq, H, d, N, T_win, k, W, w0 = 24, 4, 16, 40, 30, 9, 6, 5
+    q_pos = np.sort(g.integers(w0, w0 + T_win, Tq))
+    idx = np.full((Tq, k), -1)
+    for t in range(Tq):
+        m = g.integers(0, k + 1)
+        idx[t, :m] = np.sort(g.choice(N, m, replace=False))
+    arrays = [g.standard_normal(s) for s in ((Tq, H, d), (N, d), (T_win, d), (H,), (Tq, H, d))]
+    q, kv, xw, sink, dout = arrays
+    tq, tkv, txw, ts = (torch.tensor(a, requires_grad=True) for a in (q, kv, xw, sink))
+    o = _sparse_attn_torch(tq, tkv, idx, txw, w0, ts, q_pos, W, 0.5)
+    (o * torch.tensor(dout)).sum().backward()
+    got = O.sparse_attn_bwd(q, kv, idx, xw, w0, sink, q_pos, dout, W, 0.5)
+    for a, t in zip(got, (tq, tkv, txw, ts)):
+        np.testing.assert_allclose(a, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attn_bwd_zero_cotangent_and_no_keys():
+    """A zero cotangent gives zero gradients; a query with no key and no sink
+    weight left (every logit masked) passes no gradient to any key."""
+    g = np.random.default_rng(3)
+    H, d, n = 3, 6, 9
+    q, keys, sink = (g.standard_normal(s) for s in ((H, d), (n, d), (H,)))
+    z = O.attend_bwd(q, keys, sink, np.zeros((H, d)))
+    assert all(np.all(a == 0) for a in z)
+    dq, dk, ds = O.attend_bwd(q, np.zeros((0, d)), sink, g.standard_normal((H, d)))
+    assert dk.shape == (0, d) and np.all(dq == 0) and np.all(ds == 0)
