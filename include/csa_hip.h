@@ -285,6 +285,56 @@ csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* 
                                      float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sparse_attn_bwd — gradients of sparse_attn_fwd (cf-1.com write-up §4.3:
+ * training runs a deterministic attention backward; the formulas are the
+ * derivatives of the forward's definition above). With P_i = e^{l_i - lse_h},
+ * D_h = dO_h . o_h, dP_i = dO_h . K_i and dl_i = P_i (dP_i - D_h):
+ *     dq_h    = scale sum_i dl_i K_i,
+ *     dK_i   += sum over heads and queries of (scale dl_i q_h + P_i dO_h)
+ *              (each key row is both key and value),
+ *     dsink_h = -sum over queries of e^{sink_h - lse_h} D_h.
+ * Inputs are those of the forward plus its outputs:
+ *   out, dout  [B, Tq, H, d] of t: the forward output and its gradient
+ *   lse        float32 [B, Tq, H]: the forward's log-sum-exp (sink included)
+ * Outputs (all written, including rows no query touches):
+ *   dq         [B, Tq, H, d] of t
+ *   dkv        float32 [B, N, d];  dx_win float32 [B, T_win, d]
+ *   dsink      float32 [H] (summed over B and Tq), or NULL when sink is NULL
+ * Limits: t == CSA_BF16, H 64 or 128, d == 128, 1 <= k <= 4096,
+ * B*Tq < 2^31, B*(N + T_win) < 2^31; idx rows as indexer_topk writes them
+ * (an entry repeated within a row is counted once per occurrence).
+ * Deterministic: every sum runs in a fixed order that depends only on the
+ * shapes (no floating-point atomics), so repeated calls give identical bits.
+ * The workspace holds the per-(query, key) gradient rows of up to 4 GiB of
+ * query rows at a time (query rows are processed in passes).
+ */
+size_t sparse_attn_bwd_workspace_size(int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H,
+                                      int32_t d, int32_t k, int32_t window);
+csa_status sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
+                           const int32_t* win_start, const float* sink, const int32_t* q_pos,
+                           csa_dtype t, int64_t B, int64_t Tq, int64_t N, int64_t T_win,
+                           int32_t H, int32_t d, int32_t k, int32_t window, float scale,
+                           const void* out, const float* lse, const void* dout, void* dq,
+                           float* dkv, float* dx_win, float* dsink, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * dense_compressed_attn_bwd — gradients of dense_compressed_attn_fwd
+ * (cf-1.com write-up §3.2, §4.3): sparse_attn_bwd with the key set of every
+ * query being all visible entries j < n(p) plus its window rows. Same
+ * layouts, limits and determinism; ratio >= 1 defines n(p).
+ */
+size_t dense_attn_bwd_workspace_size(int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H,
+                                     int32_t d, int32_t window);
+csa_status dense_compressed_attn_bwd(const void* q, const void* kv, const void* x_win,
+                                     const int32_t* win_start, const float* sink,
+                                     const int32_t* q_pos, csa_dtype t, int64_t B, int64_t Tq,
+                                     int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t ratio,
+                                     int32_t window, float scale, const void* out, const float* lse,
+                                     const void* dout, void* dq, float* dkv, float* dx_win,
+                                     float* dsink, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timer (measurement support). csa_kernel_timer_start() arms the
  * library to record a pair of hipEvents around each of the next
  * `max_launches` launches of kernel `kernel_id` (a csa_kernel_id), on the
@@ -301,7 +351,8 @@ typedef enum {
   CSA_KID_TOPK = 5,
   CSA_KID_SPARSE_ATTN = 6,
   CSA_KID_DENSE_ATTN = 7,
-  CSA_KID_ATTN_MERGE = 8
+  CSA_KID_ATTN_MERGE = 8,
+  CSA_KID_ATTN_BWD = 9
 } csa_kernel_id;
 csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches);
 int32_t csa_kernel_timer_read(float* ms_out, int32_t capacity);

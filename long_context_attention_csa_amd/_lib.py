@@ -15,7 +15,7 @@ CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1 = 0, 1, 2, 3
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_UNSUPPORTED",
           4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_HIP"}
 KID = {"compress": 1, "hca_compress": 2, "quantize": 3, "index_score": 4, "topk": 5,
-       "sparse_attn": 6, "dense_attn": 7, "attn_merge": 8}
+       "sparse_attn": 6, "dense_attn": 7, "attn_merge": 8, "attn_bwd": 9}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -44,6 +44,12 @@ SIGNATURES = {
     "sparse_attn_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
                                        _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "sparse_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    "sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
+                                       _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dense_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32]),
+    "dense_compressed_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32,
+                                                 _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dense_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
     "dense_compressed_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32,
                                                  _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),

@@ -31,6 +31,7 @@ FLAGS = [
 EXTRA = {
     "indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -23,6 +23,12 @@ hipError_t launch_indexer_topk(const void*, const void*, const float*, const voi
                                const int32_t*, int64_t, int64_t, int64_t, int, int, int, int, int32_t*, void*, bool,
                                void*, hipStream_t);
 size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max);
+size_t attn_bwd_ws_bytes(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window);
+hipError_t launch_attn_bwd(bool sparse, const void* q, const void* kv, const int32_t* idx, const void* x_win,
+                           const int32_t* win_start, const float* sink, const int32_t* q_pos, const void* out,
+                           const float* lse, const void* dout, int64_t B, int64_t Tq, int64_t N, int64_t T_win,
+                           int H, int k, int window, int ratio, float scale, void* dq, float* dkv, float* dx_win,
+                           float* dsink, void* ws, hipStream_t s);
 void set_batch_invariant(int on);
 int batch_invariant();
 hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void* kv, const int32_t* idx,
@@ -336,9 +342,83 @@ csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* 
                     "dense_compressed_attn_fwd");
 }
 
+static csa_status check_attn_bwd(const char* fn, const void* q, const void* kv, const void* x_win,
+                                 const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t,
+                                 int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d,
+                                 int32_t window, const void* out, const float* lse, const void* dout, void* dq,
+                                 float* dkv, float* dx_win, float* dsink) {
+  csa_status st = check_attn_common(fn, q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win, H, d, window,
+                                    const_cast<void*>(out));
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(t == CSA_BF16, CSA_ERR_UNSUPPORTED, "%s: dtype must be CSA_BF16", fn);
+  CSA_REQUIRE(H == 64 || H == 128, CSA_ERR_UNSUPPORTED, "%s: H %d (64 or 128)", fn, H);
+  if (B * Tq == 0) return CSA_OK;
+  CSA_REQUIRE(lse && dout && dq, CSA_ERR_NULL, "%s: NULL lse, dout or dq", fn);
+  CSA_REQUIRE(N == 0 || dkv, CSA_ERR_NULL, "%s: dkv is NULL", fn);
+  CSA_REQUIRE(T_win == 0 || dx_win, CSA_ERR_NULL, "%s: dx_win is NULL", fn);
+  CSA_REQUIRE(!sink || dsink, CSA_ERR_NULL, "%s: dsink is NULL although sink is given", fn);
+  CSA_REQUIRE((int64_t)B * (N + T_win) < (int64_t)1 << 31, CSA_ERR_SHAPE, "%s: B*(N+T_win) must be < 2^31", fn);
+  return CSA_OK;
+}
+
+size_t sparse_attn_bwd_workspace_size(int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d,
+                                      int32_t k, int32_t window) {
+  (void)d;
+  if (B <= 0 || Tq <= 0 || N < 0 || T_win < 0 || H <= 0 || k < 1 || window < 0) return 0;
+  return attn_bwd_ws_bytes(true, B, Tq, N, T_win, H, k, window);
+}
+
+csa_status sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
+                           const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t, int64_t B,
+                           int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t k, int32_t window,
+                           float scale, const void* out, const float* lse, const void* dout, void* dq, float* dkv,
+                           float* dx_win, float* dsink, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  csa_status st = check_attn_bwd("sparse_attn_bwd", q, kv, x_win, win_start, sink, q_pos, t, B, Tq, N, T_win, H, d,
+                                 window, out, lse, dout, dq, dkv, dx_win, dsink);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_SHAPE, "sparse_attn_bwd: k %d (1..4096)", k);
+  if (B * Tq == 0) return CSA_OK;
+  CSA_REQUIRE(idx, CSA_ERR_NULL, "sparse_attn_bwd: idx is NULL");
+  const size_t need = sparse_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, k, window);
+  CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "sparse_attn_bwd: workspace %zu < %zu bytes", ws_bytes,
+              need);
+  return hip_status(launch_attn_bwd(true, q, kv, idx, x_win, win_start, sink, q_pos, out, lse, dout, B, Tq, N, T_win,
+                                    H, k, window, 1, scale, dq, dkv, dx_win, dsink, ws, (hipStream_t)stream),
+                    "sparse_attn_bwd");
+}
+
+size_t dense_attn_bwd_workspace_size(int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d,
+                                     int32_t window) {
+  (void)d;
+  if (B <= 0 || Tq <= 0 || N < 0 || T_win < 0 || H <= 0 || window < 0) return 0;
+  return attn_bwd_ws_bytes(false, B, Tq, N, T_win, H, 0, window);
+}
+
+csa_status dense_compressed_attn_bwd(const void* q, const void* kv, const void* x_win, const int32_t* win_start,
+                                     const float* sink, const int32_t* q_pos, csa_dtype t, int64_t B, int64_t Tq,
+                                     int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t ratio, int32_t window,
+                                     float scale, const void* out, const float* lse, const void* dout, void* dq,
+                                     float* dkv, float* dx_win, float* dsink, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  g_last_error.clear();
+  csa_status st = check_attn_bwd("dense_compressed_attn_bwd", q, kv, x_win, win_start, sink, q_pos, t, B, Tq, N,
+                                 T_win, H, d, window, out, lse, dout, dq, dkv, dx_win, dsink);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "dense_compressed_attn_bwd: ratio %d", ratio);
+  if (B * Tq == 0) return CSA_OK;
+  const size_t need = dense_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, window);
+  CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "dense_compressed_attn_bwd: workspace %zu < %zu bytes",
+              ws_bytes, need);
+  return hip_status(launch_attn_bwd(false, q, kv, nullptr, x_win, win_start, sink, q_pos, out, lse, dout, B, Tq, N,
+                                    T_win, H, 0, window, ratio, scale, dq, dkv, dx_win, dsink, ws,
+                                    (hipStream_t)stream),
+                    "dense_compressed_attn_bwd");
+}
+
 csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches) {
   g_last_error.clear();
-  CSA_REQUIRE(kernel_id >= CSA_KID_COMPRESS && kernel_id <= CSA_KID_ATTN_MERGE, CSA_ERR_SHAPE,
+  CSA_REQUIRE(kernel_id >= CSA_KID_COMPRESS && kernel_id <= CSA_KID_ATTN_BWD, CSA_ERR_SHAPE,
               "csa_kernel_timer_start: kernel id %d", kernel_id);
   CSA_REQUIRE(max_launches >= 1 && max_launches <= kMaxTimed, CSA_ERR_SHAPE,
               "csa_kernel_timer_start: max_launches %d (1..%d)", max_launches, kMaxTimed);

@@ -220,6 +220,58 @@ def dense_compressed_attn_fwd(q, kv, x_win, win_start, sink, q_pos, ratio: int =
     return (out, lse) if want_lse else out
 
 
+def sparse_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, k, window) -> int:
+    return int(lib().sparse_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, k, window))
+
+
+def _bwd_outputs(q, kv, x_win, sink):
+    B, N, T_win = q.shape[0], kv.shape[1], x_win.shape[1]
+    dev = q.device
+    dq = torch.empty_like(q)
+    dkv = torch.empty(B, N, q.shape[3], dtype=torch.float32, device=dev)
+    dxw = torch.empty(B, T_win, q.shape[3], dtype=torch.float32, device=dev)
+    dsink = torch.empty(q.shape[2], dtype=torch.float32, device=dev) if sink is not None else None
+    return dq, dkv, dxw, dsink
+
+
+def sparse_attn_bwd(q, kv, idx, x_win, win_start, sink, q_pos, out, lse, dout, window: int = 128,
+                    scale: float = 1.0, ws=None):
+    """Gradients of sparse_attn_fwd (bf16 q/kv/x_win/out/dout, H 64 or 128). Returns
+    (dq [B, Tq, H, d] bf16, dkv [B, N, d] float32, dx_win [B, T_win, d] float32,
+    dsink [H] float32 or None)."""
+    _contig(q, kv, idx, x_win, win_start, sink, q_pos, out, lse, dout)
+    t = _float_dtype(q)
+    B, Tq, H, d = q.shape
+    N, T_win, k = kv.shape[1], x_win.shape[1], idx.shape[2]
+    dq, dkv, dxw, dsink = _bwd_outputs(q, kv, x_win, sink)
+    ws, nbytes = _workspace(sparse_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, k, window), q.device, ws)
+    check("sparse_attn_bwd", lib().sparse_attn_bwd(
+        _ptr(q), _ptr(kv), _ptr(idx), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H,
+        d, k, window, scale, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv), _ptr(dxw), _ptr(dsink),
+        _ptr(ws), nbytes, _stream()))
+    return dq, dkv, dxw, dsink
+
+
+def dense_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, window) -> int:
+    return int(lib().dense_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, window))
+
+
+def dense_compressed_attn_bwd(q, kv, x_win, win_start, sink, q_pos, out, lse, dout, ratio: int = 128,
+                              window: int = 128, scale: float = 1.0, ws=None):
+    """Gradients of dense_compressed_attn_fwd; same outputs as sparse_attn_bwd."""
+    _contig(q, kv, x_win, win_start, sink, q_pos, out, lse, dout)
+    t = _float_dtype(q)
+    B, Tq, H, d = q.shape
+    N, T_win = kv.shape[1], x_win.shape[1]
+    dq, dkv, dxw, dsink = _bwd_outputs(q, kv, x_win, sink)
+    ws, nbytes = _workspace(dense_attn_bwd_workspace_size(B, Tq, N, T_win, H, d, window), q.device, ws)
+    check("dense_compressed_attn_bwd", lib().dense_compressed_attn_bwd(
+        _ptr(q), _ptr(kv), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H, d, ratio,
+        window, scale, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv), _ptr(dxw), _ptr(dsink), _ptr(ws),
+        nbytes, _stream()))
+    return dq, dkv, dxw, dsink
+
+
 def kernel_timer_start(kernel: str, max_launches: int) -> None:
     check("csa_kernel_timer_start", lib().csa_kernel_timer_start(KID[kernel], max_launches))
 
