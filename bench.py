@@ -18,7 +18,7 @@ library's kernel timer), the CPU oracle timed on a bounded sample, and extra
 workloads (CSA decode at 262k context; prefill TFLOP/s) under "extras".
 
 Usage: python bench.py [--steps K] [--warmup W]
-                       [--extras decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk|none]
+                       [--extras decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca|none]
 """
 from __future__ import annotations
 
@@ -487,6 +487,79 @@ def prefill_chunk(torch, C, syn, iters):
             "indexer_bf16_scores": bf}
 
 
+def attn_bwd_flops(n_keys, H, d=128):
+    """S, dP, dQ and the two key-row products: 10 flops per (query, key, head, channel)."""
+    return float(np.sum(n_keys, dtype=np.float64)) * H * d * 10
+
+
+def bwd_csa(torch, C, syn, iters):
+    """CSA core-attention backward, T = 65,536, 64 heads, top-512 selected by the
+    fp8 indexer plus the 128-token window and the sink (the prefill layer's
+    shapes); the forward's output and log-sum-exp are computed once in setup."""
+    dev, bf = "cuda", torch.bfloat16
+    T, H, H_I, d_I, k, W = 65536, 64, 64, 128, 512, 128
+    s = 6000
+    c = {n: syn.normal_device(s + i, (1, T, 128), dev, bf) for i, n in enumerate(["c_a", "c_b", "z_a", "z_b"])}
+    ci = {n: syn.normal_device(s + 10 + i, (1, T, d_I), dev, bf) for i, n in enumerate(["a", "b", "za", "zb"])}
+    q = syn.normal_device(s + 20, (1, T, H, 128), dev, bf, scale=1 / np.sqrt(128))
+    qi32 = syn.normal_device(s + 21, (1, T, H_I, d_I), dev)
+    qi, qs = C.csa_quantize_rows(qi32, "fp8")
+    del qi32
+    w = syn.uniform_device(s + 22, (1, T, H_I), dev)
+    sink = syn.normal_device(s + 23, (H,), dev)
+    dout = syn.normal_device(s + 24, (1, T, H, 128), dev, bf)
+    q_pos = torch.arange(T, dtype=torch.int32, device=dev)[None]
+    win_start = torch.zeros(1, dtype=torch.int32, device=dev)
+    E = C.csa_compress(c["c_a"], c["c_b"], c["z_a"], c["z_b"], 4)
+    KI = C.csa_compress(ci["a"], ci["b"], ci["za"], ci["zb"], 4, out_fmt="fp8")
+    idx = C.indexer_topk(qi, qs, w, KI[0], KI[1], "fp8", q_pos, 4, k, d_I)
+    out, lse = C.sparse_attn_fwd(q, E, idx, c["c_a"], win_start, sink, q_pos, W, 1.0, want_lse=True)
+    N = T // 4
+    ws = torch.empty(C.sparse_attn_bwd_workspace_size(1, T, N, T, H, 128, k, W), dtype=torch.uint8, device=dev)
+    fn = lambda: C.sparse_attn_bwd(q, E, idx, c["c_a"], win_start, sink, q_pos, out, lse, dout, W, 1.0, ws=ws)
+    t = time_ops(torch, [("sparse_attn_bwd", fn)], iters)["sparse_attn_bwd"]
+    main = call_kernel_ms(torch, C, fn, "attn_bwd")
+    p = np.arange(T, dtype=np.int64)
+    keys = np.minimum(k, np.minimum(N, (p + 1) // 4)) + np.minimum(p + 1, W)
+    fl = attn_bwd_flops(keys, H)
+    return {"workload": "csa_attn_bwd_bf16_T65536", "tokens": T, "heads": H, "top_k": k, "ms": round(t, 4),
+            "main_kernel_ms": None if main is None else round(main, 4), "tflop": round(fl / 1e12, 4),
+            "tflop_s": round(fl / (t * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(fl / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "main_kernel_tflop_s": None if not main else round(fl / (main * 1e-3) / 1e12, 2),
+            "workspace_gb": round(ws.numel() / 1e9, 2)}
+
+
+def bwd_hca(torch, C, syn, iters):
+    """HCA core-attention backward, T = 131,072, 64 heads, every visible entry
+    of 1024 plus the window and the sink."""
+    dev, bf = "cuda", torch.bfloat16
+    T, H, ratio, W = 131072, 64, 128, 128
+    N = T // ratio
+    s = 7000
+    q = syn.normal_device(s, (1, T, H, 128), dev, bf, scale=1 / np.sqrt(128))
+    E = syn.normal_device(s + 1, (1, N, 128), dev, bf)
+    xw = syn.normal_device(s + 2, (1, T, 128), dev, bf)
+    sink = syn.normal_device(s + 3, (H,), dev)
+    dout = syn.normal_device(s + 4, (1, T, H, 128), dev, bf)
+    q_pos = torch.arange(T, dtype=torch.int32, device=dev)[None]
+    win_start = torch.zeros(1, dtype=torch.int32, device=dev)
+    out, lse = C.dense_compressed_attn_fwd(q, E, xw, win_start, sink, q_pos, ratio, W, 1.0, want_lse=True)
+    ws = torch.empty(C.dense_attn_bwd_workspace_size(1, T, N, T, H, 128, W), dtype=torch.uint8, device=dev)
+    fn = lambda: C.dense_compressed_attn_bwd(q, E, xw, win_start, sink, q_pos, out, lse, dout, ratio, W, 1.0, ws=ws)
+    t = time_ops(torch, [("dense_attn_bwd", fn)], iters)["dense_attn_bwd"]
+    main = call_kernel_ms(torch, C, fn, "attn_bwd")
+    p = np.arange(T, dtype=np.int64)
+    keys = np.minimum(N, (p + 1) // ratio) + np.minimum(p + 1, W)
+    fl = attn_bwd_flops(keys, H)
+    return {"workload": "hca_attn_bwd_bf16_T131072", "tokens": T, "heads": H, "ms": round(t, 4),
+            "main_kernel_ms": None if main is None else round(main, 4), "tflop": round(fl / 1e12, 4),
+            "tflop_s": round(fl / (t * 1e-3) / 1e12, 2),
+            "frac_bf16_peak": round(fl / (t * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "main_kernel_tflop_s": None if not main else round(fl / (main * 1e-3) / 1e12, 2),
+            "workspace_gb": round(ws.numel() / 1e9, 2)}
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -495,7 +568,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
-    ap.add_argument("--extras", default="decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk",
+    ap.add_argument("--extras", default="decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca",
                     help="comma list of decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk or 'none'")
     ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -573,7 +646,7 @@ def main():
         del st4
         torch.cuda.empty_cache()
     for key, fn in (("decode_append", decode_append), ("prefill_csa", prefill_csa), ("prefill_hca", prefill_hca),
-                    ("prefill_chunk", prefill_chunk)):
+                    ("prefill_chunk", prefill_chunk), ("bwd_csa", bwd_csa), ("bwd_hca", bwd_hca)):
         if key in wanted:
             r = fn(torch, C, syn, args.prefill_iters)
             log(f"[bench] {r['workload']}: {r}")

@@ -32,7 +32,8 @@
 //   k_bwd_place        per chunk, query by query: the position of each slot
 //   k_attn_bwd16       per query: dq, the slot gradients G, the sink terms
 //   k_bwd_reduce       per key: sum of its contributions in list order
-// and once at the end k_bwd_sink (sink gradient over all rows, fixed tree).
+// and once at the end k_bwd_sink_part / k_bwd_sink_final (sink gradient over
+// all rows in a fixed order).
 #include "attn_tile.hpp"
 
 namespace csa {
@@ -42,6 +43,7 @@ constexpr int kBwdQc = 64;                       // query rows per placement chu
 constexpr int64_t kBwdGBudget = (int64_t)4 << 30;   // bytes of G per pass
 constexpr int kScanPer = 16;                     // totals per thread in the key scan
 constexpr int kScanBlock = kBwdThreads * kScanPer;
+constexpr int kSinkBlocks = 256;                 // first-level blocks of the sink gradient sum
 
 // Key set of a query row: n_sel selected (or visible) slots, then n_win
 // window rows starting at absolute position lo.
@@ -518,49 +520,87 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   }
 }
 
-// One wave per key: the sum of its contributions in list order (added to the
-// previous passes' sum when `accumulate`).
+// One block per key: wave w sums the w-th quarter of the key's contribution
+// list (8 loads in flight, added in list order), then the quarters are added
+// in order to the previous passes' sum (when `accumulate`). The split
+// depends only on the list length, so the result is the same on every run.
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_reduce(const float* __restrict__ G,
                                                             const uint32_t* __restrict__ off, int64_t nids,
                                                             int64_t N, int64_t T_win, float* __restrict__ dkv,
                                                             float* __restrict__ dx_win, int accumulate) {
-  const int64_t id = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
-  if (id >= nids) return;
-  const int lane = threadIdx.x & 63;
-  const int64_t b = id / (N + T_win), j = id % (N + T_win);
-  float* o = (j < N ? dkv + (b * N + j) * kD : dx_win + (b * T_win + (j - N)) * kD) + 2 * lane;
-  float2 acc = accumulate ? *reinterpret_cast<const float2*>(o) : make_float2(0.f, 0.f);
-  const uint32_t u0 = off[id], u1 = off[id + 1];
-  for (uint32_t u = u0; u < u1; ++u) {
-    const float2 v = *reinterpret_cast<const float2*>(G + (int64_t)u * kD + 2 * lane);
+  __shared__ float2 part[kBwdThreads / 64][64];
+  const int64_t id = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint32_t u0 = off[id], len = off[id + 1] - u0;
+  const uint32_t a = u0 + (uint32_t)(((uint64_t)len * wv) / 4), e = u0 + (uint32_t)(((uint64_t)len * (wv + 1)) / 4);
+  const float* gp = G + 2 * lane;
+  float2 acc = make_float2(0.f, 0.f);
+  uint32_t u = a;
+  for (; u + 8 <= e; u += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const float2*>(gp + (int64_t)(u + i) * kD);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc.x += v[i].x;
+      acc.y += v[i].y;
+    }
+  }
+  for (; u < e; ++u) {
+    const float2 v = *reinterpret_cast<const float2*>(gp + (int64_t)u * kD);
     acc.x += v.x;
     acc.y += v.y;
   }
-  *reinterpret_cast<float2*>(o) = acc;
+  part[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    const int64_t b = id / (N + T_win), j = id % (N + T_win);
+    float* o = (j < N ? dkv + (b * N + j) * kD : dx_win + (b * T_win + (j - N)) * kD) + 2 * lane;
+    float2 t = accumulate ? *reinterpret_cast<const float2*>(o) : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kBwdThreads / 64; ++w) {
+      t.x += part[w][lane].x;
+      t.y += part[w][lane].y;
+    }
+    *reinterpret_cast<float2*>(o) = t;
+  }
 }
 
-// dsink[h] = sum over rows of the per-row terms: a fixed strided split over
-// 256 threads, then a fixed tree.
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_sink(const float* __restrict__ part, int64_t rows, int H,
-                                                          float* __restrict__ dsink) {
+// Sink gradient, first level: block j sums rows [j R, (j + 1) R) for every
+// head (thread: head tid % H, rows tid / H + (256 / H) i), the row groups
+// added in order; part[j][h].
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_sink_part(const float* __restrict__ rowv, int64_t rows, int H,
+                                                               int64_t R, float* __restrict__ part) {
   __shared__ float red[kBwdThreads];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  const int tid = threadIdx.x, h = tid % H, rg = tid / H, ng = kBwdThreads / H;
+  const int64_t r0 = (int64_t)blockIdx.x * R;
+  const int64_t r1 = r0 + R < rows ? r0 + R : rows;
   float s = 0.f;
-  for (int64_t r = tid; r < rows; r += kBwdThreads) s += part[r * H + h];
+  for (int64_t r = r0 + rg; r < r1; r += ng) s += rowv[r * H + h];
   red[tid] = s;
   __syncthreads();
-  for (int o = kBwdThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
+  if (rg == 0) {
+    float t = 0.f;
+    for (int gi = 0; gi < ng; ++gi) t += red[gi * H + h];
+    part[(int64_t)blockIdx.x * H + h] = t;
   }
-  if (tid == 0) dsink[h] = red[0];
+}
+
+// Second level: dsink[h] = sum over blocks j of part[j][h], in order.
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_sink_final(const float* __restrict__ part, int nb, int H,
+                                                                float* __restrict__ dsink) {
+  const int h = threadIdx.x;
+  if (h >= H) return;
+  float t = 0.f;
+  for (int j = 0; j < nb; ++j) t += part[(int64_t)j * H + h];
+  dsink[h] = t;
 }
 
 // ------------------------------------------------------------------ host side
 
 struct BwdPlan {
   int64_t rows, smax, rows_pass, nchunks, nids, nscan;
-  size_t o_cnt, o_total, o_off, o_bsum, o_pos, o_g, o_sink, bytes;
+  size_t o_cnt, o_total, o_off, o_bsum, o_pos, o_g, o_sink, o_spart, bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -585,6 +625,7 @@ static BwdPlan bwd_plan(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T
   p.o_pos = o;   o += align256((size_t)p.rows_pass * p.smax * 4);
   p.o_g = o;     o += align256((size_t)p.rows_pass * p.smax * kD * 4);
   p.o_sink = o;  o += align256((size_t)p.rows * H * 4);
+  p.o_spart = o; o += align256((size_t)kSinkBlocks * H * 4);
   p.bytes = o;
   return p;
 }
@@ -640,12 +681,17 @@ static hipError_t run_attn_bwd(const uint16_t* q, const uint16_t* kv, const int3
     timer_after(CSA_KID_ATTN_BWD, s);
     if (e != hipSuccess) return e;
     if (p.nids > 0)
-      k_bwd_reduce<<<(unsigned)cdiv(p.nids, kBwdThreads / 64), kBwdThreads, 0, s>>>(G, off, p.nids, N, T_win, dkv,
-                                                                                   dx_win, r0 > 0 ? 1 : 0);
+      k_bwd_reduce<<<(unsigned)p.nids, kBwdThreads, 0, s>>>(G, off, p.nids, N, T_win, dkv, dx_win, r0 > 0 ? 1 : 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (sink && dsink) k_bwd_sink<<<(unsigned)H, kBwdThreads, 0, s>>>(spart, p.rows, H, dsink);
+  if (sink && dsink) {
+    float* sp2 = reinterpret_cast<float*>(wb + p.o_spart);
+    const int64_t R = cdiv(p.rows, kSinkBlocks);
+    const int nb = (int)cdiv(p.rows, R);
+    k_bwd_sink_part<<<(unsigned)nb, kBwdThreads, 0, s>>>(spart, p.rows, H, R, sp2);
+    k_bwd_sink_final<<<1, kBwdThreads, 0, s>>>(sp2, nb, H, dsink);
+  }
   return hipGetLastError();
 }
 
