@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   __shared__ __align__(16) uint16_t ot[H * kD];
   __shared__ __align__(16) uint16_t pl[H * kKT];
   __shared__ __align__(16) uint16_t dll[H * kKT];
-  __shared__ uint8_t kval[kKT];
+  __shared__ __align__(4) uint8_t kval[kKT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,24 +300,32 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 
   const uint16_t* kvb = kv + w.b * N * kD;
   const uint16_t* xwb = x_win + w.b * T_win * kD;
-  auto key_row = [&](int64_t kk) -> const uint16_t* {   // kk < nk
-    if (kk < w.n_sel) {
-      const int64_t e = SPARSE ? (int64_t)idx[r * k + kk] : kk;
-      return (e >= 0 && e < N) ? kvb + e * kD : nullptr;
-    }
-    return xwb + (w.lo + (kk - w.n_sel) - w.w0) * kD;
-  };
-  // a thread's 4 chunks of a tile: chunk i = 256 j + tid, row i / 16, chunk i % 16
-  i32x4 kr[4];
-  bool kok[4];
-  auto load_tile = [&](int64_t t) {
+  // A thread loads chunks 256 j + tid of a tile: row 16 j + tid / 16, chunk
+  // tid % 16. The selected indices of its rows are loaded one tile ahead of
+  // the rows themselves, so a row load never waits for its index load.
+  const int crow = tid >> 4, cch = tid & 15;
+  auto load_idx = [&](int64_t t, int32_t (&e)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = 256 * j + tid;
-      const int64_t kk = t * kKT + (i >> 4);
-      const uint16_t* src = kk < nk ? key_row(kk) : nullptr;
+      const int64_t kk = t * kKT + 16 * j + crow;
+      e[j] = (SPARSE && kk < w.n_sel) ? idx[r * k + kk] : 0;
+    }
+  };
+  i32x4 kr[4];
+  bool kok[4];
+  auto load_tile = [&](int64_t t, const int32_t (&e)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t kk = t * kKT + 16 * j + crow;
+      const uint16_t* src = nullptr;
+      if (kk < w.n_sel) {
+        const int64_t en = SPARSE ? (int64_t)e[j] : kk;
+        if (en >= 0 && en < N) src = kvb + en * kD;
+      } else if (kk < nk) {
+        src = xwb + (w.lo + (kk - w.n_sel) - w.w0) * kD;
+      }
       kok[j] = src != nullptr;
-      kr[j] = src ? *reinterpret_cast<const i32x4*>(src + (i & 15) * 8) : i32x4{0, 0, 0, 0};
+      kr[j] = src ? *reinterpret_cast<const i32x4*>(src + cch * 8) : i32x4{0, 0, 0, 0};
     }
   };
 
@@ -332,14 +340,37 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   const uint32_t plb = (uint32_t)(uintptr_t)pl, dlb = (uint32_t)(uintptr_t)dll;
   const int64_t ntiles = cdiv(nk, kKT);
   const int32_t* prow = posbuf + (r - r0) * smax;
-  if (ntiles > 0) load_tile(0);
+  // Tile-invariant LDS offsets of the G^T operands: the transposed reads of
+  // the Q / dO rows for d blocks 2 wv, 2 wv + 1, and of P / dl for key block
+  // nb (row trow = 4 g + col / 4 of each 16-row block, unit 4 nb + col % 4).
+  uint32_t ga[2], gb[4];
+#pragma unroll
+  for (int d2 = 0; d2 < 2; ++d2) {
+    ga[d2] = (((uint32_t)(32 * (2 * wv + d2))) ^ tl.vx) + tl.vofs;
+    opaque(ga[d2]);
+  }
+  {
+    const int trow = 4 * g + (col >> 2);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      gb[nb] = (uint32_t)trow * 128u + 8u * (uint32_t)((4 * nb + (col & 3)) ^ trow);
+      opaque(gb[nb]);
+    }
+  }
+  int32_t e_next[4];
+  {
+    int32_t e0[4];
+    load_idx(0, e0);
+    if (ntiles > 0) load_tile(0, e0);
+    load_idx(1, e_next);
+  }
   for (int64_t t = 0; t < ntiles; ++t) {
     __syncthreads();   // the previous tile's reads of kt, pl, dl are done
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i = 256 * j + tid, row = i >> 4, c = i & 15;
-      *reinterpret_cast<i32x4*>(kt + row * kD + ((c ^ (row & 15)) * 8)) = kr[j];
-      if (c == 0) kval[row] = kok[j] ? 1 : 0;
+      const int row = 16 * j + crow;
+      *reinterpret_cast<i32x4*>(kt + row * kD + ((cch ^ (row & 15)) * 8)) = kr[j];
+      if (cch == 0) kval[row] = kok[j] ? 1 : 0;
     }
     int32_t pv[4];
 #pragma unroll
@@ -348,7 +379,10 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
       pv[nb] = kk < nk ? prow[kk] : -1;
     }
     __syncthreads();
-    if (t + 1 < ntiles) load_tile(t + 1);
+    if (t + 1 < ntiles) {
+      load_tile(t + 1, e_next);
+      load_idx(t + 2, e_next);
+    }
 
     // ---- S^T = K Q^T and dP^T = K dO^T (keys 16 kb + 4 g + rr, head column col)
     float s[HPW][4][4], dp[HPW][4][4];
@@ -389,18 +423,16 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
     // ---- P = exp(l - lse), scale * dl = scale * P (dP - D); no key or no
     // softmax mass: 0
     {
-      uint32_t okm = 0;   // bit 4 kb + rr: key 16 kb + 4 g + rr holds a key
+      uint32_t okw[4];    // byte rr of word kb: key 16 kb + 4 g + rr holds a key
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) okm |= (uint32_t)kval[16 * kb + 4 * g + rr] << (4 * kb + rr);
+      for (int kb = 0; kb < 4; ++kb) okw[kb] = reinterpret_cast<const uint32_t*>(kval)[4 * kb + g];
 #pragma unroll
       for (int hb = 0; hb < HPW; ++hb)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const bool ok = live[hb] && ((okm >> (4 * kb + rr)) & 1u);
+            const bool ok = live[hb] && ((okw[kb] >> (8 * rr)) & 1u);
             const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(s[hb][kb][rr], scale2, -lse2[hb])) : 0.f;
             s[hb][kb][rr] = pv;
             dp[hb][kb][rr] = scale * pv * (dp[hb][kb][rr] - Dh[hb]);
@@ -458,16 +490,12 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
       for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[d2][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // transposed-read row of this lane within a 16-row block, and its unit
-      const int trow = 4 * g + (col >> 2);
 #pragma unroll
       for (int ks = 0; ks < H / 32; ++ks) {
         Frag<uint16_t> aq[2], ao[2];
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2) {
-          const int db = 2 * wv + d2;
-          uint32_t a = (((uint32_t)(32 * db)) ^ tl.vx) + tl.vofs + 8192u * (uint32_t)ks;
-          opaque(a);
+          const uint32_t a = ga[d2] + 8192u * (uint32_t)ks;
           const i32x2 q0 = __builtin_bit_cast(i32x2, lds_read_tr16(qtb + a));
           const i32x2 q1 = __builtin_bit_cast(i32x2, lds_read_tr16(qtb + a + 4096));
           const i32x2 o0 = __builtin_bit_cast(i32x2, lds_read_tr16(otb + a));
@@ -477,10 +505,8 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
         }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const int u = 4 * nb + (col & 3);
-          const int hlo = 32 * ks + trow, hhi = hlo + 16;
-          const uint32_t olo = (uint32_t)hlo * 128u + 8u * (uint32_t)(u ^ (hlo & 15));
-          const uint32_t ohi = (uint32_t)hhi * 128u + 8u * (uint32_t)(u ^ (hhi & 15));
+          // rows 32 ks + trow (+ 16) share the swizzle of row trow
+          const uint32_t olo = gb[nb] + 4096u * (uint32_t)ks, ohi = olo + 2048u;
           const i32x2 l0 = __builtin_bit_cast(i32x2, lds_read_tr16(dlb + olo));
           const i32x2 l1 = __builtin_bit_cast(i32x2, lds_read_tr16(dlb + ohi));
           const i32x2 p0 = __builtin_bit_cast(i32x2, lds_read_tr16(plb + olo));
