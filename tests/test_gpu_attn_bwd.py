@@ -169,3 +169,64 @@ def test_attn_bwd_deterministic():
     b = _run_sparse(q, kv, idx, xw, w0, sink, q_pos, dout, 128, 1.0)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_sparse_attn_bwd_fullsize_sampled():
+    """The CSA prefill shape the benchmark times (T = 65,536, 64 heads, top-512
+    from the fp8 indexer, window 128, sink), run exactly as there: repeated
+    calls are bit-identical; dq of sampled rows, dkv of sampled entries (the
+    oracle's per-row gradients summed over every row that selected them) and
+    dx_win of sampled window rows match the oracle."""
+    dev_, bf = "cuda", BF
+    T, H, H_I, d_I, k, W = 65536, 64, 64, 128, 512, 128
+    N = T // 4
+    s = 6000
+    c = {n: syn.normal_device(s + i, (1, T, 128), dev_, bf) for i, n in enumerate(["c_a", "c_b", "z_a", "z_b"])}
+    ci = {n: syn.normal_device(s + 10 + i, (1, T, d_I), dev_, bf) for i, n in enumerate(["a", "b", "za", "zb"])}
+    q = syn.normal_device(s + 20, (1, T, H, 128), dev_, bf, scale=1 / np.sqrt(128))
+    qi32 = syn.normal_device(s + 21, (1, T, H_I, d_I), dev_)
+    qi, qs = C.csa_quantize_rows(qi32, "fp8")
+    del qi32
+    w = syn.uniform_device(s + 22, (1, T, H_I), dev_)
+    sink = syn.normal_device(s + 23, (H,), dev_)
+    dout = syn.normal_device(s + 24, (1, T, H, 128), dev_, bf)
+    q_pos = torch.arange(T, dtype=torch.int32, device=dev_)[None]
+    win_start = torch.zeros(1, dtype=torch.int32, device=dev_)
+    E = C.csa_compress(c["c_a"], c["c_b"], c["z_a"], c["z_b"], 4)
+    KI = C.csa_compress(ci["a"], ci["b"], ci["za"], ci["zb"], 4, out_fmt="fp8")
+    idx = C.indexer_topk(qi, qs, w, KI[0], KI[1], "fp8", q_pos, 4, k, d_I)
+    out, lse = C.sparse_attn_fwd(q, E, idx, c["c_a"], win_start, sink, q_pos, W, 1.0, want_lse=True)
+    _print("bwd full size: first call")
+    a = C.sparse_attn_bwd(q, E, idx, c["c_a"], win_start, sink, q_pos, out, lse, dout, W, 1.0)
+    _print("bwd full size: second call")
+    b = C.sparse_attn_bwd(q, E, idx, c["c_a"], win_start, sink, q_pos, out, lse, dout, W, 1.0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert torch.isfinite(a[3]).all()
+    dq, dkv, dxw = host(a[0])[0], host(a[1])[0], host(a[2])[0]
+    qh, Eh, xh = host(q)[0], host(E)[0], host(c["c_a"])[0]
+    doh, idxh, sk = host(dout)[0], host(idx)[0], host(sink)
+
+    def row_bwd(p):
+        sel = idxh[p][(idxh[p] >= 0) & (idxh[p] < N)]
+        rows = O.window_rows(p, W, 0, T)
+        keys = np.concatenate([Eh[sel], xh[rows]], 0)
+        dqr, dk, _ = O.attend_bwd(qh[p], keys, sk, doh[p], 1.0)
+        return sel, rows, dqr, dk
+
+    for p in (0, 1, 3, 4, 5, 130, 2047, 2048, 2049, 4099, 9000, 20000, 33333, 50000, 65534, 65535):
+        check_grad(dq[p], row_bwd(p)[2], f"dq row {p}")
+    counts = np.bincount(idxh[idxh >= 0], minlength=N)
+    for e in (int(np.argmin(np.abs(counts - 300))), int(np.argmin(np.abs(counts - 40)))):
+        want = np.zeros(128)
+        for p in np.nonzero((idxh == e).any(axis=1))[0]:
+            sel, _, _, dk = row_bwd(int(p))
+            want += dk[int(np.nonzero(sel == e)[0][0])]
+        _print(f"  entry {e}: selected by {counts[e]} rows")
+        check_grad(dkv[e], want, f"dkv entry {e}")
+    for t in (0, 40000, 65535):
+        want = np.zeros(128)
+        for p in range(t, min(T, t + W)):
+            sel, rows, _, dk = row_bwd(p)
+            want += dk[len(sel) + int(np.nonzero(rows == t)[0][0])]
+        check_grad(dxw[t], want, f"dx_win row {t}")
