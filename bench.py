@@ -344,8 +344,9 @@ def decode_append(torch, C, syn, iters):
     """Decode-time cache maintenance of the 1M-context layer pair, B = 8: each
     step appends one token per sequence to the CSA KV cache (bf16 entries), the
     CSA indexer-key cache (fp4 entries + E8M0 scales) and the HCA cache (bf16),
-    through their state rings. The positions end a 128-token block, so every
-    call writes a CSA entry and an HCA entry (the most work a step can do)."""
+    through their state rings, and each layer's new window row to its window
+    ring (128 rows). The positions end a 128-token block, so every call writes
+    a CSA entry and an HCA entry (the most work a step can do)."""
     dev, bf = "cuda", torch.bfloat16
     B, L, W = 8, 1 << 20, 128
     N, NH = L // 4, L // 128
@@ -359,10 +360,13 @@ def decode_append(torch, C, syn, iters):
     st_kv = syn.normal_device(s + 20, (B, 8, 4, W), dev, bf)
     st_ix = syn.normal_device(s + 21, (B, 8, 4, W), dev, bf)
     st_h = syn.normal_device(s + 22, (B, 128, 2, W), dev, bf)
+    win_csa = syn.normal_device(s + 23, (B, 128, W), dev, bf)
+    win_hca = syn.normal_device(s + 24, (B, 128, W), dev, bf)
     ops = [
         ("csa_kv", lambda: C.csa_compress_append(*rows[0:4], pos, st_kv, E, None, 4)),
         ("csa_index_keys_fp4", lambda: C.csa_compress_append(*rows[4:8], pos, st_ix, KI, KIs, 4)),
         ("hca", lambda: C.hca_compress_append(rows[8], rows[9], pos, st_h, EH, 128)),
+        ("window_rows", lambda: (C.window_append(rows[0], pos, win_csa), C.window_append(rows[8], pos, win_hca))),
     ]
     # device time per op and per step: 50 steps captured in one graph,
     # replayed (a single call is shorter than its host-side launch path, and a
@@ -392,7 +396,7 @@ def decode_append(torch, C, syn, iters):
     # HCA 127 tokens x 2 streams), the new rows read and written to the ring,
     # the entries written
     rb = W * 2
-    byts = B * (2 * (7 * 4 + 4 + 4) * rb + (127 * 2 + 2 + 2) * rb + rb + W // 2 + W // 32 + rb)
+    byts = B * (2 * (7 * 4 + 4 + 4) * rb + (127 * 2 + 2 + 2) * rb + rb + W // 2 + W // 32 + rb + 2 * 2 * rb)
     return {"workload": "decode_append_pair_1m_ctx", "batch": B, "context": L,
             "us": {k: round(v, 2) for k, v in t.items()}, "step_us": round(step, 2), "step_bytes": byts,
             "timing": "hip graph replay"}

@@ -254,7 +254,13 @@ csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, cons
  * Entries of idx outside [0, N) (e.g. -1 padding) are skipped.
  *   q      [B, Tq, H, d] of t (CSA_F32 or CSA_BF16)
  *   kv     [B, N, d] of t;   idx int32 [B, Tq, k]
- *   x_win  [B, T_win, d] of t;  win_start int32 [B] (position of row 0)
+ *   x_win  [B, T_win, d] of t;  win_start int32 [B]: the first position the
+ *          rows hold. win_ring = 0: position t is row t - win_start (rows
+ *          hold positions win_start .. win_start + T_win - 1 in order);
+ *          win_ring = 1: x_win is a ring of T_win rows (cf-1.com write-up §4.4:
+ *          the window of recent uncompressed tokens is kept as a state cache)
+ *          and position t is row t mod T_win, for the same positions
+ *          win_start .. win_start + T_win - 1 (csa_window_append keeps it).
  *   sink   float32 [H], or NULL for no sink
  *   q_pos  int32 [B, Tq];  out [B, Tq, H, d] of t;  lse NULL or float32 [B, Tq, H]
  *   d == 128; H a multiple of 16, <= 256; 1 <= k <= 4096; window >= 0; B*Tq < 2^31.
@@ -265,8 +271,9 @@ size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, i
 csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
                            const int32_t* win_start, const float* sink, const int32_t* q_pos,
                            csa_dtype t, int64_t B, int64_t Tq, int64_t N, int64_t T_win,
-                           int32_t H, int32_t d, int32_t k, int32_t window, float scale,
-                           void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                           int32_t win_ring, int32_t H, int32_t d, int32_t k, int32_t window,
+                           float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream);
 
 /*
  * dense_compressed_attn_fwd — HCA core attention: every visible compressed
@@ -280,9 +287,25 @@ size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, in
 csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* x_win,
                                      const int32_t* win_start, const float* sink,
                                      const int32_t* q_pos, csa_dtype t, int64_t B, int64_t Tq,
-                                     int64_t N, int64_t T_win, int32_t H, int32_t d,
-                                     int32_t ratio, int32_t window, float scale, void* out,
-                                     float* lse, void* ws, size_t ws_bytes, void* stream);
+                                     int64_t N, int64_t T_win, int32_t win_ring, int32_t H,
+                                     int32_t d, int32_t ratio, int32_t window, float scale,
+                                     void* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream);
+
+/*
+ * csa_window_append — one decode step of the window state cache (cf-1.com
+ * write-up §4.4: recent uncompressed tokens are kept in a state cache; §3.3:
+ * their KV forms the window branch): ring[b, pos[b] mod R] = x_new[b].
+ *   x_new  [B, d] of t (CSA_F32 or CSA_BF16): the new token's window row
+ *          (the raw KV vector that the attention reads as a window key)
+ *   pos    int32 [B] >= 0: the token's position
+ *   ring   [B, R, d] of t, caller-owned, R >= 1
+ * d == 128; x_new and ring 16-byte aligned. After appending position p with
+ * R >= window, pass x_win = ring, T_win = R, win_ring = 1 and
+ * win_start = max(0, p - R + 1) to the attention calls.
+ */
+csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t d,
+                             const int32_t* pos, void* ring, int64_t R, void* stream);
 
 /*
  * sparse_attn_bwd — gradients of sparse_attn_fwd (cf-1.com write-up §4.3:

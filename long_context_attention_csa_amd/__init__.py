@@ -8,4 +8,5 @@ from .ops import (batch_invariant, csa_append_state, csa_compress, csa_compress_
                   dense_compressed_attn_bwd, dense_compressed_attn_fwd, hca_append_state,
                   hca_compress, hca_compress_append, indexer_topk, indexer_topk_workspace_size,
                   kernel_timer_read, kernel_timer_start, set_batch_invariant, sparse_attn_bwd,
-                  sparse_attn_bwd_workspace_size, sparse_attn_fwd, sparse_attn_workspace_size)
+                  sparse_attn_bwd_workspace_size, sparse_attn_fwd, sparse_attn_workspace_size,
+                  window_append)

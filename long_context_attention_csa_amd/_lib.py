@@ -43,7 +43,7 @@ SIGNATURES = {
                                                 _I32, _I32, _P, _P, _P, _SZ, _P]),
     "sparse_attn_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
-                                       _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+                                       _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
     "sparse_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
                                        _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -52,7 +52,8 @@ SIGNATURES = {
                                                  _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dense_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
     "dense_compressed_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32,
-                                                 _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+                                                 _I32, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+    "csa_window_append": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _P, _P, _I64, _P]),
     "csa_set_batch_invariant": (ctypes.c_int, [_I32]),
     "csa_get_batch_invariant": (_I32, []),
     "csa_kernel_timer_start": (ctypes.c_int, [_I32, _I32]),

@@ -31,10 +31,12 @@ hipError_t launch_attn_bwd(bool sparse, const void* q, const void* kv, const int
                            float* dsink, void* ws, hipStream_t s);
 void set_batch_invariant(int on);
 int batch_invariant();
+hipError_t launch_window_append(const void* x_new, csa_dtype t, int64_t B, const int32_t* pos, void* ring,
+                                int64_t R, hipStream_t s);
 hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void* kv, const int32_t* idx,
                             const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
-                            int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio,
-                            float scale, void* out, float* lse, void* ws, int64_t nk_max, hipStream_t st);
+                            int64_t B, int64_t Tq, int64_t N, int64_t T_win, int ring, int H, int k, int window,
+                            int ratio, float scale, void* out, float* lse, void* ws, int64_t nk_max, hipStream_t st);
 
 // ------------------------------------------------------------------ kernel timer
 namespace {
@@ -299,19 +301,21 @@ size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, i
 
 csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
                            const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t, int64_t B,
-                           int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t k, int32_t window,
-                           float scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                           int64_t Tq, int64_t N, int64_t T_win, int32_t win_ring, int32_t H, int32_t d, int32_t k,
+                           int32_t window, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* stream) {
   g_last_error.clear();
   csa_status st = check_attn_common("sparse_attn_fwd", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win, H, d,
                                     window, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_SHAPE, "sparse_attn_fwd: k %d (1..4096)", k);
+  CSA_REQUIRE(win_ring == 0 || win_ring == 1, CSA_ERR_SHAPE, "sparse_attn_fwd: win_ring %d (0 or 1)", win_ring);
   if (B * Tq == 0) return CSA_OK;
   CSA_REQUIRE(idx, CSA_ERR_NULL, "sparse_attn_fwd: idx is NULL");
   const size_t need = sparse_attn_workspace_size(B, Tq, H, d, k, window);
   CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE, "sparse_attn_fwd: workspace %zu < %zu bytes",
               ws_bytes, need);
-  return hip_status(launch_attention(true, t, q, kv, idx, x_win, win_start, sink, q_pos, B, Tq, N, T_win, H, k,
+  return hip_status(launch_attention(true, t, q, kv, idx, x_win, win_start, sink, q_pos, B, Tq, N, T_win, win_ring, H, k,
                                      window, 1, scale, out, lse, need ? ws : nullptr, (int64_t)k + window,
                                      (hipStream_t)stream),
                     "sparse_attn_fwd");
@@ -325,21 +329,38 @@ size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, in
 
 csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* x_win, const int32_t* win_start,
                                      const float* sink, const int32_t* q_pos, csa_dtype t, int64_t B, int64_t Tq,
-                                     int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t ratio, int32_t window,
-                                     float scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                                     int64_t N, int64_t T_win, int32_t win_ring, int32_t H, int32_t d, int32_t ratio,
+                                     int32_t window, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                     void* stream) {
   g_last_error.clear();
   csa_status st = check_attn_common("dense_compressed_attn_fwd", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win,
                                     H, d, window, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "dense_compressed_attn_fwd: ratio %d", ratio);
+  CSA_REQUIRE(win_ring == 0 || win_ring == 1, CSA_ERR_SHAPE, "dense_compressed_attn_fwd: win_ring %d (0 or 1)",
+              win_ring);
   if (B * Tq == 0) return CSA_OK;
   const size_t need = dense_attn_workspace_size(B, Tq, N, H, d, window);
   CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
               "dense_compressed_attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(launch_attention(false, t, q, kv, nullptr, x_win, win_start, sink, q_pos, B, Tq, N, T_win, H, 0,
+  return hip_status(launch_attention(false, t, q, kv, nullptr, x_win, win_start, sink, q_pos, B, Tq, N, T_win, win_ring, H, 0,
                                      window, ratio, scale, out, lse, need ? ws : nullptr, N + window,
                                      (hipStream_t)stream),
                     "dense_compressed_attn_fwd");
+}
+
+csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t d, const int32_t* pos, void* ring,
+                             int64_t R, void* stream) {
+  g_last_error.clear();
+  CSA_REQUIRE(is_dtype(t) && is_float(t), CSA_ERR_UNSUPPORTED, "csa_window_append: dtype must be CSA_F32 or CSA_BF16");
+  CSA_REQUIRE(d == 128, CSA_ERR_UNSUPPORTED, "csa_window_append: d %d (only 128)", d);
+  CSA_REQUIRE(B >= 0 && R >= 1 && B * R < ((int64_t)1 << 40), CSA_ERR_SHAPE, "csa_window_append: B=%lld R=%lld",
+              (long long)B, (long long)R);
+  if (B == 0) return CSA_OK;
+  CSA_REQUIRE(x_new && pos && ring, CSA_ERR_NULL, "csa_window_append: NULL tensor");
+  CSA_REQUIRE(((uintptr_t)x_new & 15) == 0 && ((uintptr_t)ring & 15) == 0, CSA_ERR_SHAPE,
+              "csa_window_append: x_new and ring must be 16-byte aligned");
+  return hip_status(launch_window_append(x_new, t, B, pos, ring, R, (hipStream_t)stream), "csa_window_append");
 }
 
 static csa_status check_attn_bwd(const char* fn, const void* q, const void* kv, const void* x_win,

@@ -58,7 +58,7 @@ template <typename T, bool SPARSE, int NW, int HPW>
 __global__ __launch_bounds__(NW * 64) void k_attn(
     const T* __restrict__ q, const T* __restrict__ kv, const int32_t* __restrict__ idx, const T* __restrict__ x_win,
     const int32_t* __restrict__ win_start, const float* __restrict__ sink, const int32_t* __restrict__ q_pos,
-    int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale, int S,
+    int64_t Tq, int64_t N, int64_t T_win, int wring, int H, int k, int window, int ratio, float scale, int S,
     T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int KP = AttnTypes<T>::KP;
   constexpr int NT = NW * 64;
@@ -88,6 +88,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
   const int64_t chunk = (nk + S - 1) / S;
   const int64_t kbeg = (int64_t)sp * chunk;
   const int64_t kend = (kbeg + chunk) < nk ? (kbeg + chunk) : nk;
+  // row of window position lo: lo - w0, or lo mod T_win for a ring (a window
+  // of at most T_win rows wraps at most once)
+  const int64_t wrow0 = wring ? lo % (T_win > 0 ? T_win : 1) : lo - w0;
 
   // heads of this lane: h0 + 16 * hb + col
   const int h0 = hg * (NW * 16 * HPW) + wv * 16 * HPW;
@@ -140,7 +143,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
               const int64_t e = SPARSE ? (int64_t)sidx[kr] : ki;
               if (e >= 0 && e < N) src = kv + (b * N + e) * kD;
             } else {
-              src = x_win + (b * T_win + (lo + (ki - n_sel) - w0)) * kD;
+              int64_t wr = wrow0 + (ki - n_sel);
+              if (wr >= T_win) wr -= T_win;
+              src = x_win + (b * T_win + wr) * kD;
             }
           }
           okb[tt][pp][i] = src != nullptr;
@@ -423,8 +428,8 @@ template <bool SPARSE, int NW, int HPW, int NBUF, int TS>
 __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ x_win, const int32_t* __restrict__ win_start, const float* __restrict__ sink,
-    const int32_t* __restrict__ q_pos, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio,
-    float scale, int S, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    const int32_t* __restrict__ q_pos, int64_t Tq, int64_t N, int64_t T_win, int wring, int H, int k, int window,
+    int ratio, float scale, int S, uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   constexpr int NWT = NW * TS;                    // waves: TS streams of NW head waves
   constexpr int NT = NWT * 64;
@@ -486,6 +491,9 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
   const int64_t chunk = (nk + S - 1) / S;
   const int64_t kbeg = (int64_t)sp * chunk;
   const int64_t kend = (kbeg + chunk) < nk ? (kbeg + chunk) : nk;
+  // row of window position lo: lo - w0, or lo mod T_win for a ring (a window
+  // of at most T_win rows wraps at most once)
+  const int64_t wrow0 = wring ? lo % (T_win > 0 ? T_win : 1) : lo - w0;
 
   const int h0 = hg * QH + hw * 16 * HPW;
   // With two tile streams (short key ranges per block) the query rows go to
@@ -561,7 +569,9 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
         const int64_t e = SPARSE ? (int64_t)sidx[kk] : ki;
         return (e >= 0 && e < N) ? kvb + e * kD : nullptr;
       }
-      return xwb + (lo + (ki - n_sel) - w0) * kD;
+      int64_t wr = wrow0 + (ki - n_sel);
+      if (wr >= T_win) wr -= T_win;
+      return xwb + wr * kD;
     };
     auto issue = [&](int t) {
       const int slot = t % NBUF;
@@ -569,9 +579,12 @@ __global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
       const int kk0 = t * kKT;
       const int64_t t0k = c0 + kk0;
       bool bad = false;
-      if (kk0 + kKT <= clen && (t0k >= n_sel || (!SPARSE && t0k + kKT <= n_sel))) {
-        // the tile's keys are consecutive rows: window rows, or entries
-        const uint16_t* tb = t0k >= n_sel ? xwb + (lo + (t0k - n_sel) - w0) * kD : kvb + t0k * kD;
+      int64_t wt = wrow0 + (t0k - n_sel);   // window row of the tile's first key (window tiles)
+      if (wt >= T_win) wt -= T_win;
+      if (kk0 + kKT <= clen && ((t0k >= n_sel && wt + kKT <= T_win) || (!SPARSE && t0k + kKT <= n_sel))) {
+        // the tile's keys are consecutive rows: window rows (not wrapping
+        // around a ring), or entries
+        const uint16_t* tb = t0k >= n_sel ? xwb + wt * kD : kvb + t0k * kD;
 #pragma unroll
         for (int j = 0; j < LPT; ++j)
           gather_lds16(tb + grow[j] * kD + gcol[j], (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
@@ -843,34 +856,34 @@ constexpr int kRing2 = 6;  // ring slots with two tile streams (2 computed + 4 i
 template <typename T, bool SPARSE, int NW, int HPW>
 static void launch_attn_t(dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                           const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
-                          int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
-                          int S, bool two_streams, void* out, float* lse, float* po, float* pml) {
+                          int64_t Tq, int64_t N, int64_t T_win, int wring, int H, int k, int window, int ratio,
+                          float scale, int S, bool two_streams, void* out, float* lse, float* po, float* pml) {
   if constexpr (sizeof(T) == 2) {
     // Few rows (decode): two tile streams per block, two waves per SIMD.
     if (two_streams)
       k_attn16<SPARSE, NW, HPW, kRing2, 2><<<grid, NW * 2 * 64, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)x_win, win_start, sink, q_pos, Tq, N, T_win,
-          H, k, window, ratio, scale, S, (uint16_t*)out, lse, po, pml);
+          wring, H, k, window, ratio, scale, S, (uint16_t*)out, lse, po, pml);
     else
       k_attn16<SPARSE, NW, HPW, kRing, 1><<<grid, NW * 64, 0, st>>>(
           (const uint16_t*)q, (const uint16_t*)kv, idx, (const uint16_t*)x_win, win_start, sink, q_pos, Tq, N, T_win,
-          H, k, window, ratio, scale, S, (uint16_t*)out, lse, po, pml);
+          wring, H, k, window, ratio, scale, S, (uint16_t*)out, lse, po, pml);
   }
   else
     k_attn<T, SPARSE, NW, HPW><<<grid, NW * 64, 0, st>>>((const T*)q, (const T*)kv, idx, (const T*)x_win, win_start,
-                                                         sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S,
-                                                         (T*)out, lse, po, pml);
+                                                         sink, q_pos, Tq, N, T_win, wring, H, k, window, ratio, scale,
+                                                         S, (T*)out, lse, po, pml);
 }
 
 template <typename T, bool SPARSE>
 static void launch_attn_sh(AttnShape sh, dim3 grid, hipStream_t st, const void* q, const void* kv, const int32_t* idx,
                            const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
-                           int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio, float scale,
-                           int S, bool two_streams, void* out, float* lse, float* po, float* pml) {
+                           int64_t Tq, int64_t N, int64_t T_win, int wring, int H, int k, int window, int ratio,
+                           float scale, int S, bool two_streams, void* out, float* lse, float* po, float* pml) {
 #define CSA_ATTN_CASE(NW_, HPW_)                                                                               \
   if (sh.nw == NW_ && sh.hpw == HPW_) {                                                                        \
-    launch_attn_t<T, SPARSE, NW_, HPW_>(grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, \
-                                        k, window, ratio, scale, S, two_streams, out, lse, po, pml);           \
+    launch_attn_t<T, SPARSE, NW_, HPW_>(grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win,    \
+                                        wring, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);  \
     return;                                                                                                    \
   }
   CSA_ATTN_CASE(4, 2)
@@ -882,10 +895,39 @@ static void launch_attn_sh(AttnShape sh, dim3 grid, hipStream_t st, const void* 
 #undef CSA_ATTN_CASE
 }
 
+// One row of 128 elements per sequence into ring row pos mod R (16 bytes per thread).
+template <typename T>
+__global__ __launch_bounds__(256) void k_window_append(const T* __restrict__ x_new, int64_t B,
+                                                       const int32_t* __restrict__ pos, T* __restrict__ ring,
+                                                       int64_t R) {
+  constexpr int C = 16 / sizeof(T);                 // elements per 16-byte chunk
+  constexpr int CPR = kD / C;                       // chunks per row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= B * CPR) return;
+  const int64_t b = i / CPR, c = i % CPR;
+  const int64_t row = (int64_t)((uint32_t)pos[b] % (uint64_t)R);
+  *reinterpret_cast<i32x4*>(ring + (b * R + row) * kD + c * C) =
+      *reinterpret_cast<const i32x4*>(x_new + b * kD + c * C);
+}
+
+hipError_t launch_window_append(const void* x_new, csa_dtype t, int64_t B, const int32_t* pos, void* ring,
+                                int64_t R, hipStream_t s) {
+  if (t == CSA_BF16) {
+    const int64_t n = B * (kD / 8);
+    k_window_append<uint16_t><<<(unsigned)cdiv(n, 256), 256, 0, s>>>(static_cast<const uint16_t*>(x_new), B, pos,
+                                                                      static_cast<uint16_t*>(ring), R);
+  } else {
+    const int64_t n = B * (kD / 4);
+    k_window_append<float><<<(unsigned)cdiv(n, 256), 256, 0, s>>>(static_cast<const float*>(x_new), B, pos,
+                                                                   static_cast<float*>(ring), R);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void* kv, const int32_t* idx,
                             const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
-                            int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window, int ratio,
-                            float scale, void* out, float* lse, void* ws, int64_t nk_max, hipStream_t st) {
+                            int64_t B, int64_t Tq, int64_t N, int64_t T_win, int wring, int H, int k, int window,
+                            int ratio, float scale, void* out, float* lse, void* ws, int64_t nk_max, hipStream_t st) {
   const int64_t rows = B * Tq;
   if (rows == 0) return hipSuccess;
   const AttnShape sh = pick_shape(H);
@@ -900,11 +942,11 @@ hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void*
   const int kid = sparse ? CSA_KID_SPARSE_ATTN : CSA_KID_DENSE_ATTN;
   timer_before(kid, st);
   if (t == CSA_BF16) {
-    if (sparse) launch_attn_sh<uint16_t, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
-    else launch_attn_sh<uint16_t, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
+    if (sparse) launch_attn_sh<uint16_t, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, wring, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
+    else launch_attn_sh<uint16_t, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, wring, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
   } else {
-    if (sparse) launch_attn_sh<float, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
-    else launch_attn_sh<float, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
+    if (sparse) launch_attn_sh<float, true>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, wring, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
+    else launch_attn_sh<float, false>(sh, grid, st, q, kv, idx, x_win, win_start, sink, q_pos, Tq, N, T_win, wring, H, k, window, ratio, scale, S, two_streams, out, lse, po, pml);
   }
   hipError_t e = hipGetLastError();
   timer_after(kid, st);

@@ -182,9 +182,10 @@ def sparse_attn_workspace_size(B, Tq, H, d, k, window) -> int:
 
 
 def sparse_attn_fwd(q, kv, idx, x_win, win_start, sink, q_pos, window: int = 128, scale: float = 1.0,
-                    want_lse: bool = False, ws=None, out=None):
+                    want_lse: bool = False, ws=None, out=None, win_ring: bool = False):
     """CSA core attention. q [B, Tq, H, d], kv [B, N, d], idx int32 [B, Tq, k],
-    x_win [B, T_win, d], win_start int32 [B], sink float32 [H] or None, q_pos int32 [B, Tq]."""
+    x_win [B, T_win, d], win_start int32 [B], sink float32 [H] or None, q_pos int32 [B, Tq].
+    win_ring: x_win is a ring holding position t at row t mod T_win."""
     _contig(q, kv, idx, x_win, win_start, sink, q_pos)
     t = _float_dtype(q)
     B, Tq, H, d = q.shape
@@ -194,7 +195,8 @@ def sparse_attn_fwd(q, kv, idx, x_win, win_start, sink, q_pos, window: int = 128
     lse = torch.empty(B, Tq, H, dtype=torch.float32, device=q.device) if want_lse else None
     ws, nbytes = _workspace(sparse_attn_workspace_size(B, Tq, H, d, k, window), q.device, ws)
     check("sparse_attn_fwd", lib().sparse_attn_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(x_win), _ptr(win_start),
-                                                   _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H, d, k, window,
+                                                   _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, int(win_ring), H, d,
+                                                   k, window,
                                                    scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
     return (out, lse) if want_lse else out
 
@@ -204,7 +206,7 @@ def dense_attn_workspace_size(B, Tq, N, H, d, window) -> int:
 
 
 def dense_compressed_attn_fwd(q, kv, x_win, win_start, sink, q_pos, ratio: int = 128, window: int = 128,
-                              scale: float = 1.0, want_lse: bool = False, ws=None, out=None):
+                              scale: float = 1.0, want_lse: bool = False, ws=None, out=None, win_ring: bool = False):
     """HCA core attention over all visible entries plus window and sink."""
     _contig(q, kv, x_win, win_start, sink, q_pos)
     t = _float_dtype(q)
@@ -215,8 +217,8 @@ def dense_compressed_attn_fwd(q, kv, x_win, win_start, sink, q_pos, ratio: int =
     lse = torch.empty(B, Tq, H, dtype=torch.float32, device=q.device) if want_lse else None
     ws, nbytes = _workspace(dense_attn_workspace_size(B, Tq, N, H, d, window), q.device, ws)
     check("dense_compressed_attn_fwd", lib().dense_compressed_attn_fwd(
-        _ptr(q), _ptr(kv), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H, d, ratio,
-        window, scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
+        _ptr(q), _ptr(kv), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, int(win_ring), H,
+        d, ratio, window, scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
     return (out, lse) if want_lse else out
 
 
@@ -270,6 +272,16 @@ def dense_compressed_attn_bwd(q, kv, x_win, win_start, sink, q_pos, out, lse, do
         window, scale, _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv), _ptr(dxw), _ptr(dsink), _ptr(ws),
         nbytes, _stream()))
     return dq, dkv, dxw, dsink
+
+
+def window_append(x_new, pos, ring):
+    """Write each sequence's new window row x_new [B, d] into ring [B, R, d] at row pos mod R."""
+    _contig(x_new, pos, ring)
+    t = _float_dtype(x_new)
+    B, d = x_new.shape
+    check("csa_window_append", lib().csa_window_append(_ptr(x_new), t, B, d, _ptr(pos), _ptr(ring), ring.shape[1],
+                                                       _stream()))
+    return ring
 
 
 def kernel_timer_start(kernel: str, max_launches: int) -> None:

@@ -113,10 +113,11 @@ def test_indexer_bf16_scores_validation():
 def test_attention_validation():
     lib = _lib.lib()
     f = lib.sparse_attn_fwd
-    base = [P, P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 64, 128, 1.0, P, None, P, 1 << 40, None]
+    #       q  kv idx xw ws0 sink pos t  B  Tq N   T_win ring H   d    k   win  scale out lse ws  wsb      stream
+    base = [P, P, P, P, P, None, P, 1, 1, 1, 64, 128, 0, 64, 128, 64, 128, 1.0, P, None, P, 1 << 40, None]
     def call(**kw):
         a = list(base)
-        pos = {"t": 7, "H": 12, "d": 13, "k": 14, "window": 15, "q": 0, "ws": 19, "wsb": 20, "idx": 2}
+        pos = {"t": 7, "ring": 12, "H": 13, "d": 14, "k": 15, "window": 16, "q": 0, "ws": 20, "wsb": 21, "idx": 2}
         for k_, v in kw.items():
             a[pos[k_]] = v
         return f(*a)
@@ -125,14 +126,27 @@ def test_attention_validation():
     assert call(t=2) == UNSUP
     assert call(k=0) == SHAPE
     assert call(window=-1) == SHAPE
+    assert call(ring=2) == SHAPE
     assert call(q=None) == NULL
     assert call(idx=None) == NULL
     g = lib.dense_compressed_attn_fwd
-    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 0, 128, 1.0, P, None, P, 1 << 40, None) == SHAPE
+    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, 0, 64, 128, 0, 128, 1.0, P, None, P, 1 << 40, None) == SHAPE
+    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, -1, 64, 128, 4, 128, 1.0, P, None, P, 1 << 40, None) == SHAPE
     # decode shapes need a split workspace
     need = lib.dense_attn_workspace_size(1, 1, 8192, 128, 128, 128)
     assert need > 0
-    assert g(P, P, P, P, None, P, 1, 1, 1, 8192, 128, 128, 128, 128, 128, 1.0, P, None, None, 0, None) == WS
+    assert g(P, P, P, P, None, P, 1, 1, 1, 8192, 128, 1, 128, 128, 128, 128, 1.0, P, None, None, 0, None) == WS
+
+
+def test_window_append_validation():
+    lib = _lib.lib()
+    f = lib.csa_window_append
+    assert f(P, 2, 2, 128, P, P, 128, None) == UNSUP         # fp8 rows
+    assert f(P, 1, 2, 64, P, P, 128, None) == UNSUP          # d != 128
+    assert f(P, 1, 2, 128, P, P, 0, None) == SHAPE           # empty ring
+    assert f(None, 1, 2, 128, P, P, 128, None) == NULL
+    assert f(ctypes.c_void_p(0x1008), 1, 2, 128, P, P, 128, None) == SHAPE   # misaligned
+    assert f(P, 1, 0, 128, None, None, 128, None) == OK      # B = 0: nothing to do
 
 
 def test_timer_validation():
