@@ -185,3 +185,19 @@ def test_batch_invariant_switch():
         ops.set_batch_invariant(False)
     assert not ops.batch_invariant()
     assert ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128) == default8
+
+
+def test_backward_workspace_passes():
+    """The backward's workspace holds at most 4 GiB of per-(query, key)
+    gradient rows: it grows with the query rows until that budget, then the
+    rows run in passes and the workspace stays bounded."""
+    lib = _lib.lib()
+    ws = lambda Tq: lib.sparse_attn_bwd_workspace_size(1, Tq, 16384, Tq, 64, 128, 512, 128)
+    small, mid, big = ws(64), ws(4096), ws(65536)
+    assert 0 < small < mid < big
+    assert mid >= 4096 * 640 * 512                     # every row's slots fit one pass
+    assert big < 5 * (1 << 30)                          # 65,536 rows: passes, bounded buffer
+    assert lib.sparse_attn_bwd_workspace_size(0, 1, 16, 16, 64, 128, 8, 128) == 0
+    d = lambda Tq: lib.dense_attn_bwd_workspace_size(1, Tq, 65536, 256, 64, 128, 128)
+    # one pass holds 64 rows of 65,664 slots; more rows add passes, not buffer (beyond per-row sink terms)
+    assert d(64) > 64 * 65536 * 512 and d(256) - d(64) < 1 << 20
