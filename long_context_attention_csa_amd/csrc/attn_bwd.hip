@@ -218,6 +218,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_place(const int32_t* __rest
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+
+// Swizzle of the 8-byte units of a P / dl row (64 keys, 128 bytes): unit u of
+// row x sits at u ^ pdl_swz(x & 15), the row's two 2-bit halves swapped. The
+// writes (16 consecutive rows, one unit) and the transposed reads (4
+// consecutive rows x 4 adjacent units) then each touch 16 distinct units.
+__device__ __forceinline__ int pdl_swz(int x) { return ((x & 3) << 2) | ((x >> 2) & 3); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // One block per query row, 4 waves; H = 64 HPW heads, wave w owns heads
@@ -242,7 +248,7 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   constexpr float kLog2e = 1.4426950408889634f;
   // key tile and the Q / dO rows: rows of 256 B, 16-byte chunk c of row x at
   // position c ^ (x & 15); P and dl: rows (heads) of 64 keys, 8-byte unit u
-  // of row x at u ^ (x & 15)
+  // of row x at u ^ pdl_swz(x & 15)
   __shared__ __align__(16) uint16_t kt[kKT * kD];
   __shared__ __align__(16) uint16_t qt[H * kD];
   __shared__ __align__(16) uint16_t ot[H * kD];
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
     const int trow = 4 * g + (col >> 2);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      gb[nb] = (uint32_t)trow * 128u + 8u * (uint32_t)((4 * nb + (col & 3)) ^ trow);
+      gb[nb] = (uint32_t)trow * 128u + 8u * (uint32_t)((4 * nb + (col & 3)) ^ pdl_swz(trow));
       opaque(gb[nb]);
     }
   }
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
       const int hh = h0 + 16 * hb + col;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t o = (uint32_t)hh * 128u + 8u * (uint32_t)((4 * kb + g) ^ (hh & 15));
+        const uint32_t o = (uint32_t)hh * 128u + 8u * (uint32_t)((4 * kb + g) ^ pdl_swz(hh & 15));
         *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(pl) + o) =
             make_uint2(cvt_pk_bf16(s[hb][kb][0], s[hb][kb][1]), cvt_pk_bf16(s[hb][kb][2], s[hb][kb][3]));
         *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(dll) + o) =
