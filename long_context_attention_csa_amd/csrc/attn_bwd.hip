@@ -310,28 +310,32 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   // tid % 16. The selected indices of its rows are loaded one tile ahead of
   // the rows themselves, so a row load never waits for its index load.
   const int crow = tid >> 4, cch = tid & 15;
+  // Branch-free: every load reads a valid address (the index clamped to the
+  // row; a slot without a key reads the query's own row, finite, masked later).
   auto load_idx = [&](int64_t t, int32_t (&e)[4]) {
+    if constexpr (SPARSE) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t kk = t * kKT + 16 * j + crow;
-      e[j] = (SPARSE && kk < w.n_sel) ? idx[r * k + kk] : 0;
+      for (int j = 0; j < 4; ++j) {
+        const int64_t kk = t * kKT + 16 * j + crow;
+        e[j] = idx[r * k + (kk < k ? kk : (int64_t)k - 1)];
+      }
     }
   };
+  const uint16_t* dummy = q + r * H * kD;
   i32x4 kr[4];
   bool kok[4];
   auto load_tile = [&](int64_t t, const int32_t (&e)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t kk = t * kKT + 16 * j + crow;
-      const uint16_t* src = nullptr;
-      if (kk < w.n_sel) {
-        const int64_t en = SPARSE ? (int64_t)e[j] : kk;
-        if (en >= 0 && en < N) src = kvb + en * kD;
-      } else if (kk < nk) {
-        src = xwb + (w.lo + (kk - w.n_sel) - w.w0) * kD;
-      }
-      kok[j] = src != nullptr;
-      kr[j] = src ? *reinterpret_cast<const i32x4*>(src + cch * 8) : i32x4{0, 0, 0, 0};
+      const bool in_sel = kk < w.n_sel;
+      const int64_t en = SPARSE ? (int64_t)e[j] : kk;
+      const bool ok_sel = in_sel && en >= 0 && en < N;
+      const bool ok_win = !in_sel && kk < nk;
+      const int64_t wr = w.lo + (kk - w.n_sel) - w.w0;
+      const uint16_t* src = ok_sel ? kvb + en * kD : (ok_win ? xwb + wr * kD : dummy);
+      kok[j] = ok_sel || ok_win;
+      kr[j] = *reinterpret_cast<const i32x4*>(src + cch * 8);
     }
   };
 
@@ -382,7 +386,8 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t kk = t * kKT + 16 * nb + col;
-      pv[nb] = kk < nk ? prow[kk] : -1;
+      const int32_t v = prow[kk < nk ? kk : nk - 1];
+      pv[nb] = kk < nk ? v : -1;
     }
     __syncthreads();
     if (t + 1 < ntiles) {
