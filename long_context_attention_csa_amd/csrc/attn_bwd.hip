@@ -224,6 +224,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 // writes (16 consecutive rows, one unit) and the transposed reads (4
 // consecutive rows x 4 adjacent units) then each touch 16 distinct units.
 __device__ __forceinline__ int pdl_swz(int x) { return ((x & 3) << 2) | ((x >> 2) & 3); }
+
+// 8-byte LDS store at a byte address.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+__device__ __forceinline__ void lds_write_b64(uint32_t a, uint32_t lo, uint32_t hi) {
+  *(lds_u32x2*)(size_t)a = u32x2_t{lo, hi};
+}
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // One block per query row, 4 waves; H = 64 HPW heads, wave w owns heads
@@ -246,15 +253,16 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
     uint16_t* __restrict__ dq, float* __restrict__ dsink_part) {
   constexpr int H = 64 * HPW;
   constexpr float kLog2e = 1.4426950408889634f;
-  // key tile and the Q / dO rows: rows of 256 B, 16-byte chunk c of row x at
-  // position c ^ (x & 15); P and dl: rows (heads) of 64 keys, 8-byte unit u
-  // of row x at u ^ pdl_swz(x & 15)
-  __shared__ __align__(16) uint16_t kt[kKT * kD];
+  // Key tiles (a 2-slot ring filled by asynchronous gathers) and the Q / dO
+  // rows: rows of 256 B, 16-byte chunk c of row x at position c ^ (x & 15).
+  // P and dl: rows (heads) of 64 keys, 8-byte unit u of row x at
+  // u ^ pdl_swz(x & 15); with 64 heads they take the key slot of their tile
+  // once its keys are consumed (16 KB), so two blocks fit a compute unit.
+  __shared__ __align__(16) uint16_t ring[2][kKT * kD];
   __shared__ __align__(16) uint16_t qt[H * kD];
   __shared__ __align__(16) uint16_t ot[H * kD];
-  __shared__ __align__(16) uint16_t pl[H * kKT];
-  __shared__ __align__(16) uint16_t dll[H * kKT];
-  __shared__ __align__(4) uint8_t kval[kKT];
+  __shared__ __align__(16) uint16_t pdl_sep[HPW == 1 ? 8 : 2 * H * kKT];
+  __shared__ __align__(4) uint8_t kval[2][kKT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -265,12 +273,15 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   const int64_t nk = w.n_sel + w.n_win;
   const int h0 = wv * 16 * HPW;
 
-  for (int j = tid; j < H * 16; j += kBwdThreads) {
-    const int h = j >> 4, c = j & 15;
-    const int pos = c ^ (h & 15);
-    *reinterpret_cast<i32x4*>(qt + h * kD + pos * 8) = *reinterpret_cast<const i32x4*>(q + (r * H + h) * kD + c * 8);
-    *reinterpret_cast<i32x4*>(ot + h * kD + pos * 8) =
-        *reinterpret_cast<const i32x4*>(dout + (r * H + h) * kD + c * 8);
+  // Q and dO rows (one per head) by asynchronous gathers, laid out like key
+  // tiles: instruction i of wave wv fills rows (4 i + wv) 4 .. + 3, lane
+  // row + lane / 16, chunk position lane % 16 (source chunk (lane % 16) ^ (row % 16)).
+#pragma unroll
+  for (int i = 0; i < H / 16; ++i) {
+    const int hr = (4 * i + wv) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (hr & 15);
+    gather_lds16(q + (r * H + hr) * kD + c * 8, (uint32_t)(uintptr_t)(qt + (4 * i + wv) * 4 * kD));
+    gather_lds16(dout + (r * H + hr) * kD + c * 8, (uint32_t)(uintptr_t)(ot + (4 * i + wv) * 4 * kD));
   }
 
   // Q and dO fragments (B operands of S^T, dP^T), D_h, lse, sink term.
@@ -306,36 +317,37 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 
   const uint16_t* kvb = kv + w.b * N * kD;
   const uint16_t* xwb = x_win + w.b * T_win * kD;
-  // A thread loads chunks 256 j + tid of a tile: row 16 j + tid / 16, chunk
-  // tid % 16. The selected indices of its rows are loaded one tile ahead of
-  // the rows themselves, so a row load never waits for its index load.
-  const int crow = tid >> 4, cch = tid & 15;
-  // Branch-free: every load reads a valid address (the index clamped to the
-  // row; a slot without a key reads the query's own row, finite, masked later).
+  // A key tile's gathers: instruction j of wave wv fills rows 16 j + grow0
+  // (grow0 = 4 wv + lane / 16) as above; the selected indices of a thread's
+  // rows are loaded a tile ahead of the gathers. Branch-free: every access is
+  // valid (the index clamped to the row; a slot without a key reads the
+  // query's own row, finite and masked later). Exactly 4 index loads and 4
+  // gathers per call, which the wait counts below rely on.
+  const int grow0 = 4 * wv + (lane >> 4);
   auto load_idx = [&](int64_t t, int32_t (&e)[4]) {
     if constexpr (SPARSE) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t kk = t * kKT + 16 * j + crow;
+        const int64_t kk = t * kKT + 16 * j + grow0;
         e[j] = idx[r * k + (kk < k ? kk : (int64_t)k - 1)];
       }
     }
   };
   const uint16_t* dummy = q + r * H * kD;
-  i32x4 kr[4];
-  bool kok[4];
-  auto load_tile = [&](int64_t t, const int32_t (&e)[4]) {
+  auto issue = [&](int64_t t, const int32_t (&e)[4]) {
+    const int sl = (int)(t & 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t kk = t * kKT + 16 * j + crow;
+      const int row = 16 * j + grow0;
+      const int64_t kk = t * kKT + row;
       const bool in_sel = kk < w.n_sel;
       const int64_t en = SPARSE ? (int64_t)e[j] : kk;
       const bool ok_sel = in_sel && en >= 0 && en < N;
       const bool ok_win = !in_sel && kk < nk;
       const int64_t wr = w.lo + (kk - w.n_sel) - w.w0;
       const uint16_t* src = ok_sel ? kvb + en * kD : (ok_win ? xwb + wr * kD : dummy);
-      kok[j] = ok_sel || ok_win;
-      kr[j] = *reinterpret_cast<const i32x4*>(src + cch * 8);
+      gather_lds16(src + (((lane & 15) ^ (row & 15)) * 8), (uint32_t)(uintptr_t)(ring[sl] + (4 * j + wv) * 4 * kD));
+      if ((lane & 15) == 0) kval[sl][row] = (ok_sel || ok_win) ? 1 : 0;
     }
   };
 
@@ -345,9 +357,7 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 #pragma unroll
     for (int db = 0; db < kD / 16; ++db) dQ[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint32_t tb = (uint32_t)(uintptr_t)kt;
   const uint32_t qtb = (uint32_t)(uintptr_t)qt, otb = (uint32_t)(uintptr_t)ot;
-  const uint32_t plb = (uint32_t)(uintptr_t)pl, dlb = (uint32_t)(uintptr_t)dll;
   const int64_t ntiles = cdiv(nk, kKT);
   const int32_t* prow = posbuf + (r - r0) * smax;
   // Tile-invariant LDS offsets of the G^T operands: the transposed reads of
@@ -371,28 +381,31 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   {
     int32_t e0[4];
     load_idx(0, e0);
-    if (ntiles > 0) load_tile(0, e0);
+    if (ntiles > 0) issue(0, e0);
     load_idx(1, e_next);
   }
   for (int64_t t = 0; t < ntiles; ++t) {
-    __syncthreads();   // the previous tile's reads of kt, pl, dl are done
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * j + crow;
-      *reinterpret_cast<i32x4*>(kt + row * kD + ((cch ^ (row & 15)) * 8)) = kr[j];
-      if (cch == 0) kval[row] = kok[j] ? 1 : 0;
+    const int sl = (int)(t & 1);
+    // Tile t's gathers are complete: the vector memory operations issued after
+    // them are its 4 index loads (sparse), the previous tile's 4 position loads
+    // and at most 8 stores, completed in order, so at most that many pending
+    // ones leave none of the gathers outstanding (tile 0: the prologue's index
+    // loads only; the Q / dO gathers are older still). The barrier then also
+    // means every wave is past the previous tile's use of the other slot.
+    if (t == 0) wait_vm<SPARSE ? 4 : 0>();
+    else wait_vm<SPARSE ? 8 : 4>();
+    __syncthreads();
+    if (t + 1 < ntiles) {
+      issue(t + 1, e_next);
+      load_idx(t + 2, e_next);
     }
+    const uint32_t tb = (uint32_t)(uintptr_t)ring[sl];
     int32_t pv[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t kk = t * kKT + 16 * nb + col;
       const int32_t v = prow[kk < nk ? kk : nk - 1];
       pv[nb] = kk < nk ? v : -1;
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      load_tile(t + 1, e_next);
-      load_idx(t + 2, e_next);
     }
 
     // ---- S^T = K Q^T and dP^T = K dO^T (keys 16 kb + 4 g + rr, head column col)
@@ -436,7 +449,7 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
     {
       uint32_t okw[4];    // byte rr of word kb: key 16 kb + 4 g + rr holds a key
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) okw[kb] = reinterpret_cast<const uint32_t*>(kval)[4 * kb + g];
+      for (int kb = 0; kb < 4; ++kb) okw[kb] = reinterpret_cast<const uint32_t*>(kval[sl])[4 * kb + g];
 #pragma unroll
       for (int hb = 0; hb < HPW; ++hb)
 #pragma unroll
@@ -479,17 +492,19 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
         }
       }
     }
-    // ---- P and scale * dl to LDS, [head][key]
+    // ---- P and scale * dl to LDS, [head][key] (64 heads: into this tile's key
+    // slot, once every wave is done with its keys)
+    if constexpr (HPW == 1) __syncthreads();
+    const uint32_t plb = HPW == 1 ? tb : (uint32_t)(uintptr_t)pdl_sep;
+    const uint32_t dlb = plb + (uint32_t)(H * kKT * 2);
 #pragma unroll
     for (int hb = 0; hb < HPW; ++hb) {
       const int hh = h0 + 16 * hb + col;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const uint32_t o = (uint32_t)hh * 128u + 8u * (uint32_t)((4 * kb + g) ^ pdl_swz(hh & 15));
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(pl) + o) =
-            make_uint2(cvt_pk_bf16(s[hb][kb][0], s[hb][kb][1]), cvt_pk_bf16(s[hb][kb][2], s[hb][kb][3]));
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(dll) + o) =
-            make_uint2(cvt_pk_bf16(dp[hb][kb][0], dp[hb][kb][1]), cvt_pk_bf16(dp[hb][kb][2], dp[hb][kb][3]));
+        lds_write_b64(plb + o, cvt_pk_bf16(s[hb][kb][0], s[hb][kb][1]), cvt_pk_bf16(s[hb][kb][2], s[hb][kb][3]));
+        lds_write_b64(dlb + o, cvt_pk_bf16(dp[hb][kb][0], dp[hb][kb][1]), cvt_pk_bf16(dp[hb][kb][2], dp[hb][kb][3]));
       }
     }
     __syncthreads();
