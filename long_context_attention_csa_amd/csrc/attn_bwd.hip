@@ -31,6 +31,8 @@
 //   k_bwd_scan_*       exclusive prefix of the totals over keys: list offsets
 //   k_bwd_place        per chunk, query by query: the position of each slot
 //   k_attn_bwd16       per query: dq, the slot gradients G, the sink terms
+//                      (D = dO . O per row and head comes from k_bwd_delta, run
+//                      once before the passes)
 //   k_bwd_reduce       per key: sum of its contributions in list order
 // and once at the end k_bwd_sink_part / k_bwd_sink_final (sink gradient over
 // all rows in a fixed order).
@@ -217,7 +219,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_place(const int32_t* __rest
   }
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 
 // Swizzle of the 8-byte units of a P / dl row (64 keys, 128 bytes): unit u of
 // row x sits at u ^ pdl_swz(x & 15), the row's two 2-bit halves swapped. The
@@ -231,7 +232,28 @@ typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
 __device__ __forceinline__ void lds_write_b64(uint32_t a, uint32_t lo, uint32_t hi) {
   *(lds_u32x2*)(size_t)a = u32x2_t{lo, hi};
 }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// D[r, h] = dO[r, h] . O[r, h] for every (row, head): 16 lanes per pair,
+// 8 elements each, summed over the 16 lanes by xor-shuffles (fixed order).
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_delta(const uint16_t* __restrict__ out,
+                                                           const uint16_t* __restrict__ dout, int64_t pairs,
+                                                           float* __restrict__ D) {
+  const int64_t pr = (int64_t)blockIdx.x * (kBwdThreads / 16) + (threadIdx.x >> 4);
+  const int l = threadIdx.x & 15;
+  float acc = 0.f;
+  if (pr < pairs) {
+    const i32x4 a = *reinterpret_cast<const i32x4*>(dout + pr * kD + 8 * l);
+    const i32x4 o = *reinterpret_cast<const i32x4*>(out + pr * kD + 8 * l);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float((uint32_t)a[e] << 16), __uint_as_float((uint32_t)o[e] << 16), acc);
+      acc = fmaf(__uint_as_float((uint32_t)a[e] & 0xffff0000u), __uint_as_float((uint32_t)o[e] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m);
+  if (pr < pairs && l == 0) D[pr] = acc;
+}
 
 // One block per query row, 4 waves; H = 64 HPW heads, wave w owns heads
 // [16 HPW w, 16 HPW (w + 1)) for the products over d and the d blocks
@@ -247,7 +269,7 @@ template <bool SPARSE, int HPW>
 __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ x_win, const int32_t* __restrict__ win_start, const float* __restrict__ sink,
-    const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ out, const float* __restrict__ lse,
+    const int32_t* __restrict__ q_pos, const float* __restrict__ Dv, const float* __restrict__ lse,
     const uint16_t* __restrict__ dout, int64_t r0, int64_t Tq, int64_t N, int64_t T_win, int k, int window,
     int ratio, float scale, const int32_t* __restrict__ posbuf, int64_t smax, float* __restrict__ G,
     uint16_t* __restrict__ dq, float* __restrict__ dsink_part) {
@@ -291,22 +313,12 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 #pragma unroll
   for (int hb = 0; hb < HPW; ++hb) {
     const int64_t hrow = r * H + h0 + 16 * hb + col;
-    float acc = 0.f;
 #pragma unroll
     for (int ks = 0; ks < kD / 32; ++ks) {
       qf[hb][ks].load(q + hrow * kD + 32 * ks + 8 * g);
       df[hb][ks].load(dout + hrow * kD + 32 * ks + 8 * g);
-      Frag<uint16_t> of;
-      of.load(out + hrow * kD + 32 * ks + 8 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a = (uint32_t)df[hb][ks].v[e], o = (uint32_t)of.v[e];
-        acc = fmaf(bf16_lo(a), bf16_lo(o), acc);
-        acc = fmaf(bf16_hi(a), bf16_hi(o), acc);
-      }
     }
-    acc += __shfl_xor(acc, 16);
-    acc += __shfl_xor(acc, 32);
+    const float acc = Dv[hrow];
     Dh[hb] = acc;
     const float L = lse[hrow];
     live[hb] = L > -INFINITY;
@@ -652,7 +664,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_sink_final(const float* __r
 
 struct BwdPlan {
   int64_t rows, smax, rows_pass, nchunks, nids, nscan;
-  size_t o_cnt, o_total, o_off, o_bsum, o_pos, o_g, o_sink, o_spart, bytes;
+  size_t o_cnt, o_total, o_off, o_bsum, o_pos, o_g, o_sink, o_spart, o_delta, bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -678,6 +690,7 @@ static BwdPlan bwd_plan(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T
   p.o_g = o;     o += align256((size_t)p.rows_pass * p.smax * kD * 4);
   p.o_sink = o;  o += align256((size_t)p.rows * H * 4);
   p.o_spart = o; o += align256((size_t)kSinkBlocks * H * 4);
+  p.o_delta = o; o += align256((size_t)p.rows * H * 4);
   p.bytes = o;
   return p;
 }
@@ -707,6 +720,8 @@ static hipError_t run_attn_bwd(const uint16_t* q, const uint16_t* kv, const int3
   int32_t* pos = reinterpret_cast<int32_t*>(wb + p.o_pos);
   float* G = reinterpret_cast<float*>(wb + p.o_g);
   float* spart = reinterpret_cast<float*>(wb + p.o_sink);
+  float* delta = reinterpret_cast<float*>(wb + p.o_delta);
+  k_bwd_delta<<<(unsigned)cdiv(p.rows * H, kBwdThreads / 16), kBwdThreads, 0, s>>>(out, dout, p.rows * H, delta);
   for (int64_t r0 = 0; r0 < p.rows; r0 += p.rows_pass) {
     const int64_t r1 = r0 + p.rows_pass < p.rows ? r0 + p.rows_pass : p.rows;
     const int64_t nr = r1 - r0;
@@ -722,11 +737,11 @@ static hipError_t run_attn_bwd(const uint16_t* q, const uint16_t* kv, const int3
                                                               window, ratio, p.nids, cnt, off, pos, p.smax);
     timer_before(CSA_KID_ATTN_BWD, s);
     if (H == 64)
-      k_attn_bwd16<SPARSE, 1><<<(unsigned)nr, kBwdThreads, 0, s>>>(q, kv, idx, x_win, win_start, sink, q_pos, out,
+      k_attn_bwd16<SPARSE, 1><<<(unsigned)nr, kBwdThreads, 0, s>>>(q, kv, idx, x_win, win_start, sink, q_pos, delta,
                                                                   lse, dout, r0, Tq, N, T_win, k, window, ratio,
                                                                   scale, pos, p.smax, G, dq, spart);
     else
-      k_attn_bwd16<SPARSE, 2><<<(unsigned)nr, kBwdThreads, 0, s>>>(q, kv, idx, x_win, win_start, sink, q_pos, out,
+      k_attn_bwd16<SPARSE, 2><<<(unsigned)nr, kBwdThreads, 0, s>>>(q, kv, idx, x_win, win_start, sink, q_pos, delta,
                                                                   lse, dout, r0, Tq, N, T_win, k, window, ratio,
                                                                   scale, pos, p.smax, G, dq, spart);
     hipError_t e = hipGetLastError();
