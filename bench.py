@@ -583,8 +583,8 @@ def main():
                          "transfer for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); multi-GPU runs are not part of "
-              "this build. Run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the sharded path exists only as "
+              "a design. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
