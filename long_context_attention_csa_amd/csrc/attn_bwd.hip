@@ -34,6 +34,9 @@
 //                      (D = dO . O per row and head comes from k_bwd_delta, run
 //                      once before the passes)
 //   k_bwd_reduce       per key: sum of its contributions in list order
+// Dense layers take contributions for their window rows only; the entries'
+// gradients come from k_attn_bwd_dense_kv (per block of entries and segment
+// of query rows, summed in registers) and k_bwd_seg_reduce.
 // and once at the end k_bwd_sink_part / k_bwd_sink_final (sink gradient over
 // all rows in a fixed order).
 #include "attn_tile.hpp"
@@ -74,9 +77,12 @@ __device__ __forceinline__ BwdRow bwd_row(int64_t r, int64_t Tq, int64_t N, int6
 
 // Key id of slot j (< n_sel + n_win): entry e of batch b is b (N + T_win) + e,
 // window row t is b (N + T_win) + N + t; -1 for a slot without a key.
+// Dense layers count window slots only, with ids b T_win + t (their entries'
+// gradients come from k_attn_bwd_dense_kv).
 template <bool SPARSE>
 __device__ __forceinline__ int64_t bwd_slot_id(const BwdRow& w, const int32_t* __restrict__ idx, int64_t r, int k,
                                                int64_t N, int64_t T_win, int64_t j) {
+  if (!SPARSE) return j < w.n_sel ? -1 : w.b * T_win + (w.lo + (j - w.n_sel) - w.w0);
   const int64_t base = w.b * (N + T_win);
   if (j < w.n_sel) {
     const int64_t e = SPARSE ? (int64_t)idx[r * k + j] : j;
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_count(const int32_t* __rest
   const BwdRow w = bwd_row<SPARSE>(r, Tq, N, T_win, k, window, ratio, win_start, q_pos);
   uint32_t* c = cnt + (int64_t)(blockIdx.x / kBwdQc) * nids;
   const int64_t nk = w.n_sel + w.n_win;
-  for (int64_t j = threadIdx.x; j < nk; j += kBwdThreads) {
+  for (int64_t j = (SPARSE ? 0 : w.n_sel) + threadIdx.x; j < nk; j += kBwdThreads) {
     const int64_t id = bwd_slot_id<SPARSE>(w, idx, r, k, N, T_win, j);
     if (id >= 0) atomicAdd(c + id, 1u);
   }
@@ -210,8 +216,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_place(const int32_t* __rest
     if (r >= r1) break;
     const BwdRow w = bwd_row<SPARSE>(r, Tq, N, T_win, k, window, ratio, win_start, q_pos);
     const int64_t nk = w.n_sel + w.n_win;
-    int32_t* prow = posbuf + (r - r0) * smax;
-    for (int64_t j = threadIdx.x; j < nk; j += kBwdThreads) {
+    const int64_t j0 = SPARSE ? 0 : w.n_sel;   // dense rows list window slots only
+    int32_t* prow = posbuf + (r - r0) * smax - j0;
+    for (int64_t j = j0 + threadIdx.x; j < nk; j += kBwdThreads) {
       const int64_t id = bwd_slot_id<SPARSE>(w, idx, r, k, N, T_win, j);
       prow[j] = id >= 0 ? (int32_t)(off[id] + atomicAdd(c + id, 1u)) : -1;
     }
@@ -231,6 +238,80 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
 __device__ __forceinline__ void lds_write_b64(uint32_t a, uint32_t lo, uint32_t hi) {
   *(lds_u32x2*)(size_t)a = u32x2_t{lo, hi};
+}
+
+// P and scale * dl of a lane (head h0 + 16 hb + col, keys 16 kb + 4 g .. + 3)
+// into the [head][key] tiles at plb / dlb.
+template <int HPW>
+__device__ __forceinline__ void write_pdl(uint32_t plb, uint32_t dlb, int h0, int g, int col,
+                                          const float (&s)[HPW][4][4], const float (&dp)[HPW][4][4]) {
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) {
+    const int hh = h0 + 16 * hb + col;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint32_t o = (uint32_t)hh * 128u + 8u * (uint32_t)((4 * kb + g) ^ pdl_swz(hh & 15));
+      lds_write_b64(plb + o, cvt_pk_bf16(s[hb][kb][0], s[hb][kb][1]), cvt_pk_bf16(s[hb][kb][2], s[hb][kb][3]));
+      lds_write_b64(dlb + o, cvt_pk_bf16(dp[hb][kb][0], dp[hb][kb][1]), cvt_pk_bf16(dp[hb][kb][2], dp[hb][kb][3]));
+    }
+  }
+}
+
+// acc += G^T = Q^T (scale dl) + dO^T P for the wave's d blocks 2 wv, 2 wv + 1
+// and the 4 key blocks of a 64-key tile; K runs over the H heads, 32 per step.
+// ga / gb: the lane's tile-invariant transposed-read offsets.
+template <int H>
+__device__ __forceinline__ void gt_accum(f32x4 (&acc)[2][4], uint32_t qtb, uint32_t otb, uint32_t plb, uint32_t dlb,
+                                         const uint32_t (&ga)[2], const uint32_t (&gb)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < H / 32; ++ks) {
+    Frag<uint16_t> aq[2], ao[2];
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2) {
+      const uint32_t a = ga[d2] + 8192u * (uint32_t)ks;
+      const i32x2 q0 = __builtin_bit_cast(i32x2, lds_read_tr16(qtb + a));
+      const i32x2 q1 = __builtin_bit_cast(i32x2, lds_read_tr16(qtb + a + 4096));
+      const i32x2 o0 = __builtin_bit_cast(i32x2, lds_read_tr16(otb + a));
+      const i32x2 o1 = __builtin_bit_cast(i32x2, lds_read_tr16(otb + a + 4096));
+      aq[d2].v = i32x4{q0[0], q0[1], q1[0], q1[1]};
+      ao[d2].v = i32x4{o0[0], o0[1], o1[0], o1[1]};
+    }
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      // rows 32 ks + trow (+ 16) share the swizzle of row trow
+      const uint32_t olo = gb[nb] + 4096u * (uint32_t)ks, ohi = olo + 2048u;
+      const i32x2 l0 = __builtin_bit_cast(i32x2, lds_read_tr16(dlb + olo));
+      const i32x2 l1 = __builtin_bit_cast(i32x2, lds_read_tr16(dlb + ohi));
+      const i32x2 p0 = __builtin_bit_cast(i32x2, lds_read_tr16(plb + olo));
+      const i32x2 p1 = __builtin_bit_cast(i32x2, lds_read_tr16(plb + ohi));
+      Frag<uint16_t> bl, bp;
+      bl.v = i32x4{l0[0], l0[1], l1[0], l1[1]};
+      bp.v = i32x4{p0[0], p0[1], p1[0], p1[1]};
+#pragma unroll
+      for (int d2 = 0; d2 < 2; ++d2) {
+        acc[d2][nb] = mma8(aq[d2], bl, acc[d2][nb]);
+        acc[d2][nb] = mma8(ao[d2], bp, acc[d2][nb]);
+      }
+    }
+  }
+}
+
+// The lane's tile-invariant offsets for gt_accum: transposed reads of the
+// Q / dO rows for d blocks 2 wv, 2 wv + 1, and of P / dl for key block nb
+// (row trow = 4 g + col / 4 of each 16-row block, unit 4 nb + col % 4).
+__device__ __forceinline__ void gt_offsets(const TileLanes& tl, int wv, int g, int col, uint32_t (&ga)[2],
+                                           uint32_t (&gb)[4]) {
+#pragma unroll
+  for (int d2 = 0; d2 < 2; ++d2) {
+    ga[d2] = (((uint32_t)(32 * (2 * wv + d2))) ^ tl.vx) + tl.vofs;
+    opaque(ga[d2]);
+  }
+  const int trow = 4 * g + (col >> 2);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    gb[nb] = (uint32_t)trow * 128u + 8u * (uint32_t)((4 * nb + (col & 3)) ^ pdl_swz(trow));
+    opaque(gb[nb]);
+  }
 }
 
 // D[r, h] = dO[r, h] . O[r, h] for every (row, head): 16 lanes per pair,
@@ -372,23 +453,8 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   const uint32_t qtb = (uint32_t)(uintptr_t)qt, otb = (uint32_t)(uintptr_t)ot;
   const int64_t ntiles = cdiv(nk, kKT);
   const int32_t* prow = posbuf + (r - r0) * smax;
-  // Tile-invariant LDS offsets of the G^T operands: the transposed reads of
-  // the Q / dO rows for d blocks 2 wv, 2 wv + 1, and of P / dl for key block
-  // nb (row trow = 4 g + col / 4 of each 16-row block, unit 4 nb + col % 4).
-  uint32_t ga[2], gb[4];
-#pragma unroll
-  for (int d2 = 0; d2 < 2; ++d2) {
-    ga[d2] = (((uint32_t)(32 * (2 * wv + d2))) ^ tl.vx) + tl.vofs;
-    opaque(ga[d2]);
-  }
-  {
-    const int trow = 4 * g + (col >> 2);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      gb[nb] = (uint32_t)trow * 128u + 8u * (uint32_t)((4 * nb + (col & 3)) ^ pdl_swz(trow));
-      opaque(gb[nb]);
-    }
-  }
+  uint32_t ga[2], gb[4];   // tile-invariant offsets of the key-row gradient product
+  gt_offsets(tl, wv, g, col, ga, gb);
   int32_t e_next[4];
   {
     int32_t e0[4];
@@ -416,8 +482,14 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int64_t kk = t * kKT + 16 * nb + col;
-      const int32_t v = prow[kk < nk ? kk : nk - 1];
-      pv[nb] = kk < nk ? v : -1;
+      if constexpr (SPARSE) {
+        const int32_t v = prow[kk < nk ? kk : nk - 1];
+        pv[nb] = kk < nk ? v : -1;
+      } else {   // dense rows list window slots only
+        const bool win = kk >= w.n_sel && kk < nk;
+        const int32_t v = prow[win ? kk - w.n_sel : 0];
+        pv[nb] = win ? v : -1;
+      }
     }
 
     // ---- S^T = K Q^T and dP^T = K dO^T (keys 16 kb + 4 g + rr, head column col)
@@ -504,61 +576,22 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
         }
       }
     }
-    // ---- P and scale * dl to LDS, [head][key] (64 heads: into this tile's key
-    // slot, once every wave is done with its keys)
-    if constexpr (HPW == 1) __syncthreads();
-    const uint32_t plb = HPW == 1 ? tb : (uint32_t)(uintptr_t)pdl_sep;
-    const uint32_t dlb = plb + (uint32_t)(H * kKT * 2);
-#pragma unroll
-    for (int hb = 0; hb < HPW; ++hb) {
-      const int hh = h0 + 16 * hb + col;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint32_t o = (uint32_t)hh * 128u + 8u * (uint32_t)((4 * kb + g) ^ pdl_swz(hh & 15));
-        lds_write_b64(plb + o, cvt_pk_bf16(s[hb][kb][0], s[hb][kb][1]), cvt_pk_bf16(s[hb][kb][2], s[hb][kb][3]));
-        lds_write_b64(dlb + o, cvt_pk_bf16(dp[hb][kb][0], dp[hb][kb][1]), cvt_pk_bf16(dp[hb][kb][2], dp[hb][kb][3]));
-      }
-    }
-    __syncthreads();
-    // ---- G^T = Q^T (scale dl) + dO^T P for d blocks 2 wv, 2 wv + 1 and the
-    // 4 key blocks; K runs over the heads, 32 per step
-    {
+    // ---- key-row gradients of the tile (dense layers: only tiles holding
+    // window keys; the entries' gradients come from k_attn_bwd_dense_kv)
+    if (SPARSE || t * kKT + kKT > w.n_sel) {   // block-uniform
+      // P and scale * dl to LDS, [head][key] (64 heads: into this tile's key
+      // slot, once every wave is done with its keys)
+      if constexpr (HPW == 1) __syncthreads();
+      const uint32_t plb = HPW == 1 ? tb : (uint32_t)(uintptr_t)pdl_sep;
+      const uint32_t dlb = plb + (uint32_t)(H * kKT * 2);
+      write_pdl<HPW>(plb, dlb, h0, g, col, s, dp);
+      __syncthreads();
       f32x4 acc[2][4];
 #pragma unroll
       for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[d2][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < H / 32; ++ks) {
-        Frag<uint16_t> aq[2], ao[2];
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) {
-          const uint32_t a = ga[d2] + 8192u * (uint32_t)ks;
-          const i32x2 q0 = __builtin_bit_cast(i32x2, lds_read_tr16(qtb + a));
-          const i32x2 q1 = __builtin_bit_cast(i32x2, lds_read_tr16(qtb + a + 4096));
-          const i32x2 o0 = __builtin_bit_cast(i32x2, lds_read_tr16(otb + a));
-          const i32x2 o1 = __builtin_bit_cast(i32x2, lds_read_tr16(otb + a + 4096));
-          aq[d2].v = i32x4{q0[0], q0[1], q1[0], q1[1]};
-          ao[d2].v = i32x4{o0[0], o0[1], o1[0], o1[1]};
-        }
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          // rows 32 ks + trow (+ 16) share the swizzle of row trow
-          const uint32_t olo = gb[nb] + 4096u * (uint32_t)ks, ohi = olo + 2048u;
-          const i32x2 l0 = __builtin_bit_cast(i32x2, lds_read_tr16(dlb + olo));
-          const i32x2 l1 = __builtin_bit_cast(i32x2, lds_read_tr16(dlb + ohi));
-          const i32x2 p0 = __builtin_bit_cast(i32x2, lds_read_tr16(plb + olo));
-          const i32x2 p1 = __builtin_bit_cast(i32x2, lds_read_tr16(plb + ohi));
-          Frag<uint16_t> bl, bp;
-          bl.v = i32x4{l0[0], l0[1], l1[0], l1[1]};
-          bp.v = i32x4{p0[0], p0[1], p1[0], p1[1]};
-#pragma unroll
-          for (int d2 = 0; d2 < 2; ++d2) {
-            acc[d2][nb] = mma8(aq[d2], bl, acc[d2][nb]);
-            acc[d2][nb] = mma8(ao[d2], bp, acc[d2][nb]);
-          }
-        }
-      }
+      gt_accum<H>(acc, qtb, otb, plb, dlb, ga, gb);
       // lane: rows d = 16 db + 4 g .. + 3 of key 16 nb + col
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -584,6 +617,156 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
   }
 }
 
+// Dense layers, compressed entries: one block per (block of 64 entries,
+// sequence, segment of query rows). The entries stay in LDS; for every query
+// row of the segment that sees at least one of them, the block gathers the
+// row's Q and dO, forms S^T, dP^T, P and scale * dl for the 64 entries
+// (entries past n(p) get P = 0) and adds G^T = Q^T (scale dl) + dO^T P to
+// accumulators that live in registers across the rows. Each block writes its
+// segment's partial once; k_bwd_seg_reduce adds the segments in order. This
+// replaces a 512-byte contribution row per (query, entry).
+template <int HPW>
+__global__ __launch_bounds__(kBwdThreads, 2) void k_attn_bwd_dense_kv(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ q_pos,
+    const float* __restrict__ Dv, const float* __restrict__ lse, const uint16_t* __restrict__ dout, int64_t Tq,
+    int64_t N, int ratio, float scale, int64_t seg, int nseg, float* __restrict__ part) {
+  constexpr int H = 64 * HPW;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ __align__(16) uint16_t kt[kKT * kD];      // the block's 64 entries
+  __shared__ __align__(16) uint16_t qt[H * kD];        // the current row's Q (one row per head)
+  __shared__ __align__(16) uint16_t ot[H * kD];        // and dO
+  __shared__ __align__(16) uint16_t pdl[2 * H * kKT];  // P, then scale * dl, [head][key]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, col = lane & 15;
+  const TileLanes tl(lane, 15);
+  const int64_t e0 = (int64_t)blockIdx.x * kKT;
+  const int64_t b = blockIdx.y / nseg, sgi = blockIdx.y % nseg;
+  const int64_t t0 = sgi * seg, t1 = (t0 + seg) < Tq ? (t0 + seg) : Tq;
+  const int h0 = wv * 16 * HPW;
+  const float scale2 = scale * kLog2e;
+  // the block's entries (rows past N read entry N - 1: never visible)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * j + 4 * wv + (lane >> 4);
+    const int64_t e = (e0 + row) < N ? (e0 + row) : N - 1;
+    gather_lds16(kv + (b * N + e) * kD + (((lane & 15) ^ (row & 15)) * 8),
+                 (uint32_t)(uintptr_t)(kt + (4 * j + wv) * 4 * kD));
+  }
+  const uint32_t tb = (uint32_t)(uintptr_t)kt, qtb = (uint32_t)(uintptr_t)qt, otb = (uint32_t)(uintptr_t)ot;
+  const uint32_t plb = (uint32_t)(uintptr_t)pdl, dlb = plb + (uint32_t)(H * kKT * 2);
+  uint32_t ga[2], gb[4];
+  gt_offsets(tl, wv, g, col, ga, gb);
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[d2][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t r = b * Tq + t;
+    const int n = __builtin_amdgcn_readfirstlane((int)visible(q_pos[r], ratio, N));
+    if (n <= e0) continue;   // uniform: none of the block's entries is visible
+    // the row's Q and dO rows, laid out like key tiles
+#pragma unroll
+    for (int i = 0; i < H / 16; ++i) {
+      const int hr = (4 * i + wv) * 4 + (lane >> 4);
+      const int c = (lane & 15) ^ (hr & 15);
+      gather_lds16(q + (r * H + hr) * kD + c * 8, (uint32_t)(uintptr_t)(qt + (4 * i + wv) * 4 * kD));
+      gather_lds16(dout + (r * H + hr) * kD + c * 8, (uint32_t)(uintptr_t)(ot + (4 * i + wv) * 4 * kD));
+    }
+    float Dh[HPW], lse2[HPW];
+    bool live[HPW];
+#pragma unroll
+    for (int hb = 0; hb < HPW; ++hb) {
+      const int64_t hrow = r * H + h0 + 16 * hb + col;
+      Dh[hb] = Dv[hrow];
+      const float L = lse[hrow];
+      live[hb] = L > -INFINITY;
+      lse2[hb] = live[hb] ? L * kLog2e : 0.f;
+    }
+    wait_vm<0>();
+    __syncthreads();
+    // S^T = K Q^T, dP^T = K dO^T (entries 16 kb + 4 g + rr, head column col);
+    // the B operands come from the Q / dO rows in LDS
+    float sv[HPW][4][4], dp[HPW][4][4];
+    {
+      f32x4 as[4][HPW], ad[4][HPW];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+          as[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          ad[kb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) {
+        uint32_t ka = (((uint32_t)(64 * ks)) ^ tl.kx) + tl.kofs;
+        opaque(ka);
+        Frag<uint16_t> a[4], qf[HPW], df[HPW];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) a[kb].v = lds_read_b128(tb + ka + 4096 * kb);
+#pragma unroll
+        for (int hb = 0; hb < HPW; ++hb) {
+          qf[hb].v = lds_read_b128(qtb + ka + 4096 * (wv * HPW + hb));
+          df[hb].v = lds_read_b128(otb + ka + 4096 * (wv * HPW + hb));
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) {
+            as[kb][hb] = mma8(a[kb], qf[hb], as[kb][hb]);
+            ad[kb][hb] = mma8(a[kb], df[hb], ad[kb][hb]);
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int hb = 0; hb < HPW; ++hb) {
+            const bool ok = live[hb] && (e0 + 16 * kb + 4 * g + rr) < n;
+            const float pv = ok ? __builtin_amdgcn_exp2f(fmaf(as[kb][hb][rr], scale2, -lse2[hb])) : 0.f;
+            sv[hb][kb][rr] = pv;
+            dp[hb][kb][rr] = scale * pv * (ad[kb][hb][rr] - Dh[hb]);
+          }
+    }
+    write_pdl<HPW>(plb, dlb, h0, g, col, sv, dp);
+    __syncthreads();
+    gt_accum<H>(acc, qtb, otb, plb, dlb, ga, gb);
+    __syncthreads();   // the next row's gathers and P / dl writes reuse qt, ot, pdl
+  }
+  // partial of this segment: lane rows d = 16 db + 4 g .. + 3 of entry e0 + 16 nb + col
+  float* pb = part + ((b * nseg + sgi) * N + e0) * kD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    if (e0 + 16 * nb + col >= N) continue;
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2) {
+      const int db = 2 * wv + d2;
+      *reinterpret_cast<float4*>(pb + (16 * nb + col) * kD + 16 * db + 4 * g) =
+          make_float4(acc[d2][nb][0], acc[d2][nb][1], acc[d2][nb][2], acc[d2][nb][3]);
+    }
+  }
+}
+
+// dkv[b, e] = sum over segments s (in order) of part[b, s, e]: one wave per entry.
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_seg_reduce(const float* __restrict__ part, int64_t B, int64_t N,
+                                                                int nseg, float* __restrict__ dkv) {
+  const int64_t i = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+  if (i >= B * N) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t b = i / N, e = i % N;
+  float2 acc = make_float2(0.f, 0.f);
+  for (int sg = 0; sg < nseg; ++sg) {
+    const float2 v = *reinterpret_cast<const float2*>(part + ((b * nseg + sg) * N + e) * kD + 2 * lane);
+    acc.x += v.x;
+    acc.y += v.y;
+  }
+  *reinterpret_cast<float2*>(dkv + i * kD + 2 * lane) = acc;
+}
+
 // One block per key: wave w sums the w-th quarter of the key's contribution
 // list (8 loads in flight, added in list order), then the quarters are added
 // in order to the previous passes' sum (when `accumulate`). The split
@@ -591,9 +774,9 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_reduce(const float* __restrict__ G,
                                                             const uint32_t* __restrict__ off, int64_t nids,
                                                             int64_t N, int64_t T_win, float* __restrict__ dkv,
-                                                            float* __restrict__ dx_win, int accumulate) {
+                                                            float* __restrict__ dx_win, int accumulate, int win_only) {
   __shared__ float2 part[kBwdThreads / 64][64];
-  const int64_t id = blockIdx.x;
+  const int64_t id = blockIdx.x;   // win_only (dense layers): ids are window rows b T_win + t
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint32_t u0 = off[id], len = off[id + 1] - u0;
   const uint32_t a = u0 + (uint32_t)(((uint64_t)len * wv) / 4), e = u0 + (uint32_t)(((uint64_t)len * (wv + 1)) / 4);
@@ -619,7 +802,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_reduce(const float* __restr
   __syncthreads();
   if (wv == 0) {
     const int64_t b = id / (N + T_win), j = id % (N + T_win);
-    float* o = (j < N ? dkv + (b * N + j) * kD : dx_win + (b * T_win + (j - N)) * kD) + 2 * lane;
+    float* o = (win_only ? dx_win + id * kD : j < N ? dkv + (b * N + j) * kD : dx_win + (b * T_win + (j - N)) * kD) +
+               2 * lane;
     float2 t = accumulate ? *reinterpret_cast<const float2*>(o) : make_float2(0.f, 0.f);
 #pragma unroll
     for (int w = 0; w < kBwdThreads / 64; ++w) {
@@ -663,8 +847,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_sink_final(const float* __r
 // ------------------------------------------------------------------ host side
 
 struct BwdPlan {
-  int64_t rows, smax, rows_pass, nchunks, nids, nscan;
-  size_t o_cnt, o_total, o_off, o_bsum, o_pos, o_g, o_sink, o_spart, o_delta, bytes;
+  int64_t rows, smax, rows_pass, nchunks, nids, nscan, nkb, seg, nseg;
+  size_t o_cnt, o_total, o_off, o_bsum, o_pos, o_g, o_sink, o_spart, o_delta, o_part, bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -673,14 +857,28 @@ static BwdPlan bwd_plan(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T
   BwdPlan p;
   p.rows = B * Tq;
   const int64_t wmax = window < T_win ? (int64_t)window : T_win;
-  p.smax = (sparse ? (int64_t)k : N) + wmax;
+  // contribution slots per query row: selected entries and window rows
+  // (sparse), window rows only (dense)
+  p.smax = (sparse ? (int64_t)k : 0) + wmax;
   if (p.smax < 1) p.smax = 1;
   int64_t rp = kBwdGBudget / (p.smax * kD * 4) / kBwdQc * kBwdQc;
   if (rp < kBwdQc) rp = kBwdQc;
   p.rows_pass = rp < p.rows ? rp : p.rows;
   p.nchunks = cdiv(p.rows_pass, kBwdQc);
-  p.nids = B * (N + T_win);
+  p.nids = sparse ? B * (N + T_win) : B * T_win;
   p.nscan = cdiv(p.nids, kScanBlock);
+  // dense entries: blocks of 64 entries x sequences x segments of query rows,
+  // about 2048 blocks
+  p.nkb = cdiv(N, kKT);
+  p.seg = 1;
+  p.nseg = 0;
+  if (!sparse && N > 0) {
+    int64_t ns = cdiv(2048, p.nkb * B);
+    if (ns > Tq) ns = Tq;
+    if (ns < 1) ns = 1;
+    p.seg = cdiv(Tq, ns);
+    p.nseg = cdiv(Tq, p.seg);
+  }
   size_t o = 0;
   p.o_cnt = o;   o += align256((size_t)p.nchunks * p.nids * 4);
   p.o_total = o; o += align256((size_t)p.nids * 4);
@@ -691,6 +889,7 @@ static BwdPlan bwd_plan(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T
   p.o_sink = o;  o += align256((size_t)p.rows * H * 4);
   p.o_spart = o; o += align256((size_t)kSinkBlocks * H * 4);
   p.o_delta = o; o += align256((size_t)p.rows * H * 4);
+  p.o_part = o;  o += align256((size_t)B * p.nseg * N * kD * 4);
   p.bytes = o;
   return p;
 }
@@ -726,15 +925,17 @@ static hipError_t run_attn_bwd(const uint16_t* q, const uint16_t* kv, const int3
     const int64_t r1 = r0 + p.rows_pass < p.rows ? r0 + p.rows_pass : p.rows;
     const int64_t nr = r1 - r0;
     const int64_t nch = cdiv(nr, kBwdQc);
-    k_fill_u32<<<fill_grid(nch * p.nids), kBwdThreads, 0, s>>>(cnt, nch * p.nids, 0u);
-    k_bwd_count<SPARSE><<<(unsigned)nr, kBwdThreads, 0, s>>>(idx, win_start, q_pos, r0, Tq, N, T_win, k, window,
-                                                             ratio, p.nids, cnt);
-    k_bwd_chunk_scan<<<(unsigned)cdiv(p.nids, kBwdThreads), kBwdThreads, 0, s>>>(cnt, p.nids, (int)nch, total);
-    k_bwd_scan_sums<<<(unsigned)p.nscan, kBwdThreads, 0, s>>>(total, p.nids, bsum);
-    k_bwd_scan_top<<<1, kBwdThreads, 0, s>>>(bsum, p.nscan);
-    k_bwd_scan_apply<<<(unsigned)p.nscan, kBwdThreads, 0, s>>>(total, p.nids, bsum, off);
-    k_bwd_place<SPARSE><<<(unsigned)nch, kBwdThreads, 0, s>>>(idx, win_start, q_pos, r0, r1, Tq, N, T_win, k,
-                                                              window, ratio, p.nids, cnt, off, pos, p.smax);
+    if (p.nids > 0) {   // keys that take contributions (none: a dense layer without window rows)
+      k_fill_u32<<<fill_grid(nch * p.nids), kBwdThreads, 0, s>>>(cnt, nch * p.nids, 0u);
+      k_bwd_count<SPARSE><<<(unsigned)nr, kBwdThreads, 0, s>>>(idx, win_start, q_pos, r0, Tq, N, T_win, k, window,
+                                                               ratio, p.nids, cnt);
+      k_bwd_chunk_scan<<<(unsigned)cdiv(p.nids, kBwdThreads), kBwdThreads, 0, s>>>(cnt, p.nids, (int)nch, total);
+      k_bwd_scan_sums<<<(unsigned)p.nscan, kBwdThreads, 0, s>>>(total, p.nids, bsum);
+      k_bwd_scan_top<<<1, kBwdThreads, 0, s>>>(bsum, p.nscan);
+      k_bwd_scan_apply<<<(unsigned)p.nscan, kBwdThreads, 0, s>>>(total, p.nids, bsum, off);
+      k_bwd_place<SPARSE><<<(unsigned)nch, kBwdThreads, 0, s>>>(idx, win_start, q_pos, r0, r1, Tq, N, T_win, k,
+                                                                window, ratio, p.nids, cnt, off, pos, p.smax);
+    }
     timer_before(CSA_KID_ATTN_BWD, s);
     if (H == 64)
       k_attn_bwd16<SPARSE, 1><<<(unsigned)nr, kBwdThreads, 0, s>>>(q, kv, idx, x_win, win_start, sink, q_pos, delta,
@@ -748,9 +949,25 @@ static hipError_t run_attn_bwd(const uint16_t* q, const uint16_t* kv, const int3
     timer_after(CSA_KID_ATTN_BWD, s);
     if (e != hipSuccess) return e;
     if (p.nids > 0)
-      k_bwd_reduce<<<(unsigned)p.nids, kBwdThreads, 0, s>>>(G, off, p.nids, N, T_win, dkv, dx_win, r0 > 0 ? 1 : 0);
+      k_bwd_reduce<<<(unsigned)p.nids, kBwdThreads, 0, s>>>(G, off, p.nids, N, T_win, dkv, dx_win, r0 > 0 ? 1 : 0,
+                                                            SPARSE ? 0 : 1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (!SPARSE && p.nseg > 0) {   // dense: the entries' gradients, summed over query segments
+    float* part = reinterpret_cast<float*>(wb + p.o_part);
+    const dim3 grid((unsigned)p.nkb, (unsigned)(B * p.nseg));
+    timer_before(CSA_KID_ATTN_BWD, s);
+    if (H == 64)
+      k_attn_bwd_dense_kv<1><<<grid, kBwdThreads, 0, s>>>(q, kv, q_pos, delta, lse, dout, Tq, N, ratio, scale, p.seg,
+                                                         (int)p.nseg, part);
+    else
+      k_attn_bwd_dense_kv<2><<<grid, kBwdThreads, 0, s>>>(q, kv, q_pos, delta, lse, dout, Tq, N, ratio, scale, p.seg,
+                                                         (int)p.nseg, part);
+    hipError_t e = hipGetLastError();
+    timer_after(CSA_KID_ATTN_BWD, s);
+    if (e != hipSuccess) return e;
+    k_bwd_seg_reduce<<<(unsigned)cdiv(B * N, kBwdThreads / 64), kBwdThreads, 0, s>>>(part, B, N, (int)p.nseg, dkv);
   }
   if (sink && dsink) {
     float* sp2 = reinterpret_cast<float*>(wb + p.o_spart);

@@ -198,6 +198,8 @@ def test_backward_workspace_passes():
     assert mid >= 4096 * 640 * 512                     # every row's slots fit one pass
     assert big < 5 * (1 << 30)                          # 65,536 rows: passes, bounded buffer
     assert lib.sparse_attn_bwd_workspace_size(0, 1, 16, 16, 64, 128, 8, 128) == 0
-    d = lambda Tq: lib.dense_attn_bwd_workspace_size(1, Tq, 65536, 256, 64, 128, 128)
-    # one pass holds 64 rows of 65,664 slots; more rows add passes, not buffer (beyond per-row sink terms)
-    assert d(64) > 64 * 65536 * 512 and d(256) - d(64) < 1 << 20
+    # dense layers: contribution rows for the window slots only (the entries'
+    # gradients are summed per block of entries and segment of query rows)
+    d = lambda Tq, N, T_win: lib.dense_attn_bwd_workspace_size(1, Tq, N, T_win, 64, 128, 128)
+    assert 64 * 128 * 512 < d(64, 65536, 256) < 64 * 65536 * 512
+    assert d(131072, 1024, 131072) < 6 * (1 << 30)      # 4 GiB of window rows per pass + segment partials
