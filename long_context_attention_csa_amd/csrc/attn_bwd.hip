@@ -636,6 +636,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void k_attn_bwd_dense_kv(
   __shared__ __align__(16) uint16_t qt[H * kD];        // the current row's Q (one row per head)
   __shared__ __align__(16) uint16_t ot[H * kD];        // and dO
   __shared__ __align__(16) uint16_t pdl[2 * H * kKT];  // P, then scale * dl, [head][key]
+  __shared__ int nvis[kBwdThreads];                      // n(p) of the next 256 rows of the segment
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -666,7 +667,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void k_attn_bwd_dense_kv(
 
   for (int64_t t = t0; t < t1; ++t) {
     const int64_t r = b * Tq + t;
-    const int n = __builtin_amdgcn_readfirstlane((int)visible(q_pos[r], ratio, N));
+    if (((t - t0) & (kBwdThreads - 1)) == 0) {   // uniform: stage n(p) of the next 256 rows
+      __syncthreads();
+      const int64_t tt = t + tid;
+      nvis[tid] = tt < t1 ? (int)visible(q_pos[b * Tq + tt], ratio, N) : 0;
+      __syncthreads();
+    }
+    const int n = __builtin_amdgcn_readfirstlane(nvis[(t - t0) & (kBwdThreads - 1)]);
     if (n <= e0) continue;   // uniform: none of the block's entries is visible
     // the row's Q and dO rows, laid out like key tiles
 #pragma unroll
