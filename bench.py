@@ -18,7 +18,7 @@ library's kernel timer), the CPU oracle timed on a bounded sample, and extra
 workloads (CSA decode at 262k context; prefill TFLOP/s) under "extras".
 
 Usage: python bench.py [--steps K] [--warmup W]
-                       [--extras decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca|none]
+                       [--extras decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca|none]
 """
 from __future__ import annotations
 
@@ -62,7 +62,8 @@ def recorded_traffic(kernel: str, source: str):
 
 # ----------------------------------------------------------------------------- decode workloads
 
-def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies, wid, host_sample=True):
+def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies, wid, host_sample=True,
+                    bf16_scores=False):
     """Build the caches (copies of them) and one-step closures for a decode workload."""
     dev = "cuda"
     N = L // 4
@@ -95,7 +96,8 @@ def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies,
     st["win_start"] = torch.full((B,), L - 127, dtype=torch.int32, device=dev)
     st["idx"] = torch.empty(B, 1, k, dtype=torch.int32, device=dev)
     st["out"] = torch.empty(B, 1, H, 128, dtype=bf, device=dev)
-    st["ws_idx"] = torch.empty(C.indexer_topk_workspace_size(B, 1, N, H_I, d_I, k, fmt), dtype=torch.uint8, device=dev)
+    st["ws_idx"] = torch.empty(C.indexer_topk_workspace_size(B, 1, N, H_I, d_I, k, fmt, bf16_scores),
+                               dtype=torch.uint8, device=dev)
     st["ws_sp"] = torch.empty(max(1, C.sparse_attn_workspace_size(B, 1, H, 128, k, 128)), dtype=torch.uint8, device=dev)
     bytes_idx = B * N * (d_I // 2 + d_I // 32 if fmt == "fp4" else d_I + 4) + B * H_I * (d_I + 8)
     bytes_sp = B * (k + 128) * 256 + 2 * B * H * 256 + B * k * 4
@@ -116,7 +118,7 @@ def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies,
 
     def step(c):
         C.indexer_topk(st["qi"], st["qs"], st["w"], st["codes"][c], st["scales"][c], fmt, st["q_pos"], 4, k, d_I,
-                       ws=st["ws_idx"], idx_out=st["idx"])
+                       ws=st["ws_idx"], idx_out=st["idx"], bf16_scores=bf16_scores)
         C.sparse_attn_fwd(st["q"], st["kv"][c], st["idx"], st["x_win"], st["win_start"], st["sink"], st["q_pos"],
                           128, 1.0, ws=st["ws_sp"], out=st["out"])
         if hca:
@@ -216,10 +218,11 @@ def cpu_baseline_decode(O, st, seconds):
 
 
 def run_decode(torch, C, syn, O, args, which):
-    if which == "pair1m":
-        st = decode_workload(torch, C, syn, "csa_hca_decode_pair_1m_ctx", B=8, L=1 << 20, H=128, H_I=64, d_I=128,
-                             k=1024, fmt="fp4", hca=True, copies=args.copies, wid=5,
-                             host_sample=not args.no_cpu_baseline)
+    if which in ("pair1m", "pair1m_bf16"):
+        bf = which == "pair1m_bf16"
+        st = decode_workload(torch, C, syn, "csa_hca_decode_pair_1m_ctx" + ("_bf16_scores" if bf else ""), B=8,
+                             L=1 << 20, H=128, H_I=64, d_I=128, k=1024, fmt="fp4", hca=True, copies=args.copies,
+                             wid=5, host_sample=not args.no_cpu_baseline and not bf, bf16_scores=bf)
     else:
         st = decode_workload(torch, C, syn, "csa_decode_262k_ctx", B=32, L=1 << 18, H=128, H_I=64, d_I=128,
                              k=1024, fmt="fp8", hca=False, copies=args.copies, wid=4, host_sample=False)
@@ -572,7 +575,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
-    ap.add_argument("--extras", default="decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca",
+    ap.add_argument("--extras", default="decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca",
                     help="comma list of decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk or 'none'")
     ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -640,6 +643,14 @@ def main():
     wanted = [] if args.extras == "none" else [x for x in args.extras.split(",") if x]
     del st
     torch.cuda.empty_cache()
+    if "decode_bf16" in wanted:
+        # the same decode pair with bfloat16 index scores (indexer_topk_bf16_scores)
+        stb, msb, wallb, ktb = run_decode(torch, C, syn, O, args, "pair1m_bf16")
+        extras["csa_hca_decode_pair_1m_ctx_bf16_scores"] = {
+            "queries_per_s": round(stb["B"] / (msb * 1e-3), 1), "ms_per_step": round(msb, 5),
+            "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in ktb.items()}}
+        del stb
+        torch.cuda.empty_cache()
     if "decode4" in wanted:
         st4, ms4, wall4, kt4 = run_decode(torch, C, syn, O, args, "decode4")
         extras["csa_decode_262k_ctx"] = {
