@@ -470,8 +470,13 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
     // ones leave none of the gathers outstanding (tile 0: the prologue's index
     // loads only; the Q / dO gathers are older still). The barrier then also
     // means every wave is past the previous tile's use of the other slot.
+    // Dense rows: a tile of entries only skips the key-row gradient phase,
+    // whose 4 position loads are then not issued either (the compiler keeps
+    // them inside that phase), so nothing follows the gathers and the wait
+    // must drain them.
     if (t == 0) wait_vm<SPARSE ? 4 : 0>();
-    else wait_vm<SPARSE ? 8 : 4>();
+    else if (SPARSE || t * kKT > w.n_sel) wait_vm<SPARSE ? 8 : 4>();
+    else wait_vm<0>();
     __syncthreads();
     if (t + 1 < ntiles) {
       issue(t + 1, e_next);

@@ -230,3 +230,71 @@ def test_sparse_attn_bwd_fullsize_sampled():
             sel, rows, _, dk = row_bwd(p)
             want += dk[len(sel) + int(np.nonzero(rows == t)[0][0])]
         check_grad(dxw[t], want, f"dx_win row {t}")
+
+
+def test_dense_attn_bwd_fullsize_sampled():
+    """The HCA prefill shape the benchmark times (T = 131,072, 64 heads, ratio
+    128: 1,024 entries, window 128, sink), run exactly as there: repeated calls
+    are bit-identical; dq of sampled rows, dkv of the last entries (each seen
+    by the few hundred rows after its block: the oracle's per-row gradients
+    summed over all of them) and dx_win of sampled window rows match the
+    oracle."""
+    dev_, bf = "cuda", BF
+    T, H, ratio, W = 131072, 64, 128, 128
+    N = T // ratio
+    s = 7000
+    q = syn.normal_device(s, (1, T, H, 128), dev_, bf, scale=1 / np.sqrt(128))
+    E = syn.normal_device(s + 1, (1, N, 128), dev_, bf)
+    xw = syn.normal_device(s + 2, (1, T, 128), dev_, bf)
+    sink = syn.normal_device(s + 3, (H,), dev_)
+    dout = syn.normal_device(s + 4, (1, T, H, 128), dev_, bf)
+    q_pos = torch.arange(T, dtype=torch.int32, device=dev_)[None]
+    win_start = torch.zeros(1, dtype=torch.int32, device=dev_)
+    out, lse = C.dense_compressed_attn_fwd(q, E, xw, win_start, sink, q_pos, ratio, W, 1.0, want_lse=True)
+    _print("dense bwd full size: first call")
+    a = C.dense_compressed_attn_bwd(q, E, xw, win_start, sink, q_pos, out, lse, dout, ratio, W, 1.0)
+    _print("dense bwd full size: second call")
+    b = C.dense_compressed_attn_bwd(q, E, xw, win_start, sink, q_pos, out, lse, dout, ratio, W, 1.0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert torch.isfinite(a[3]).all()
+    entries = (N - 1, N - 2, N - 9)   # seen by rows from ratio * (e + 1) - 1 on
+    dq_rows = (0, 1, 126, 127, 128, 255, 4099, 65535, 65536, 100001, T - 2, T - 1)
+    win_rows = (0, 70000, T - 1)
+    need = set(dq_rows)
+    need.update(range(ratio * (min(entries) + 1) - 1, T))
+    for t in win_rows:
+        need.update(range(t, min(T, t + W)))
+    rows = np.array(sorted(need), dtype=np.int64)
+    at = {int(p): i for i, p in enumerate(rows)}
+    ri = torch.as_tensor(rows, device=dev_)
+    qh, doh = host(q[0, ri]), host(dout[0, ri])
+    dq = host(a[0][0, ri])
+    dkv, dxw = host(a[1])[0], host(a[2])[0]
+    Eh, xh, sk = host(E)[0], host(xw)[0], host(sink)
+    cache = {}
+
+    def row_bwd(p):
+        if p not in cache:
+            n = int(O.visible_entries(p, ratio, N))
+            wr = O.window_rows(p, W, 0, T)
+            keys = np.concatenate([Eh[:n], xh[wr]], 0)
+            dqr, dk, _ = O.attend_bwd(qh[at[p]], keys, sk, doh[at[p]], 1.0)
+            cache[p] = (n, wr, dqr, dk)
+        return cache[p]
+
+    for p in dq_rows:
+        check_grad(dq[at[p]], row_bwd(p)[2], f"dq row {p}")
+    for e in entries:
+        want = np.zeros(128)
+        seen = range(ratio * (e + 1) - 1, T)
+        for p in seen:
+            want += row_bwd(p)[3][e]
+        _print(f"  entry {e}: seen by {len(seen)} rows")
+        check_grad(dkv[e], want, f"dkv entry {e}")
+    for t in win_rows:
+        want = np.zeros(128)
+        for p in range(t, min(T, t + W)):
+            n, wr, _, dk = row_bwd(p)
+            want += dk[n + int(np.nonzero(wr == t)[0][0])]
+        check_grad(dxw[t], want, f"dx_win row {t}")
