@@ -89,6 +89,11 @@ def test_full_decode(case):
         qh = syn.normal_device(s + 13, (B, 1, H, 128), DEV, BF, scale=1 / np.sqrt(128))
         sinkh = syn.normal_device(s + 14, (H,), DEV)
         outh = C.dense_compressed_attn_fwd(qh, kvh, xh, win_start, sinkh, q_pos, 128, 128, 1.0)
+        assert torch.equal(outh, C.dense_compressed_attn_fwd(qh, kvh, xh, win_start, sinkh, q_pos, 128, 128, 1.0))
+    # repeated calls give the same bits
+    idx2, sc2 = C.indexer_topk(qi, qs, w, kc, ks, fmt, q_pos, 4, k, d_I, want_scores=True)
+    assert torch.equal(idx, idx2) and torch.equal(sc, sc2)
+    assert torch.equal(out, C.sparse_attn_fwd(q, kv, idx, xw, win_start, sink, q_pos, 128, 1.0))
     torch.cuda.synchronize()
     got_idx, got_s = host(idx)[:, 0], host(sc)[:, 0]
     # every row: the selection is the oracle's selection over the GPU's scores
@@ -128,6 +133,9 @@ def test_full_csa_prefill_T65536():
     kc, ks = C.csa_compress(ci[0], ci[1], ci[2], ci[3], 4, out_fmt="fp8")
     idx = C.indexer_topk(qi, qs, w, kc, ks, "fp8", q_pos, 4, k, d_I)
     out = C.sparse_attn_fwd(q, E, idx, c[0], win_start, sink, q_pos, W, 1.0)
+    # repeated calls give the same bits
+    assert torch.equal(idx, C.indexer_topk(qi, qs, w, kc, ks, "fp8", q_pos, 4, k, d_I))
+    assert torch.equal(out, C.sparse_attn_fwd(q, E, idx, c[0], win_start, sink, q_pos, W, 1.0))
     torch.cuda.synchronize()
     # compressor: every entry against the oracle
     ch = [host(x[0]) for x in c]
@@ -172,6 +180,7 @@ def test_full_hca_prefill_T131072():
     win_start = torch.zeros(1, dtype=torch.int32, device=DEV)
     E = C.hca_compress(cc, zz, 128)
     out = C.dense_compressed_attn_fwd(q, E, cc, win_start, sink, q_pos, 128, W, 1.0)
+    assert torch.equal(out, C.dense_compressed_attn_fwd(q, E, cc, win_start, sink, q_pos, 128, W, 1.0))
     torch.cuda.synchronize()
     ch = host(cc[0])
     assert_close(host(E[0]), O.hca_compress(ch, host(zz[0]), 128), "bf16", "HCA compressed entries")
@@ -211,6 +220,10 @@ def test_full_prefill_chunk_1m():
     idx = C.indexer_topk(qi, qs, w, kc, ks, "fp4", q_pos, 4, k, d_I)
     out = C.sparse_attn_fwd(q, E, idx, xw, win_start, sink, q_pos, W, 1.0)
     outh = C.dense_compressed_attn_fwd(qh, Eh, xh, win_start, sinkh, q_pos, 128, W, 1.0)
+    # repeated calls give the same bits
+    assert torch.equal(idx, C.indexer_topk(qi, qs, w, kc, ks, "fp4", q_pos, 4, k, d_I))
+    assert torch.equal(out, C.sparse_attn_fwd(q, E, idx, xw, win_start, sink, q_pos, W, 1.0))
+    assert torch.equal(outh, C.dense_compressed_attn_fwd(qh, Eh, xh, win_start, sinkh, q_pos, 128, W, 1.0))
     torch.cuda.synchronize()
     g = np.random.default_rng(13)
     fixed = [0, 1, Tq - 1]
