@@ -20,8 +20,10 @@
  *    the caller. Tensors are dense, row-major, with the shapes given below.
  *  - The library never allocates device memory in these calls. Scratch space
  *    is the caller's `ws` buffer, sized by the matching *_workspace_size().
- *  - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
- *    asynchronously; the caller synchronises before reading results.
+ *  - `stream` is the hipStream_t to enqueue on (NULL = the default stream).
+ *    Work is enqueued asynchronously; the caller synchronises before reading
+ *    results. C callers compile with -D__HIP_PLATFORM_AMD__ (the HIP runtime
+ *    header that defines hipStream_t requires it).
  *  - Arguments are validated on the host before anything is launched. On
  *    failure the call returns a non-zero csa_status, launches nothing, and
  *    csa_last_error() holds a description (thread-local). A failed kernel
@@ -32,13 +34,16 @@
  *  - Entry visibility is causal: with compression ratio m, the query at
  *    position p sees entries j < n(p) = min(N, floor((p+1)/m)).
  *  - Results are deterministic: the same inputs give bit-identical outputs.
- *  - Calls are not thread-safe with respect to csa_kernel_timer_*.
+ *    Results and workspace sizes depend only on the arguments: the library
+ *    keeps no mode state between calls.
  */
 #ifndef CSA_HIP_H
 #define CSA_HIP_H
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -85,7 +90,7 @@ const char* csa_version(void);
  * The sign bit of a code is the sign of the input (tiny negatives give -0).
  */
 csa_status csa_quantize_rows(const void* x, csa_dtype in_t, int64_t rows, int32_t width,
-                             void* out, csa_dtype out_t, void* scale, void* stream);
+                             void* out, csa_dtype out_t, void* scale, hipStream_t stream);
 
 /*
  * csa_compress — CSA compressor: overlapped, gated, two-stream, ratio:1
@@ -106,7 +111,7 @@ csa_status csa_quantize_rows(const void* x, csa_dtype in_t, int64_t rows, int32_
  */
 csa_status csa_compress(const void* c_a, const void* c_b, const void* z_a, const void* z_b,
                         csa_dtype in_t, int64_t B, int64_t T, int32_t width, int32_t ratio,
-                        void* out, csa_dtype out_t, void* out_scale, void* stream);
+                        void* out, csa_dtype out_t, void* out_scale, hipStream_t stream);
 
 /*
  * hca_compress — HCA compressor: non-overlapped, gated, single stream,
@@ -118,7 +123,7 @@ csa_status csa_compress(const void* c_a, const void* c_b, const void* z_a, const
  *   width  64 or 128;  ratio 1..4096.
  */
 csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B, int64_t T,
-                        int32_t width, int32_t ratio, void* out, csa_dtype out_t, void* stream);
+                        int32_t width, int32_t ratio, void* out, csa_dtype out_t, hipStream_t stream);
 
 /*
  * csa_compress_append — decode-time step of the CSA compressor (cf-1.com
@@ -144,7 +149,7 @@ csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B,
 csa_status csa_compress_append(const void* c_a, const void* c_b, const void* z_a, const void* z_b,
                                csa_dtype in_t, int64_t B, int32_t width, int32_t ratio, const int32_t* pos,
                                void* state, int64_t N_cap, void* out, csa_dtype out_t, void* out_scale,
-                               void* stream);
+                               hipStream_t stream);
 
 /*
  * hca_compress_append — decode-time step of the HCA compressor (cf-1.com
@@ -163,23 +168,7 @@ csa_status csa_compress_append(const void* c_a, const void* c_b, const void* z_a
  */
 csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int64_t B, int32_t width,
                                int32_t ratio, const int32_t* pos, void* state, int64_t N_cap, void* out,
-                               csa_dtype out_t, void* stream);
-
-/*
- * csa_set_batch_invariant / csa_get_batch_invariant — batch-invariant mode
- * (cf-1.com write-up §4.3: the kernel library is batch-invariant and
- * deterministic). Process-wide switch, off by default. When on, the
- * attention calls (sparse_attn_fwd, dense_compressed_attn_fwd) plan their key
- * splits and tile streams from one sequence's query count Tq instead of the
- * batch's B*Tq, so each sequence's output and LSE are the same bits whatever
- * else is in the batch (the indexer and the compressors already compute each
- * row on its own). Decode batches then use the split count of a single
- * sequence. The workspace-size queries follow the mode: query them after
- * setting it, and do not change it between a query and the call it sizes.
- * Every result is deterministic in both modes.
- */
-csa_status csa_set_batch_invariant(int32_t on);
-int32_t csa_get_batch_invariant(void);
+                               csa_dtype out_t, hipStream_t stream);
 
 /*
  * indexer_topk — lightning-indexer scores and per-query top-k selection
@@ -213,7 +202,7 @@ csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w,
                         const int32_t* q_pos, int64_t B, int64_t Tq, int64_t N,
                         int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
                         int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
-                        void* stream);
+                        hipStream_t stream);
 
 /*
  * indexer_topk_bf16_scores — indexer_topk with bfloat16 index scores
@@ -238,7 +227,28 @@ csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, cons
                                     const int32_t* q_pos, int64_t B, int64_t Tq, int64_t N,
                                     int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
                                     int32_t* idx_out, uint16_t* score_out, void* ws,
-                                    size_t ws_bytes, void* stream);
+                                    size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Options of the two attention calls and their workspace queries, OR-ed into
+ * `flags` (0 = none; other bits are rejected with CSA_ERR_SHAPE):
+ *  CSA_ATTN_WIN_RING         x_win is a ring of T_win rows (cf-1.com write-up
+ *                            §4.4: the window of recent uncompressed tokens is
+ *                            kept as a state cache) and position t is row
+ *                            t mod T_win, for the positions win_start ..
+ *                            win_start + T_win - 1 (csa_window_append keeps
+ *                            it). Without it position t is row t - win_start.
+ *  CSA_ATTN_BATCH_INVARIANT  batch-invariant planning (cf-1.com write-up §4.3:
+ *                            the kernel library is batch-invariant and
+ *                            deterministic): key splits and tile streams are
+ *                            planned from one sequence's query count Tq
+ *                            instead of the batch's B*Tq, so each sequence's
+ *                            output and LSE are the same bits whatever else
+ *                            is in the batch. The workspace query must be
+ *                            given the same flag as the call it sizes.
+ * Every result is deterministic with and without these options.
+ */
+enum { CSA_ATTN_WIN_RING = 1, CSA_ATTN_BATCH_INVARIANT = 2 };
 
 /*
  * sparse_attn_fwd — CSA core attention over the selected compressed entries,
@@ -246,8 +256,8 @@ csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, cons
  * yfxerp.com write-up §3 sliding_window 128, attention_sink).
  * For the query at position p and head h, with keys (= values, one shared KV
  * head for all query heads) K = {kv[s] : s in idx[p], 0 <= s < N} joined with
- * the window rows {x_win[t - win_start] : max(0, p-window+1) <= t <= p,
- * win_start <= t < win_start + T_win}:
+ * the window rows of positions max(0, p-window+1) <= t <= p that x_win holds
+ * (win_start <= t < win_start + T_win):
  *     l_i = scale * q_h . K_i,
  *     o_h = sum_i e^{l_i} K_i / (e^{sink_h} + sum_i e^{l_i}),
  *     lse_h = log(e^{sink_h} + sum_i e^{l_i}).
@@ -255,42 +265,41 @@ csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, cons
  *   q      [B, Tq, H, d] of t (CSA_F32 or CSA_BF16)
  *   kv     [B, N, d] of t;   idx int32 [B, Tq, k]
  *   x_win  [B, T_win, d] of t;  win_start int32 [B]: the first position the
- *          rows hold. win_ring = 0: position t is row t - win_start (rows
- *          hold positions win_start .. win_start + T_win - 1 in order);
- *          win_ring = 1: x_win is a ring of T_win rows (cf-1.com write-up §4.4:
- *          the window of recent uncompressed tokens is kept as a state cache)
- *          and position t is row t mod T_win, for the same positions
- *          win_start .. win_start + T_win - 1 (csa_window_append keeps it).
+ *          rows hold (row layout: see CSA_ATTN_WIN_RING)
  *   sink   float32 [H], or NULL for no sink
  *   q_pos  int32 [B, Tq];  out [B, Tq, H, d] of t;  lse NULL or float32 [B, Tq, H]
+ *   ws     the workspace sparse_attn_workspace_size() returns for the same
+ *          shapes and flags (NULL allowed when it returns 0)
+ *   flags  CSA_ATTN_* options
  *   d == 128; H a multiple of 16, <= 256; 1 <= k <= 4096; window >= 0; B*Tq < 2^31.
- * Accumulation is float32; a query with no keys and no sink gives o = 0.
+ * Accumulation is float32; a query with no keys and no sink gives o = 0 and
+ * lse = -inf.
  */
 size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, int32_t k,
-                                  int32_t window);
+                                  int32_t window, uint32_t flags);
 csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
                            const int32_t* win_start, const float* sink, const int32_t* q_pos,
                            csa_dtype t, int64_t B, int64_t Tq, int64_t N, int64_t T_win,
-                           int32_t win_ring, int32_t H, int32_t d, int32_t k, int32_t window,
-                           float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                           void* stream);
+                           int32_t H, int32_t d, int32_t k, int32_t window, float scale,
+                           void* out, float* lse, void* ws, size_t ws_bytes, uint32_t flags,
+                           hipStream_t stream);
 
 /*
  * dense_compressed_attn_fwd — HCA core attention: every visible compressed
  * entry (j < n(p), dense, no selection), plus the window and the sink
- * (cf-1.com write-up §3.2, §3.3). Same formula and layouts as
+ * (cf-1.com write-up §3.2, §3.3). Same formula, layouts, flags and limits as
  * sparse_attn_fwd with idx = 0..n(p)-1.
  *   ratio >= 1 defines n(p); B*Tq < 2^31.
  */
 size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t d,
-                                 int32_t window);
+                                 int32_t window, uint32_t flags);
 csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* x_win,
                                      const int32_t* win_start, const float* sink,
                                      const int32_t* q_pos, csa_dtype t, int64_t B, int64_t Tq,
-                                     int64_t N, int64_t T_win, int32_t win_ring, int32_t H,
-                                     int32_t d, int32_t ratio, int32_t window, float scale,
-                                     void* out, float* lse, void* ws, size_t ws_bytes,
-                                     void* stream);
+                                     int64_t N, int64_t T_win, int32_t H, int32_t d,
+                                     int32_t ratio, int32_t window, float scale, void* out,
+                                     float* lse, void* ws, size_t ws_bytes, uint32_t flags,
+                                     hipStream_t stream);
 
 /*
  * csa_window_append — one decode step of the window state cache (cf-1.com
@@ -301,11 +310,11 @@ csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* 
  *   pos    int32 [B] >= 0: the token's position
  *   ring   [B, R, d] of t, caller-owned, R >= 1
  * d == 128; x_new and ring 16-byte aligned. After appending position p with
- * R >= window, pass x_win = ring, T_win = R, win_ring = 1 and
+ * R >= window, pass x_win = ring, T_win = R, the CSA_ATTN_WIN_RING flag and
  * win_start = max(0, p - R + 1) to the attention calls.
  */
 csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t d,
-                             const int32_t* pos, void* ring, int64_t R, void* stream);
+                             const int32_t* pos, void* ring, int64_t R, hipStream_t stream);
 
 /*
  * sparse_attn_bwd — gradients of sparse_attn_fwd (cf-1.com write-up §4.3:
@@ -339,7 +348,7 @@ csa_status sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, co
                            int32_t H, int32_t d, int32_t k, int32_t window, float scale,
                            const void* out, const float* lse, const void* dout, void* dq,
                            float* dkv, float* dx_win, float* dsink, void* ws, size_t ws_bytes,
-                           void* stream);
+                           hipStream_t stream);
 
 /*
  * dense_compressed_attn_bwd — gradients of dense_compressed_attn_fwd
@@ -355,30 +364,7 @@ csa_status dense_compressed_attn_bwd(const void* q, const void* kv, const void* 
                                      int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t ratio,
                                      int32_t window, float scale, const void* out, const float* lse,
                                      const void* dout, void* dq, float* dkv, float* dx_win,
-                                     float* dsink, void* ws, size_t ws_bytes, void* stream);
-
-/*
- * Kernel timer (measurement support). csa_kernel_timer_start() arms the
- * library to record a pair of hipEvents around each of the next
- * `max_launches` launches of kernel `kernel_id` (a csa_kernel_id), on the
- * stream the kernel is launched on. csa_kernel_timer_read() waits for the
- * last recorded event, writes up to `capacity` durations in milliseconds and
- * returns how many launches were recorded (negative on error); it disarms the
- * timer. Not for use under stream capture.
- */
-typedef enum {
-  CSA_KID_COMPRESS = 1,
-  CSA_KID_HCA_COMPRESS = 2,
-  CSA_KID_QUANTIZE = 3,
-  CSA_KID_INDEX_SCORE = 4,
-  CSA_KID_TOPK = 5,
-  CSA_KID_SPARSE_ATTN = 6,
-  CSA_KID_DENSE_ATTN = 7,
-  CSA_KID_ATTN_MERGE = 8,
-  CSA_KID_ATTN_BWD = 9
-} csa_kernel_id;
-csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches);
-int32_t csa_kernel_timer_read(float* ms_out, int32_t capacity);
+                                     float* dsink, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

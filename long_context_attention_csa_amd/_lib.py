@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(HERE, "libcsa_hip.so")
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_FP4_E2M1 = 0, 1, 2, 3
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_UNSUPPORTED",
           4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_HIP"}
+ATTN_WIN_RING, ATTN_BATCH_INVARIANT = 1, 2
 KID = {"compress": 1, "hca_compress": 2, "quantize": 3, "index_score": 4, "topk": 5,
        "sparse_attn": 6, "dense_attn": 7, "attn_merge": 8, "attn_bwd": 9}
 
@@ -22,8 +23,9 @@ _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 _F = ctypes.c_float
+_U32 = ctypes.c_uint32
 
-# name -> (restype, argtypes); mirrors include/csa_hip.h
+# name -> (restype, argtypes); mirrors include/csa_hip.h and include/csa_hip_timer.h
 SIGNATURES = {
     "csa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "csa_last_error": (ctypes.c_char_p, []),
@@ -41,21 +43,19 @@ SIGNATURES = {
     "indexer_topk_bf16_scores_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32, ctypes.c_int]),
     "indexer_topk_bf16_scores": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _I32, _I32,
                                                 _I32, _I32, _P, _P, _P, _SZ, _P]),
-    "sparse_attn_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32]),
+    "sparse_attn_workspace_size": (_SZ, [_I64, _I64, _I32, _I32, _I32, _I32, _U32]),
     "sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
-                                       _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+                                       _I32, _I32, _F, _P, _P, _P, _SZ, _U32, _P]),
     "sparse_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
                                        _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "dense_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32]),
     "dense_compressed_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32,
                                                  _I32, _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "dense_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32]),
+    "dense_attn_workspace_size": (_SZ, [_I64, _I64, _I64, _I32, _I32, _I32, _U32]),
     "dense_compressed_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32,
-                                                 _I32, _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _P]),
+                                                 _I32, _I32, _I32, _F, _P, _P, _P, _SZ, _U32, _P]),
     "csa_window_append": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I32, _P, _P, _I64, _P]),
-    "csa_set_batch_invariant": (ctypes.c_int, [_I32]),
-    "csa_get_batch_invariant": (_I32, []),
     "csa_kernel_timer_start": (ctypes.c_int, [_I32, _I32]),
     "csa_kernel_timer_read": (_I32, [ctypes.POINTER(ctypes.c_float), _I32]),
 }

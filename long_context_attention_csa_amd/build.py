@@ -19,7 +19,9 @@ LIB = os.path.join(HERE, "libcsa_hip.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Werror",
+    # the host pass warns that it does not know the device-only feature below
+    "-Wno-unused-command-line-argument",
     # packed fp32 vector instructions stay off (see the design notes)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

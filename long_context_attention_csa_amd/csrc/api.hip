@@ -1,11 +1,15 @@
 // C ABI of libcsa_hip: argument validation, workspace sizing, status strings,
-// kernel timer, and dispatch to the kernels. Contract: include/csa_hip.h.
+// kernel timer, and dispatch to the kernels. Contract: include/csa_hip.h
+// (the timer: include/csa_hip_timer.h).
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
 #include <string>
 
+#include "../../include/csa_hip_timer.h"
 #include "common.hpp"
 
 namespace csa {
@@ -22,42 +26,59 @@ size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes);
 hipError_t launch_indexer_topk(const void*, const void*, const float*, const void*, const void*, csa_dtype,
                                const int32_t*, int64_t, int64_t, int64_t, int, int, int, int, int32_t*, void*, bool,
                                void*, hipStream_t);
-size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max);
+size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max, bool batch_inv);
 size_t attn_bwd_ws_bytes(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window);
 hipError_t launch_attn_bwd(bool sparse, const void* q, const void* kv, const int32_t* idx, const void* x_win,
                            const int32_t* win_start, const float* sink, const int32_t* q_pos, const void* out,
                            const float* lse, const void* dout, int64_t B, int64_t Tq, int64_t N, int64_t T_win,
                            int H, int k, int window, int ratio, float scale, void* dq, float* dkv, float* dx_win,
                            float* dsink, void* ws, hipStream_t s);
-void set_batch_invariant(int on);
-int batch_invariant();
 hipError_t launch_window_append(const void* x_new, csa_dtype t, int64_t B, const int32_t* pos, void* ring,
                                 int64_t R, hipStream_t s);
 hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void* kv, const int32_t* idx,
                             const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                             int64_t B, int64_t Tq, int64_t N, int64_t T_win, int ring, int H, int k, int window,
-                            int ratio, float scale, void* out, float* lse, void* ws, int64_t nk_max, hipStream_t st);
+                            int ratio, float scale, void* out, float* lse, void* ws, int64_t nk_max, bool batch_inv,
+                            hipStream_t st);
 
 // ------------------------------------------------------------------ kernel timer
+// Disarmed by default: a launch then costs one relaxed atomic load. Armed, the
+// events around each launch of the chosen kernel are recorded under a lock.
 namespace {
 constexpr int kMaxTimed = 4096;
 struct Timer {
-  int kid = 0;
+  std::mutex mu;
+  std::atomic<int> kid{0};
   int cap = 0;
   int n = 0;
+  bool open = false;     // a launch's first event is recorded, its second not yet
   hipEvent_t ev[2 * kMaxTimed];
   bool created = false;
 } g_timer;
 }  // namespace
 
+// The thread that records a launch's first event holds the lock until the
+// launch and its second event are enqueued, so the pair brackets that launch.
+thread_local bool t_timer_locked = false;
+
 void timer_before(int kid, hipStream_t s) {
-  if (g_timer.kid == kid && g_timer.n < g_timer.cap) (void)hipEventRecord(g_timer.ev[2 * g_timer.n], s);
+  if (g_timer.kid.load(std::memory_order_relaxed) != kid) return;
+  g_timer.mu.lock();
+  t_timer_locked = true;
+  if (g_timer.kid.load() == kid && g_timer.n < g_timer.cap) {
+    (void)hipEventRecord(g_timer.ev[2 * g_timer.n], s);
+    g_timer.open = true;
+  }
 }
-void timer_after(int kid, hipStream_t s) {
-  if (g_timer.kid == kid && g_timer.n < g_timer.cap) {
+void timer_after(int, hipStream_t s) {
+  if (!t_timer_locked) return;
+  if (g_timer.open) {
     (void)hipEventRecord(g_timer.ev[2 * g_timer.n + 1], s);
     ++g_timer.n;
+    g_timer.open = false;
   }
+  t_timer_locked = false;
+  g_timer.mu.unlock();
 }
 }  // namespace csa
 
@@ -108,7 +129,7 @@ const char* csa_last_error(void) { return g_last_error.c_str(); }
 const char* csa_version(void) { return "csa_hip 0.1 gfx950"; }
 
 csa_status csa_quantize_rows(const void* x, csa_dtype in_t, int64_t rows, int32_t width, void* out, csa_dtype out_t,
-                             void* scale, void* stream) {
+                             void* scale, hipStream_t stream) {
   g_last_error.clear();
   CSA_REQUIRE(is_dtype(in_t) && is_dtype(out_t), CSA_ERR_UNSUPPORTED, "csa_quantize_rows: unknown dtype");
   CSA_REQUIRE(is_float(in_t), CSA_ERR_UNSUPPORTED, "csa_quantize_rows: input must be CSA_F32 or CSA_BF16");
@@ -120,13 +141,13 @@ csa_status csa_quantize_rows(const void* x, csa_dtype in_t, int64_t rows, int32_
               "csa_quantize_rows: width %d must be a multiple of %d", width, out_t == CSA_FP4_E2M1 ? 32 : 8);
   if (rows == 0) return CSA_OK;
   CSA_REQUIRE(x && out && scale, CSA_ERR_NULL, "csa_quantize_rows: x, out and scale are required");
-  return hip_status(launch_quantize_rows(x, in_t, rows, width, out, out_t, scale, (hipStream_t)stream),
+  return hip_status(launch_quantize_rows(x, in_t, rows, width, out, out_t, scale, stream),
                     "csa_quantize_rows");
 }
 
 csa_status csa_compress(const void* c_a, const void* c_b, const void* z_a, const void* z_b, csa_dtype in_t,
                         int64_t B, int64_t T, int32_t width, int32_t ratio, void* out, csa_dtype out_t,
-                        void* out_scale, void* stream) {
+                        void* out_scale, hipStream_t stream) {
   g_last_error.clear();
   CSA_REQUIRE(is_dtype(in_t) && is_dtype(out_t), CSA_ERR_UNSUPPORTED, "csa_compress: unknown dtype");
   CSA_REQUIRE(is_float(in_t), CSA_ERR_UNSUPPORTED, "csa_compress: input must be CSA_F32 or CSA_BF16");
@@ -141,12 +162,12 @@ csa_status csa_compress(const void* c_a, const void* c_b, const void* z_a, const
   CSA_REQUIRE(is_float(out_t) || out_scale, CSA_ERR_NULL, "csa_compress: out_scale required for %s output",
               out_t == CSA_FP8_E4M3 ? "fp8" : "fp4");
   return hip_status(launch_csa_compress(c_a, c_b, z_a, z_b, in_t, B, T, width, ratio, out, out_t, out_scale,
-                                        (hipStream_t)stream),
+                                        stream),
                     "csa_compress");
 }
 
 csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B, int64_t T, int32_t width,
-                        int32_t ratio, void* out, csa_dtype out_t, void* stream) {
+                        int32_t ratio, void* out, csa_dtype out_t, hipStream_t stream) {
   g_last_error.clear();
   CSA_REQUIRE(is_dtype(in_t) && is_dtype(out_t), CSA_ERR_UNSUPPORTED, "hca_compress: unknown dtype");
   CSA_REQUIRE(is_float(in_t) && is_float(out_t), CSA_ERR_UNSUPPORTED,
@@ -157,14 +178,14 @@ csa_status hca_compress(const void* c, const void* z, csa_dtype in_t, int64_t B,
   const int64_t N = T / ratio;
   if (B * N == 0) return CSA_OK;
   CSA_REQUIRE(c && z && out, CSA_ERR_NULL, "hca_compress: NULL tensor");
-  return hip_status(launch_hca_compress(c, z, in_t, B, T, width, ratio, out, out_t, (hipStream_t)stream),
+  return hip_status(launch_hca_compress(c, z, in_t, B, T, width, ratio, out, out_t, stream),
                     "hca_compress");
 }
 
 csa_status csa_compress_append(const void* c_a, const void* c_b, const void* z_a, const void* z_b,
                                csa_dtype in_t, int64_t B, int32_t width, int32_t ratio, const int32_t* pos,
                                void* state, int64_t N_cap, void* out, csa_dtype out_t, void* out_scale,
-                               void* stream) {
+                               hipStream_t stream) {
   g_last_error.clear();
   CSA_REQUIRE(is_dtype(in_t) && is_dtype(out_t), CSA_ERR_UNSUPPORTED, "csa_compress_append: unknown dtype");
   CSA_REQUIRE(is_float(in_t), CSA_ERR_UNSUPPORTED, "csa_compress_append: input must be CSA_F32 or CSA_BF16");
@@ -180,13 +201,13 @@ csa_status csa_compress_append(const void* c_a, const void* c_b, const void* z_a
   CSA_REQUIRE(is_float(out_t) || out_scale, CSA_ERR_NULL, "csa_compress_append: out_scale required for %s output",
               out_t == CSA_FP8_E4M3 ? "fp8" : "fp4");
   return hip_status(launch_csa_append(c_a, c_b, z_a, z_b, in_t, B, width, ratio, pos, state, N_cap, out, out_t,
-                                      out_scale, (hipStream_t)stream),
+                                      out_scale, stream),
                     "csa_compress_append");
 }
 
 csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int64_t B, int32_t width,
                                int32_t ratio, const int32_t* pos, void* state, int64_t N_cap, void* out,
-                               csa_dtype out_t, void* stream) {
+                               csa_dtype out_t, hipStream_t stream) {
   g_last_error.clear();
   CSA_REQUIRE(is_dtype(in_t) && is_dtype(out_t), CSA_ERR_UNSUPPORTED, "hca_compress_append: unknown dtype");
   CSA_REQUIRE(is_float(in_t) && is_float(out_t), CSA_ERR_UNSUPPORTED,
@@ -199,17 +220,9 @@ csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int
   if (B == 0) return CSA_OK;
   CSA_REQUIRE(c && z && pos && state && out, CSA_ERR_NULL, "hca_compress_append: NULL tensor");
   return hip_status(launch_hca_append(c, z, in_t, B, width, ratio, pos, state, N_cap, out, out_t,
-                                      (hipStream_t)stream),
+                                      stream),
                     "hca_compress_append");
 }
-
-csa_status csa_set_batch_invariant(int32_t on) {
-  g_last_error.clear();
-  set_batch_invariant(on);
-  return CSA_OK;
-}
-
-int32_t csa_get_batch_invariant(void) { return batch_invariant(); }
 
 size_t indexer_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t k,
                                    csa_dtype qk_t) {
@@ -229,7 +242,7 @@ static csa_status indexer_common(const char* fn, const void* q_idx, const void* 
                                  const void* k_idx, const void* k_scale, csa_dtype qk_t, const int32_t* q_pos,
                                  int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
                                  int32_t* idx_out, void* score_out, bool bf16, void* ws, size_t ws_bytes,
-                                 void* stream) {
+                                 hipStream_t stream) {
   CSA_REQUIRE(is_dtype(qk_t), CSA_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)qk_t);
   CSA_REQUIRE(B >= 0 && Tq >= 0 && N >= 0 && N < (int64_t(1) << 30) && B * Tq < (int64_t(1) << 31), CSA_ERR_SHAPE,
               "%s: B=%lld Tq=%lld N=%lld", fn, (long long)B, (long long)Tq, (long long)N);
@@ -250,14 +263,14 @@ static csa_status indexer_common(const char* fn, const void* q_idx, const void* 
                            : indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, qk_t);
   CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   return hip_status(launch_indexer_topk(q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio, k,
-                                        idx_out, score_out, bf16, ws, (hipStream_t)stream),
+                                        idx_out, score_out, bf16, ws, stream),
                     fn);
 }
 
 csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
                         const void* k_scale, csa_dtype qk_t, const int32_t* q_pos, int64_t B, int64_t Tq,
                         int64_t N, int32_t H_I, int32_t d_I, int32_t ratio, int32_t k, int32_t* idx_out,
-                        float* score_out, void* ws, size_t ws_bytes, void* stream) {
+                        float* score_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error.clear();
   return indexer_common("indexer_topk", q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio,
                         k, idx_out, score_out, false, ws, ws_bytes, stream);
@@ -267,7 +280,7 @@ csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, cons
                                     const void* k_scale, csa_dtype qk_t, const int32_t* q_pos, int64_t B,
                                     int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t ratio, int32_t k,
                                     int32_t* idx_out, uint16_t* score_out, void* ws, size_t ws_bytes,
-                                    void* stream) {
+                                    hipStream_t stream) {
   g_last_error.clear();
   return indexer_common("indexer_topk_bf16_scores", q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I,
                         d_I, ratio, k, idx_out, score_out, true, ws, ws_bytes, stream);
@@ -293,64 +306,70 @@ static csa_status check_attn_common(const char* fn, const void* q, const void* k
   return CSA_OK;
 }
 
-size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, int32_t k, int32_t window) {
+static constexpr uint32_t kAttnFlags = CSA_ATTN_WIN_RING | CSA_ATTN_BATCH_INVARIANT;
+
+size_t sparse_attn_workspace_size(int64_t B, int64_t Tq, int32_t H, int32_t d, int32_t k, int32_t window,
+                                  uint32_t flags) {
   (void)d;
   if (B <= 0 || Tq <= 0 || H <= 0) return 0;
-  return attn_ws_bytes(B, Tq, H, (int64_t)k + window);
+  return attn_ws_bytes(B, Tq, H, (int64_t)k + window, (flags & CSA_ATTN_BATCH_INVARIANT) != 0);
 }
 
 csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, const void* x_win,
                            const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t, int64_t B,
-                           int64_t Tq, int64_t N, int64_t T_win, int32_t win_ring, int32_t H, int32_t d, int32_t k,
-                           int32_t window, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t k, int32_t window,
+                           float scale, void* out, float* lse, void* ws, size_t ws_bytes, uint32_t flags,
+                           hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_common("sparse_attn_fwd", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win, H, d,
                                     window, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_SHAPE, "sparse_attn_fwd: k %d (1..4096)", k);
-  CSA_REQUIRE(win_ring == 0 || win_ring == 1, CSA_ERR_SHAPE, "sparse_attn_fwd: win_ring %d (0 or 1)", win_ring);
+  CSA_REQUIRE((flags & ~kAttnFlags) == 0, CSA_ERR_SHAPE, "sparse_attn_fwd: unknown flags 0x%x", flags);
   if (B * Tq == 0) return CSA_OK;
   CSA_REQUIRE(idx, CSA_ERR_NULL, "sparse_attn_fwd: idx is NULL");
-  const size_t need = sparse_attn_workspace_size(B, Tq, H, d, k, window);
+  const bool binv = (flags & CSA_ATTN_BATCH_INVARIANT) != 0;
+  // one reading of the options: the size checked here is the one the launch plans with
+  const size_t need = attn_ws_bytes(B, Tq, H, (int64_t)k + window, binv);
   CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE, "sparse_attn_fwd: workspace %zu < %zu bytes",
               ws_bytes, need);
-  return hip_status(launch_attention(true, t, q, kv, idx, x_win, win_start, sink, q_pos, B, Tq, N, T_win, win_ring, H, k,
-                                     window, 1, scale, out, lse, need ? ws : nullptr, (int64_t)k + window,
-                                     (hipStream_t)stream),
+  return hip_status(launch_attention(true, t, q, kv, idx, x_win, win_start, sink, q_pos, B, Tq, N, T_win,
+                                     (flags & CSA_ATTN_WIN_RING) ? 1 : 0, H, k, window, 1, scale, out, lse,
+                                     need ? ws : nullptr, (int64_t)k + window, binv, stream),
                     "sparse_attn_fwd");
 }
 
-size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t d, int32_t window) {
+size_t dense_attn_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H, int32_t d, int32_t window,
+                                 uint32_t flags) {
   (void)d;
   if (B <= 0 || Tq <= 0 || H <= 0) return 0;
-  return attn_ws_bytes(B, Tq, H, N + window);
+  return attn_ws_bytes(B, Tq, H, N + window, (flags & CSA_ATTN_BATCH_INVARIANT) != 0);
 }
 
 csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* x_win, const int32_t* win_start,
                                      const float* sink, const int32_t* q_pos, csa_dtype t, int64_t B, int64_t Tq,
-                                     int64_t N, int64_t T_win, int32_t win_ring, int32_t H, int32_t d, int32_t ratio,
-                                     int32_t window, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t ratio, int32_t window,
+                                     float scale, void* out, float* lse, void* ws, size_t ws_bytes, uint32_t flags,
+                                     hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_common("dense_compressed_attn_fwd", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win,
                                     H, d, window, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "dense_compressed_attn_fwd: ratio %d", ratio);
-  CSA_REQUIRE(win_ring == 0 || win_ring == 1, CSA_ERR_SHAPE, "dense_compressed_attn_fwd: win_ring %d (0 or 1)",
-              win_ring);
+  CSA_REQUIRE((flags & ~kAttnFlags) == 0, CSA_ERR_SHAPE, "dense_compressed_attn_fwd: unknown flags 0x%x", flags);
   if (B * Tq == 0) return CSA_OK;
-  const size_t need = dense_attn_workspace_size(B, Tq, N, H, d, window);
+  const bool binv = (flags & CSA_ATTN_BATCH_INVARIANT) != 0;
+  const size_t need = attn_ws_bytes(B, Tq, H, N + window, binv);
   CSA_REQUIRE(need == 0 || (ws && ws_bytes >= need), CSA_ERR_WORKSPACE,
               "dense_compressed_attn_fwd: workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(launch_attention(false, t, q, kv, nullptr, x_win, win_start, sink, q_pos, B, Tq, N, T_win, win_ring, H, 0,
-                                     window, ratio, scale, out, lse, need ? ws : nullptr, N + window,
-                                     (hipStream_t)stream),
+  return hip_status(launch_attention(false, t, q, kv, nullptr, x_win, win_start, sink, q_pos, B, Tq, N, T_win,
+                                     (flags & CSA_ATTN_WIN_RING) ? 1 : 0, H, 0, window, ratio, scale, out, lse,
+                                     need ? ws : nullptr, N + window, binv, stream),
                     "dense_compressed_attn_fwd");
 }
 
 csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t d, const int32_t* pos, void* ring,
-                             int64_t R, void* stream) {
+                             int64_t R, hipStream_t stream) {
   g_last_error.clear();
   CSA_REQUIRE(is_dtype(t) && is_float(t), CSA_ERR_UNSUPPORTED, "csa_window_append: dtype must be CSA_F32 or CSA_BF16");
   CSA_REQUIRE(d == 128, CSA_ERR_UNSUPPORTED, "csa_window_append: d %d (only 128)", d);
@@ -360,7 +379,7 @@ csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t 
   CSA_REQUIRE(x_new && pos && ring, CSA_ERR_NULL, "csa_window_append: NULL tensor");
   CSA_REQUIRE(((uintptr_t)x_new & 15) == 0 && ((uintptr_t)ring & 15) == 0, CSA_ERR_SHAPE,
               "csa_window_append: x_new and ring must be 16-byte aligned");
-  return hip_status(launch_window_append(x_new, t, B, pos, ring, R, (hipStream_t)stream), "csa_window_append");
+  return hip_status(launch_window_append(x_new, t, B, pos, ring, R, stream), "csa_window_append");
 }
 
 static csa_status check_attn_bwd(const char* fn, const void* q, const void* kv, const void* x_win,
@@ -393,7 +412,7 @@ csa_status sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, co
                            const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t, int64_t B,
                            int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t k, int32_t window,
                            float scale, const void* out, const float* lse, const void* dout, void* dq, float* dkv,
-                           float* dx_win, float* dsink, void* ws, size_t ws_bytes, void* stream) {
+                           float* dx_win, float* dsink, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_bwd("sparse_attn_bwd", q, kv, x_win, win_start, sink, q_pos, t, B, Tq, N, T_win, H, d,
                                  window, out, lse, dout, dq, dkv, dx_win, dsink);
@@ -405,7 +424,7 @@ csa_status sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, co
   CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "sparse_attn_bwd: workspace %zu < %zu bytes", ws_bytes,
               need);
   return hip_status(launch_attn_bwd(true, q, kv, idx, x_win, win_start, sink, q_pos, out, lse, dout, B, Tq, N, T_win,
-                                    H, k, window, 1, scale, dq, dkv, dx_win, dsink, ws, (hipStream_t)stream),
+                                    H, k, window, 1, scale, dq, dkv, dx_win, dsink, ws, stream),
                     "sparse_attn_bwd");
 }
 
@@ -421,7 +440,7 @@ csa_status dense_compressed_attn_bwd(const void* q, const void* kv, const void* 
                                      int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t ratio, int32_t window,
                                      float scale, const void* out, const float* lse, const void* dout, void* dq,
                                      float* dkv, float* dx_win, float* dsink, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_bwd("dense_compressed_attn_bwd", q, kv, x_win, win_start, sink, q_pos, t, B, Tq, N,
                                  T_win, H, d, window, out, lse, dout, dq, dkv, dx_win, dsink);
@@ -433,7 +452,7 @@ csa_status dense_compressed_attn_bwd(const void* q, const void* kv, const void* 
               ws_bytes, need);
   return hip_status(launch_attn_bwd(false, q, kv, nullptr, x_win, win_start, sink, q_pos, out, lse, dout, B, Tq, N,
                                     T_win, H, 0, window, ratio, scale, dq, dkv, dx_win, dsink, ws,
-                                    (hipStream_t)stream),
+                                    stream),
                     "dense_compressed_attn_bwd");
 }
 
@@ -443,6 +462,7 @@ csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches) {
               "csa_kernel_timer_start: kernel id %d", kernel_id);
   CSA_REQUIRE(max_launches >= 1 && max_launches <= kMaxTimed, CSA_ERR_SHAPE,
               "csa_kernel_timer_start: max_launches %d (1..%d)", max_launches, kMaxTimed);
+  std::lock_guard<std::mutex> lock(g_timer.mu);
   if (!g_timer.created) {
     for (int i = 0; i < 2 * kMaxTimed; ++i) {
       hipError_t e = hipEventCreate(&g_timer.ev[i]);
@@ -450,15 +470,16 @@ csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches) {
     }
     g_timer.created = true;
   }
-  g_timer.kid = kernel_id;
   g_timer.cap = max_launches;
   g_timer.n = 0;
+  g_timer.kid.store(kernel_id);
   return CSA_OK;
 }
 
 int32_t csa_kernel_timer_read(float* ms_out, int32_t capacity) {
+  std::lock_guard<std::mutex> lock(g_timer.mu);
   const int n = g_timer.n;
-  g_timer.kid = 0;
+  g_timer.kid.store(0);
   g_timer.cap = 0;
   g_timer.n = 0;
   if (n == 0) return 0;

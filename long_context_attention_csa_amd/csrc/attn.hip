@@ -24,8 +24,6 @@
 // triples are merged in a fixed order, so results are deterministic.
 #include "attn_tile.hpp"
 
-#include <atomic>
-
 namespace csa {
 
 template <typename T> struct AttnTypes;
@@ -425,7 +423,7 @@ __device__ __forceinline__ void attn_tile16(uint32_t tb, const TileLanes& tl, bo
 }
 
 template <bool SPARSE, int NW, int HPW, int NBUF, int TS>
-__global__ __launch_bounds__(NW * TS * 64, TS == 1 ? 2 : 1) void k_attn16(
+__global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_attn16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     const uint16_t* __restrict__ x_win, const int32_t* __restrict__ win_start, const float* __restrict__ sink,
     const int32_t* __restrict__ q_pos, int64_t Tq, int64_t N, int64_t T_win, int wring, int H, int k, int window,
@@ -825,18 +823,16 @@ static AttnPlan plan_attention(int64_t rows, int H, int64_t nk_max) {
   return {(int)(s < 1 ? 1 : s)};
 }
 
-// Batch-invariant mode: the split count and the tile-stream choice are
-// planned from one sequence's rows (Tq) instead of the whole batch (B * Tq),
-// so a sequence's result does not depend on what else is in the batch.
-static std::atomic<int> g_batch_invariant{0};
-void set_batch_invariant(int on) { g_batch_invariant.store(on ? 1 : 0); }
-int batch_invariant() { return g_batch_invariant.load(); }
-static int64_t plan_rows(int64_t B, int64_t Tq) { return g_batch_invariant.load() ? Tq : B * Tq; }
+// Batch-invariant planning (a per-call option): the split count and the
+// tile-stream choice follow one sequence's rows (Tq) instead of the whole
+// batch (B * Tq), so a sequence's result does not depend on what else is in
+// the batch.
+static int64_t plan_rows(int64_t B, int64_t Tq, bool batch_inv) { return batch_inv ? Tq : B * Tq; }
 
 int attn_splits(int64_t rows, int H, int64_t nk_max) { return plan_attention(rows, H, nk_max).S; }
 
-size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max) {
-  const int S = attn_splits(plan_rows(B, Tq), H, nk_max);
+size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max, bool batch_inv) {
+  const int S = attn_splits(plan_rows(B, Tq, batch_inv), H, nk_max);
   if (S == 1) return 0;
   return (size_t)(B * Tq) * H * S * (kD + 2) * 4;
 }
@@ -927,11 +923,12 @@ hipError_t launch_window_append(const void* x_new, csa_dtype t, int64_t B, const
 hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void* kv, const int32_t* idx,
                             const void* x_win, const int32_t* win_start, const float* sink, const int32_t* q_pos,
                             int64_t B, int64_t Tq, int64_t N, int64_t T_win, int wring, int H, int k, int window,
-                            int ratio, float scale, void* out, float* lse, void* ws, int64_t nk_max, hipStream_t st) {
+                            int ratio, float scale, void* out, float* lse, void* ws, int64_t nk_max, bool batch_inv,
+                            hipStream_t st) {
   const int64_t rows = B * Tq;
   if (rows == 0) return hipSuccess;
   const AttnShape sh = pick_shape(H);
-  const int64_t prow = plan_rows(B, Tq);
+  const int64_t prow = plan_rows(B, Tq, batch_inv);
   const AttnPlan pl = plan_attention(prow, H, nk_max);
   const int S = pl.S;
   // two tile streams when the planned grid is small (few rows: decode)

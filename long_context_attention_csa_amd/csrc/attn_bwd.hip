@@ -631,7 +631,7 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 // segment's partial once; k_bwd_seg_reduce adds the segments in order. This
 // replaces a 512-byte contribution row per (query, entry).
 template <int HPW>
-__global__ __launch_bounds__(kBwdThreads, 2) void k_attn_bwd_dense_kv(
+__global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd_dense_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ q_pos,
     const float* __restrict__ Dv, const float* __restrict__ lse, const uint16_t* __restrict__ dout, int64_t Tq,
     int64_t N, int ratio, float scale, int64_t seg, int nseg, float* __restrict__ part) {
@@ -789,6 +789,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_reduce(const float* __restr
                                                             float* __restrict__ dx_win, int accumulate, int win_only) {
   __shared__ float2 part[kBwdThreads / 64][64];
   const int64_t id = blockIdx.x;   // win_only (dense layers): ids are window rows b T_win + t
+  if (id >= nids) return;          // uniform: the grid has one block per id
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const uint32_t u0 = off[id], len = off[id + 1] - u0;
   const uint32_t a = u0 + (uint32_t)(((uint64_t)len * wv) / 4), e = u0 + (uint32_t)(((uint64_t)len * (wv + 1)) / 4);

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include "../../include/csa_hip.h"
+#include "../../include/csa_hip_timer.h"
 
 namespace csa {
 
@@ -153,24 +154,31 @@ __device__ __forceinline__ i32x4 lds_read_b128(uint32_t a) { return *(lds_i32x4*
 // as an LDS store: it would otherwise drain every outstanding load before
 // each later LDS access or barrier (it cannot tell the ring slots apart),
 // which serialises the staging pipeline. Completion is tracked explicitly
-// with wait_vm() followed by a barrier before a slot is read. No register
-// outputs.
+// with wait_vm() followed by a barrier before a slot is read. The LDS base
+// goes through M0, which the compiler reserves: each statement saves M0 in a
+// scratch SGPR and restores it after the issue (the instruction reads M0 when
+// it is issued), so no value the compiler keeps there is lost. No vector
+// register outputs.
 __device__ __forceinline__ void gather_lds16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_base) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_base) : "memory");
 }
 
 // The same with a wave-uniform base address (in scalar registers) and a
 // 32-bit per-lane byte offset: no per-lane 64-bit address arithmetic.
 __device__ __forceinline__ void gather_lds16_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
 }
 
 // One dword per active lane: lane i's 4 bytes at sbase + voff go to LDS
 // address lds_base + 4 * i.
 __device__ __forceinline__ void gather_lds4_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
 }
 
 template <int N_OUT>

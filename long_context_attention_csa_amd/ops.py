@@ -11,7 +11,8 @@ import ctypes
 
 import torch
 
-from ._lib import (CSA_BF16, CSA_F32, CSA_FP4_E2M1, CSA_FP8_E4M3, KID, check, lib)
+from ._lib import (ATTN_BATCH_INVARIANT, ATTN_WIN_RING, CSA_BF16, CSA_F32, CSA_FP4_E2M1, CSA_FP8_E4M3, KID,
+                   check, lib)
 
 FMT = {"f32": CSA_F32, "bf16": CSA_BF16, "fp8": CSA_FP8_E4M3, "fp4": CSA_FP4_E2M1}
 
@@ -140,15 +141,6 @@ def hca_compress_append(c, z, pos, state, out, ratio: int = 128):
                                                            _stream()))
 
 
-def set_batch_invariant(on: bool) -> None:
-    """Batch-invariant mode of the attention calls (process-wide)."""
-    check("csa_set_batch_invariant", lib().csa_set_batch_invariant(1 if on else 0))
-
-
-def batch_invariant() -> bool:
-    return bool(lib().csa_get_batch_invariant())
-
-
 def indexer_topk_workspace_size(B, Tq, N, H_I, d_I, k, fmt: str, bf16_scores: bool = False) -> int:
     fn = lib().indexer_topk_bf16_scores_workspace_size if bf16_scores else lib().indexer_topk_workspace_size
     return int(fn(B, Tq, N, H_I, d_I, k, FMT[fmt]))
@@ -177,15 +169,22 @@ def indexer_topk(q_idx, q_scale, w, k_idx, k_scale, fmt: str, q_pos, ratio: int,
     return (idx_out, scores) if want_scores else idx_out
 
 
-def sparse_attn_workspace_size(B, Tq, H, d, k, window) -> int:
-    return int(lib().sparse_attn_workspace_size(B, Tq, H, d, k, window))
+def _attn_flags(win_ring: bool, batch_invariant: bool) -> int:
+    return (ATTN_WIN_RING if win_ring else 0) | (ATTN_BATCH_INVARIANT if batch_invariant else 0)
+
+
+def sparse_attn_workspace_size(B, Tq, H, d, k, window, batch_invariant: bool = False) -> int:
+    return int(lib().sparse_attn_workspace_size(B, Tq, H, d, k, window, _attn_flags(False, batch_invariant)))
 
 
 def sparse_attn_fwd(q, kv, idx, x_win, win_start, sink, q_pos, window: int = 128, scale: float = 1.0,
-                    want_lse: bool = False, ws=None, out=None, win_ring: bool = False):
+                    want_lse: bool = False, ws=None, out=None, win_ring: bool = False,
+                    batch_invariant: bool = False):
     """CSA core attention. q [B, Tq, H, d], kv [B, N, d], idx int32 [B, Tq, k],
     x_win [B, T_win, d], win_start int32 [B], sink float32 [H] or None, q_pos int32 [B, Tq].
-    win_ring: x_win is a ring holding position t at row t mod T_win."""
+    win_ring: x_win is a ring holding position t at row t mod T_win.
+    batch_invariant: plan the kernel from one sequence's rows (each sequence's
+    result is then the same bits whatever else is in the batch)."""
     _contig(q, kv, idx, x_win, win_start, sink, q_pos)
     t = _float_dtype(q)
     B, Tq, H, d = q.shape
@@ -193,20 +192,21 @@ def sparse_attn_fwd(q, kv, idx, x_win, win_start, sink, q_pos, window: int = 128
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty(B, Tq, H, dtype=torch.float32, device=q.device) if want_lse else None
-    ws, nbytes = _workspace(sparse_attn_workspace_size(B, Tq, H, d, k, window), q.device, ws)
+    ws, nbytes = _workspace(sparse_attn_workspace_size(B, Tq, H, d, k, window, batch_invariant), q.device, ws)
     check("sparse_attn_fwd", lib().sparse_attn_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(x_win), _ptr(win_start),
-                                                   _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, int(win_ring), H, d,
-                                                   k, window,
-                                                   scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
+                                                   _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H, d, k, window,
+                                                   scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+                                                   _attn_flags(win_ring, batch_invariant), _stream()))
     return (out, lse) if want_lse else out
 
 
-def dense_attn_workspace_size(B, Tq, N, H, d, window) -> int:
-    return int(lib().dense_attn_workspace_size(B, Tq, N, H, d, window))
+def dense_attn_workspace_size(B, Tq, N, H, d, window, batch_invariant: bool = False) -> int:
+    return int(lib().dense_attn_workspace_size(B, Tq, N, H, d, window, _attn_flags(False, batch_invariant)))
 
 
 def dense_compressed_attn_fwd(q, kv, x_win, win_start, sink, q_pos, ratio: int = 128, window: int = 128,
-                              scale: float = 1.0, want_lse: bool = False, ws=None, out=None, win_ring: bool = False):
+                              scale: float = 1.0, want_lse: bool = False, ws=None, out=None, win_ring: bool = False,
+                              batch_invariant: bool = False):
     """HCA core attention over all visible entries plus window and sink."""
     _contig(q, kv, x_win, win_start, sink, q_pos)
     t = _float_dtype(q)
@@ -215,10 +215,10 @@ def dense_compressed_attn_fwd(q, kv, x_win, win_start, sink, q_pos, ratio: int =
     if out is None:
         out = torch.empty_like(q)
     lse = torch.empty(B, Tq, H, dtype=torch.float32, device=q.device) if want_lse else None
-    ws, nbytes = _workspace(dense_attn_workspace_size(B, Tq, N, H, d, window), q.device, ws)
+    ws, nbytes = _workspace(dense_attn_workspace_size(B, Tq, N, H, d, window, batch_invariant), q.device, ws)
     check("dense_compressed_attn_fwd", lib().dense_compressed_attn_fwd(
-        _ptr(q), _ptr(kv), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, int(win_ring), H,
-        d, ratio, window, scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _stream()))
+        _ptr(q), _ptr(kv), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H, d, ratio,
+        window, scale, _ptr(out), _ptr(lse), _ptr(ws), nbytes, _attn_flags(win_ring, batch_invariant), _stream()))
     return (out, lse) if want_lse else out
 
 

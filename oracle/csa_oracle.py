@@ -373,6 +373,11 @@ def attend(q, keys, sink, scale: float = 1.0):
     l_i = scale * q_h . key_i; the sink adds no value and is not scaled.
     Shared KV with one KV head for all query heads (MQA).
 
+    A head whose key set is empty and whose sink is -inf (no sink) has no
+    term at all: o = 0 and lse = -inf. This is the limit of the formula as the
+    sink logit goes to -inf with no keys (o is 0 for every finite sink), and
+    the value the library's contract states for that case.
+
     q: [H, d], keys: [n, d], sink: [H]. Returns (o [H, d], lse [H]) in float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -380,10 +385,12 @@ def attend(q, keys, sink, scale: float = 1.0):
     sink = np.asarray(sink, dtype=np.float64)
     logits = scale * (q @ keys.T)                                  # [H, n]
     M = np.maximum(sink, logits.max(axis=1) if keys.shape[0] else -np.inf)
-    e = np.exp(logits - M[:, None])
-    den = np.exp(sink - M) + e.sum(axis=1)
-    o = (e @ keys) / den[:, None]
-    lse = M + np.log(den)
+    empty = M == -np.inf                                           # no key and no sink
+    Ms = np.where(empty, 0.0, M)
+    e = np.exp(logits - Ms[:, None])
+    den = np.exp(sink - Ms) + e.sum(axis=1)
+    o = np.where(empty[:, None], 0.0, (e @ keys) / np.where(empty, 1.0, den)[:, None])
+    lse = np.where(empty, -np.inf, Ms + np.log(np.where(empty, 1.0, den)))
     return o, lse
 
 
@@ -523,36 +530,34 @@ def dense_attn_bwd(q, kv, x_win, win_start: int, sink, q_pos, ratio: int, dout, 
 # ---------------------------------------------------------------------------
 
 
-def csa_layer(inp: dict, k: int, ratio: int = 4, window: int = 128, index_format: str = "f32"):
+def csa_layer(inp: dict, k: int, ratio: int = 4, window: int = 128):
     """One CSA layer forward on one sequence of prefill tokens 0..T-1.
 
-    compress KV streams -> compress indexer streams (and quantise them) ->
-    indexer scores -> top-k -> sparse attention with window and sink.
-    [cf-1 §3.1, §3.3, §3.4]. The window rows are stream A's raw vectors
-    (reading: the pages do not say which raw vector the window uses).
-    index_format: "f32" (no quantisation), "fp8" or "fp4" (queries and keys
-    quantised in the same format, queries per (token, head)).
-    Returns dict with kv, k_i (dequantised), scores, idx, o, lse.
+    compress KV streams -> compress indexer streams -> indexer scores ->
+    top-k -> sparse attention with window and sink, all in float64 (the
+    indexer operands are not quantised here; the quantised formats have their
+    own functions above). [cf-1 §3.1, §3.3, §3.4]. The window rows are stream
+    A's raw vectors (reading: the pages do not say which raw vector the window
+    uses).
+    Returns dict with kv, k_i, scores, idx, o, lse.
     """
     T = inp["c_a"].shape[0]
     kv = csa_compress(inp["c_a"], inp["c_b"], inp["z_a"], inp["z_b"], ratio)
     k_i = csa_compress(inp["ci_a"], inp["ci_b"], inp["zi_a"], inp["zi_b"], ratio)
-    q_i = np.asarray(inp["q_i"], dtype=np.float64)
-    if index_format == "fp8":
-        k_i = dequant_fp8_rows(*quant_fp8_rows(k_i.astype(np.float32)))
-        q_i = dequant_fp8_rows(*quant_fp8_rows(q_i.astype(np.float32)))
-    elif index_format == "fp4":
-        k_i = dequant_mxfp4_rows(*quant_mxfp4_rows(k_i.astype(np.float32)))
-        q_i = dequant_mxfp4_rows(*quant_mxfp4_rows(q_i.astype(np.float32)))
     q_pos = np.arange(T)
-    scores = indexer_scores(q_i, inp["w"], k_i, q_pos, ratio)
+    scores = indexer_scores(inp["q_i"], inp["w"], k_i, q_pos, ratio)
     idx = topk_select(scores, visible_entries(q_pos, ratio, kv.shape[0]), k)
     o, lse = sparse_attn(inp["q"], kv, idx, inp["c_a"], 0, inp["sink"], q_pos, window)
     return {"kv": kv, "k_i": k_i, "scores": scores, "idx": idx, "o": o, "lse": lse}
 
 
 def hca_layer(inp: dict, ratio: int = 128, window: int = 128):
-    """One HCA layer forward on one sequence of prefill tokens 0..T-1 [cf-1 §3.2, §3.3]."""
+    """One HCA layer forward on one sequence of prefill tokens 0..T-1 [cf-1 §3.2, §3.3].
+
+    compress (ratio:1, one stream) -> dense attention over every visible
+    entry, the window rows (the raw stream C, the same reading as CSA's
+    window) and the sink. Returns dict with kv, o, lse.
+    """
     T = inp["c"].shape[0]
     kv = hca_compress(inp["c"], inp["z"], ratio)
     q_pos = np.arange(T)

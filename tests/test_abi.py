@@ -10,14 +10,14 @@ import pytest
 from long_context_attention_csa_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "csa_hip.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("csa_hip.h", "csa_hip_timer.h")]
 
 OK, NULL, SHAPE, UNSUP, WS = 0, 1, 2, 3, 4
 P = ctypes.c_void_p(0x1000)   # a non-NULL pointer that is never dereferenced (validation fails first)
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "while")))
@@ -113,11 +113,11 @@ def test_indexer_bf16_scores_validation():
 def test_attention_validation():
     lib = _lib.lib()
     f = lib.sparse_attn_fwd
-    #       q  kv idx xw ws0 sink pos t  B  Tq N   T_win ring H   d    k   win  scale out lse ws  wsb      stream
-    base = [P, P, P, P, P, None, P, 1, 1, 1, 64, 128, 0, 64, 128, 64, 128, 1.0, P, None, P, 1 << 40, None]
+    #       q  kv idx xw ws0 sink pos t  B  Tq N   T_win H   d    k   win  scale out lse ws  wsb      flags stream
+    base = [P, P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 64, 128, 1.0, P, None, P, 1 << 40, 0, None]
     def call(**kw):
         a = list(base)
-        pos = {"t": 7, "ring": 12, "H": 13, "d": 14, "k": 15, "window": 16, "q": 0, "ws": 20, "wsb": 21, "idx": 2}
+        pos = {"t": 7, "H": 12, "d": 13, "k": 14, "window": 15, "q": 0, "ws": 19, "wsb": 20, "flags": 21, "idx": 2}
         for k_, v in kw.items():
             a[pos[k_]] = v
         return f(*a)
@@ -126,16 +126,24 @@ def test_attention_validation():
     assert call(t=2) == UNSUP
     assert call(k=0) == SHAPE
     assert call(window=-1) == SHAPE
-    assert call(ring=2) == SHAPE
+    assert call(flags=4) == SHAPE      # unknown option bit
+    assert "flags" in _err(lib)
     assert call(q=None) == NULL
     assert call(idx=None) == NULL
     g = lib.dense_compressed_attn_fwd
-    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, 0, 64, 128, 0, 128, 1.0, P, None, P, 1 << 40, None) == SHAPE
-    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, -1, 64, 128, 4, 128, 1.0, P, None, P, 1 << 40, None) == SHAPE
+    #   q  kv xw ws0 sink pos t  B  Tq N   T_win H   d    ratio win scale out lse ws wsb     flags stream
+    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 0, 128, 1.0, P, None, P, 1 << 40, 0, None) == SHAPE
+    assert g(P, P, P, P, None, P, 1, 1, 1, 64, -1, 64, 128, 4, 128, 1.0, P, None, P, 1 << 40, 0, None) == SHAPE
+    assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 4, 128, 1.0, P, None, P, 1 << 40, 8, None) == SHAPE
     # decode shapes need a split workspace
-    need = lib.dense_attn_workspace_size(1, 1, 8192, 128, 128, 128)
+    need = lib.dense_attn_workspace_size(1, 1, 8192, 128, 128, 128, 0)
     assert need > 0
-    assert g(P, P, P, P, None, P, 1, 1, 1, 8192, 128, 1, 128, 128, 128, 128, 1.0, P, None, None, 0, None) == WS
+    assert g(P, P, P, P, None, P, 1, 1, 1, 8192, 128, 128, 128, 128, 128, 1.0, P, None, None, 0, 0, None) == WS
+    # a workspace sized without the batch-invariant flag is too small for a call with it
+    b8 = lib.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128, 0)
+    b8i = lib.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128, 2)
+    assert b8i > b8
+    assert g(P, P, P, P, None, P, 1, 8, 1, 8192, 128, 128, 128, 128, 128, 1.0, P, None, P, b8, 2, None) == WS
 
 
 def test_window_append_validation():
@@ -168,22 +176,19 @@ def test_append_validation():
     assert lib.hca_compress_append(P, P, 1, 2, 128, 128, None, P, 10, P, 1, None) == NULL
 
 
-def test_batch_invariant_switch():
-    """Host logic of the batch-invariant mode: the switch, and the attention
-    workspace of a decode batch that plans each sequence's splits alone."""
+def test_batch_invariant_flag_workspace():
+    """Host logic of batch-invariant planning, a per-call flag: the attention
+    workspace of a decode batch planned per sequence is the sum of the
+    single-sequence workspaces, the default plan's is not, and asking with
+    the flag leaves later queries without it unchanged (no mode state)."""
     from long_context_attention_csa_amd import ops
-    assert not ops.batch_invariant()
     default8 = ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128)
     one = ops.dense_attn_workspace_size(1, 1, 8192, 128, 128, 128)
-    ops.set_batch_invariant(True)
-    try:
-        assert ops.batch_invariant()
-        assert ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128) == 8 * one
-        assert ops.sparse_attn_workspace_size(8, 1, 128, 128, 1024, 128) == \
-            8 * ops.sparse_attn_workspace_size(1, 1, 128, 128, 1024, 128)
-    finally:
-        ops.set_batch_invariant(False)
-    assert not ops.batch_invariant()
+    assert one == ops.dense_attn_workspace_size(1, 1, 8192, 128, 128, 128, batch_invariant=True)
+    assert ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128, batch_invariant=True) == 8 * one
+    assert default8 != 8 * one
+    assert ops.sparse_attn_workspace_size(8, 1, 128, 128, 1024, 128, batch_invariant=True) == \
+        8 * ops.sparse_attn_workspace_size(1, 1, 128, 128, 1024, 128)
     assert ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128) == default8
 
 
@@ -203,3 +208,20 @@ def test_backward_workspace_passes():
     d = lambda Tq, N, T_win: lib.dense_attn_bwd_workspace_size(1, Tq, N, T_win, 64, 128, 128)
     assert 64 * 128 * 512 < d(64, 65536, 256) < 64 * 65536 * 512
     assert d(131072, 1024, 131072) < 6 * (1 << 30)      # 4 GiB of window rows per pass + segment partials
+
+
+def test_headers_compile_as_c(tmp_path):
+    """Both headers are plain C: a C11 translation unit that includes them and
+    takes the address of every declared function compiles with gcc."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi.c"
+    names = declared_functions()
+    body = "\n".join(f"  (void)&{n};" for n in names)
+    src.write_text('#include "csa_hip.h"\n#include "csa_hip_timer.h"\nint main(void) {\n' + body + "\n  return 0;\n}\n")
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-c", str(src),
+                        "-o", str(tmp_path / "abi.o")], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr

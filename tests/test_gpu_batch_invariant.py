@@ -1,7 +1,8 @@
-"""Batch-invariant mode: with it on, a sequence's attention output and LSE are
-the same bits whether it runs alone or inside a batch (decode rows, where the
-default plan splits keys by batch size, and multi-query rows); results still
-match the oracle. The mode is restored to off afterwards."""
+"""Batch-invariant planning (the CSA_ATTN_BATCH_INVARIANT flag of one call): a
+sequence's attention output and LSE are the same bits whether it runs alone or
+inside a batch (decode rows, where the default plan splits keys by batch
+size, and multi-query rows); results still match the oracle. Calls without
+the flag in the same process are unaffected (no mode state)."""
 import numpy as np
 import pytest
 import torch
@@ -23,17 +24,8 @@ def _case(seed, B, Tq, N, H, T_win):
     return q, kv, xw, sink
 
 
-@pytest.fixture
-def invariant_mode():
-    C.set_batch_invariant(True)
-    try:
-        yield
-    finally:
-        C.set_batch_invariant(False)
-
-
 @pytest.mark.parametrize("B,Tq,H", [(5, 1, 128), (3, 6, 64)])
-def test_dense_attn_batch_invariant(invariant_mode, B, Tq, H):
+def test_dense_attn_batch_invariant(B, Tq, H):
     N = 3000
     L = 128 * N + 50
     T_win = 128 + Tq - 1
@@ -43,16 +35,18 @@ def test_dense_attn_batch_invariant(invariant_mode, B, Tq, H):
     args = lambda sl: (dev(q[sl], BF), dev(kv[sl], BF), dev(xw[sl], BF), dev(win_start[sl], torch.int32),
                        dev(sink), dev(q_pos[sl], torch.int32), 128, 128)
     print("dense batch-invariant", B, Tq, H, flush=True)
-    out, lse = C.dense_compressed_attn_fwd(*args(slice(None)), want_lse=True)
+    out, lse = C.dense_compressed_attn_fwd(*args(slice(None)), want_lse=True, batch_invariant=True)
+    plain = C.dense_compressed_attn_fwd(*args(slice(None)))          # interleaved call without the flag
     for b in (0, B - 1):
-        o1, l1 = C.dense_compressed_attn_fwd(*args(slice(b, b + 1)), want_lse=True)
+        o1, l1 = C.dense_compressed_attn_fwd(*args(slice(b, b + 1)), want_lse=True, batch_invariant=True)
         assert torch.equal(out[b:b + 1], o1) and torch.equal(lse[b:b + 1], l1), f"sequence {b}"
+    assert torch.equal(C.dense_compressed_attn_fwd(*args(slice(None))), plain)
     o, _ = O.dense_attn(q[0], kv[0], xw[0], int(win_start[0]), sink, q_pos[0], 128, 128)
     assert_close(host(out)[0], o, "bf16", "dense batch-invariant vs oracle")
 
 
 @pytest.mark.parametrize("B,Tq,H,k", [(4, 1, 128, 1024), (3, 5, 64, 512)])
-def test_sparse_attn_batch_invariant(invariant_mode, B, Tq, H, k):
+def test_sparse_attn_batch_invariant(B, Tq, H, k):
     N = 5000
     T_win = 128 + Tq - 1
     q_pos = np.stack([np.arange(4 * N - Tq, 4 * N) + b for b in range(B)]).astype(np.int32)
@@ -63,9 +57,11 @@ def test_sparse_attn_batch_invariant(invariant_mode, B, Tq, H, k):
     args = lambda sl: (dev(q[sl], BF), dev(kv[sl], BF), dev(idx[sl], torch.int32), dev(xw[sl], BF),
                        dev(win_start[sl], torch.int32), dev(sink), dev(q_pos[sl], torch.int32), 128, 1.0)
     print("sparse batch-invariant", B, Tq, H, k, flush=True)
-    out, lse = C.sparse_attn_fwd(*args(slice(None)), want_lse=True)
+    out, lse = C.sparse_attn_fwd(*args(slice(None)), want_lse=True, batch_invariant=True)
+    plain = C.sparse_attn_fwd(*args(slice(None)))
     for b in (0, B - 1):
-        o1, l1 = C.sparse_attn_fwd(*args(slice(b, b + 1)), want_lse=True)
+        o1, l1 = C.sparse_attn_fwd(*args(slice(b, b + 1)), want_lse=True, batch_invariant=True)
         assert torch.equal(out[b:b + 1], o1) and torch.equal(lse[b:b + 1], l1), f"sequence {b}"
+    assert torch.equal(C.sparse_attn_fwd(*args(slice(None))), plain)
     o, _ = O.sparse_attn(q[0], kv[0], idx[0], xw[0], int(win_start[0]), sink, q_pos[0], 128)
     assert_close(host(out)[0], o, "bf16", "sparse batch-invariant vs oracle")

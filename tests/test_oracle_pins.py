@@ -499,6 +499,76 @@ def test_layer_brute_force_T16(seed):
         assert np.array_equal(sel, sel_ref)
 
 
+def _hca_layer_by_masks(inp, ratio, window):
+    """Second formulation of the HCA layer: compression as a masked softmax over
+    all T tokens per entry, then one masked softmax over [sink | all entries |
+    all raw tokens] with the causal entry mask and the window mask."""
+    c = np.asarray(inp["c"], dtype=np.float64)
+    z = np.asarray(inp["z"], dtype=np.float64)
+    T, d = c.shape
+    N = T // ratio
+    tok = np.arange(T)
+    E = np.zeros((N, d))
+    for j in range(N):
+        m = (tok // ratio) == j
+        logit = np.where(m[:, None], z, -np.inf)
+        wgt = np.exp(logit - logit.max(axis=0))
+        E[j] = (wgt * np.where(m[:, None], c, 0.0)).sum(axis=0) / wgt.sum(axis=0)
+    vis = (ratio * np.arange(N)[None, :] + ratio - 1) <= tok[:, None]          # [T, N]
+    win = (tok[None, :] <= tok[:, None]) & (tok[None, :] > tok[:, None] - window)
+    keys = np.concatenate([E, c], axis=0)
+    mask = np.concatenate([vis, win], axis=1)
+    q = np.asarray(inp["q"], dtype=np.float64)
+    logits = np.where(mask[:, None, :], np.einsum("thd,kd->thk", q, keys), -np.inf)
+    sink = np.broadcast_to(np.asarray(inp["sink"], np.float64)[None, :, None], (T, q.shape[1], 1))
+    allz = np.concatenate([sink, logits], axis=2)
+    p = np.exp(allz - allz.max(axis=2, keepdims=True))
+    p = p / p.sum(axis=2, keepdims=True)
+    return E, np.einsum("thk,kd->thd", p[:, :, 1:], keys)
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("T,ratio,window", [(64, 8, 16), (72, 8, 1), (384, 128, 128), (300, 128, 7)])
+def test_hca_layer_brute_force(seed, T, ratio, window):
+    """Whole HCA layer (ratio 8 at T = 64 and 72, ratio 128 at T = 384 and 300,
+    trailing partial blocks included): the oracle's gather formulation equals
+    the mask formulation, entries and outputs."""
+    inp = syn.hca_prefill(700 + seed, T=T, H=2, bf16=False, d=8)
+    got = O.hca_layer(inp, ratio=ratio, window=window)
+    E_ref, o_ref = _hca_layer_by_masks(inp, ratio, window)
+    np.testing.assert_allclose(got["kv"], E_ref, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(got["o"], o_ref, rtol=1e-12, atol=1e-13)
+
+
+def test_empty_key_set_without_sink_is_zero():
+    """No key and no sink: o = 0 and lse = -inf, the limit of the finite-sink
+    values (o = 0 for every finite sink with no keys, lse = sink), computed
+    without a floating-point warning."""
+    g = np.random.default_rng(5)
+    H, d = 3, 6
+    q = g.standard_normal((H, d))
+    none = np.zeros((0, d))
+    with np.errstate(all="raise"):
+        o, lse = O.attend(q, none, np.full(H, -np.inf))
+        assert np.all(o == 0) and np.all(lse == -np.inf)
+        for s in (-1e3, 0.0, 2.5):
+            o_f, l_f = O.attend(q, none, np.full(H, s))
+            assert np.all(o_f == 0) and np.allclose(l_f, s)
+        # mixed heads: one with a sink, one without, over the same key
+        keys = g.standard_normal((1, d))
+        o2, l2 = O.attend(q[:2], keys, np.array([-np.inf, 0.4]))
+        np.testing.assert_allclose(o2[0], keys[0], rtol=1e-15)          # a single key: weight 1
+        e = np.exp(q[1] @ keys[0])
+        np.testing.assert_allclose(o2[1], e * keys[0] / (np.exp(0.4) + e), rtol=1e-14)
+        np.testing.assert_allclose(l2[0], q[0] @ keys[0], rtol=1e-14)
+    # in the sparse layer: a row with no selected entry and a window of 0
+    kv = g.standard_normal((5, d))
+    q3 = g.standard_normal((2, H, d))
+    idx = np.array([[-1, -1], [0, 4]])
+    o3, l3 = O.sparse_attn(q3, kv, idx, np.zeros((1, d)), 0, np.full(H, -np.inf), np.array([0, 9]), window=0)
+    assert np.all(o3[0] == 0) and np.all(l3[0] == -np.inf) and np.all(np.isfinite(o3[1]))
+
+
 # ---------------------------------------------------------------- attention backward
 
 def _sparse_case(seed, Tq=4, H=2, d=5, N=7, T_win=6, k=3, win_start=2):
