@@ -22,7 +22,7 @@ hipError_t launch_csa_append(const void*, const void*, const void*, const void*,
 hipError_t launch_hca_append(const void*, const void*, csa_dtype, int64_t, int, int, const int32_t*, void*, int64_t,
                              void*, csa_dtype, hipStream_t);
 hipError_t launch_quantize_rows(const void*, csa_dtype, int64_t, int, void*, csa_dtype, void*, hipStream_t);
-size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes);
+size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes, int d_I, csa_dtype fmt, int k);
 hipError_t launch_indexer_topk(const void*, const void*, const float*, const void*, const void*, csa_dtype,
                                const int32_t*, int64_t, int64_t, int64_t, int, int, int, int, int32_t*, void*, bool,
                                void*, hipStream_t);
@@ -226,16 +226,16 @@ csa_status hca_compress_append(const void* c, const void* z, csa_dtype in_t, int
 
 size_t indexer_topk_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I, int32_t k,
                                    csa_dtype qk_t) {
-  (void)H_I; (void)d_I; (void)k; (void)qk_t;
+  (void)H_I;
   if (B <= 0 || Tq <= 0 || N < 0) return 0;
-  return indexer_ws_bytes(B, Tq, N, 4);
+  return indexer_ws_bytes(B, Tq, N, 4, d_I, qk_t, k);
 }
 
 size_t indexer_topk_bf16_scores_workspace_size(int64_t B, int64_t Tq, int64_t N, int32_t H_I, int32_t d_I,
                                                int32_t k, csa_dtype qk_t) {
-  (void)H_I; (void)d_I; (void)k; (void)qk_t;
+  (void)H_I;
   if (B <= 0 || Tq <= 0 || N < 0) return 0;
-  return indexer_ws_bytes(B, Tq, N, 2);
+  return indexer_ws_bytes(B, Tq, N, 2, d_I, qk_t, k);
 }
 
 static csa_status indexer_common(const char* fn, const void* q_idx, const void* q_scale, const float* w,

@@ -206,6 +206,30 @@ __device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
   return v;
 }
 
+// Wave-wide maximum of an unsigned value, in every lane (DPP row rotations,
+// then the two permlane swaps across rows).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x128, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x124, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x122, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x121, 0xf, 0xf, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max((uint32_t)a[0], (uint32_t)a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max((uint32_t)c[0], (uint32_t)c[1]);
+}
+
+// Selection composite of entry i with order key `key`: larger composite =
+// earlier in the total order (score descending, index ascending); 0 marks
+// "no entry" (below every real composite: an order key is never 0 for a
+// finite score).
+__device__ __forceinline__ unsigned long long composite(uint32_t key, int64_t i) {
+  return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
+}
+__device__ __forceinline__ int composite_index(unsigned long long c) {
+  return (int)(0xffffffffu - (uint32_t)(c & 0xffffffffu));
+}
+
 // ------------------------------------------------------------------ score kernel
 // grid.x: entry chunk (chunk_entries entries each), grid.y: query group
 // (QB consecutive queries of one sequence), 256 threads (4 waves).
@@ -404,12 +428,21 @@ __device__ __forceinline__ uint32_t transpose_rows_bytes(uint32_t w, int lane) {
   return __builtin_amdgcn_perm(b[1], b[0], ((lane >> 4) & 1) ? 0x07030501u : 0x06020400u);
 }
 
-template <int FMT, int HB, int NB, int DEPTH, typename SC>
+//
+// Selection summary (LT > 0, the list mode): instead of group maxima, each
+// wave leaves the LT largest selection composites of its 64 * NB entries
+// (score key, inverted index; 0 past the visible entries), largest first, at
+// lbase + (r - lrow0) * (4 X LT) + (4 x + w) LT. Each lane sorts its NB
+// composites; then LT rounds take the wave's largest head (a wave maximum of
+// the keys, and of the inverted indices among lanes that tie on the key) and
+// the lane that held it moves to its next composite. The top-k selection then
+// reads these lists (k_topk_lists) instead of the group maxima.
+template <int FMT, int HB, int NB, int DEPTH, int LT, typename SC>
 __global__ __launch_bounds__(256) void k_index_score_dec(
     const void* __restrict__ q_idx, const void* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k_idx, const void* __restrict__ k_scale, const int32_t* __restrict__ q_pos,
     int64_t Tq, int64_t N, int H_I, int ratio, int64_t row_begin, SC* __restrict__ sbase, int64_t srow0,
-    float* __restrict__ gbase, int64_t grow0) {
+    float* __restrict__ gbase, int64_t grow0, unsigned long long* __restrict__ lbase, int64_t lrow0) {
   constexpr int DI = 128;
   constexpr int RB = FMT == CSA_FP4_E2M1 ? DI / 2 : DI;    // bytes per key row
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -513,7 +546,8 @@ __global__ __launch_bounds__(256) void k_index_score_dec(
     return part;
   };
 
-  float out_s[NB], out_g[NB];
+  float out_s[NB];
+  [[maybe_unused]] float out_g[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     __builtin_amdgcn_sched_barrier(0);   // keep the ring: no load hoisted across batches
@@ -528,18 +562,64 @@ __global__ __launch_bounds__(256) void k_index_score_dec(
     float s = reduce_scatter4(p0, p1, p2, p3);
     if constexpr (FMT == CSA_FP8_E4M3) s *= d.sc;
     s = ScoreT<SC>::round(s);
-    const bool ok = batch_base(i) + lane < nvis;
     out_s[i] = s;
-    out_g[i] = max_row16(ok ? s : -INFINITY);
+    if constexpr (LT == 0) {
+      const bool ok = batch_base(i) + lane < nvis;
+      out_g[i] = max_row16(ok ? s : -INFINITY);
+    }
   }
-  const int64_t G = (N + kGroup - 1) / kGroup;
   SC* srow = sbase + (r - srow0) * N;
-  float* grow = gbase + (r - grow0) * G;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int64_t e0 = batch_base(i);
     if (e0 + lane < nvis) ScoreT<SC>::store(srow, e0 + lane, out_s[i]);
-    if (col == 0 && e0 + 16 * g < nvis) grow[(e0 + 16 * g) / kGroup] = out_g[i];
+  }
+  if constexpr (LT == 0) {
+    const int64_t G = (N + kGroup - 1) / kGroup;
+    float* grow = gbase + (r - grow0) * G;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t e0 = batch_base(i);
+      if (col == 0 && e0 + 16 * g < nvis) grow[(e0 + 16 * g) / kGroup] = out_g[i];
+    }
+  } else {
+    static_assert(NB == 4 && LT <= 64, "list mode sorts four composites per lane");
+    unsigned long long c[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int64_t e = batch_base(i) + lane;
+      c[i] = e < nvis ? composite(order_key(out_s[i]), e) : 0ull;
+    }
+    auto cas = [](unsigned long long& a, unsigned long long& b) {   // a >= b afterwards
+      const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
+      a = hi;
+      b = lo;
+    };
+    cas(c[0], c[1]); cas(c[2], c[3]); cas(c[0], c[2]); cas(c[1], c[3]); cas(c[1], c[2]);
+    unsigned long long mine = 0ull;
+#pragma unroll
+    for (int t = 0; t < LT; ++t) {
+      const uint32_t hk = (uint32_t)(c[0] >> 32), hi = (uint32_t)c[0];
+      const uint32_t mk = wave_max_u32(hk);
+      const unsigned long long tied = __ballot(hk == mk);
+      uint32_t mi;
+      if (__popcll(tied) == 1) {   // wave-uniform; the usual case: one lane holds the key
+        mi = __builtin_amdgcn_readlane(hi, __ffsll((long long)tied) - 1);
+      } else {
+        mi = wave_max_u32(hk == mk ? hi : 0u);
+      }
+      const unsigned long long top = ((unsigned long long)mk << 32) | mi;
+      if (lane == t) mine = top;
+      if (c[0] == top) {   // the lane that held it (all lanes once every composite is 0)
+        c[0] = c[1];
+        c[1] = c[2];
+        c[2] = c[3];
+        c[3] = 0ull;
+      }
+    }
+    const int64_t X = gridDim.x;
+    unsigned long long* lrow = lbase + (r - lrow0) * (4 * X * LT) + ((int64_t)blockIdx.x * 4 + wv) * LT;
+    if (lane < LT) lrow[lane] = mine;
   }
 }
 
@@ -779,13 +859,6 @@ struct TopkSmem {
   unsigned long long prefix, mask, thresh;
   int done;
 };
-
-__device__ __forceinline__ unsigned long long composite(uint32_t key, int64_t i) {
-  return ((unsigned long long)key << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
-}
-__device__ __forceinline__ int composite_index(unsigned long long c) {
-  return (int)(0xffffffffu - (uint32_t)(c & 0xffffffffu));
-}
 
 // Bucket of the target-th largest element of sm.hist (bins scanned from the
 // top); sets sm.bin and sm.need = target - (count in higher bins).
@@ -1318,6 +1391,254 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_select(const SC* __restri
   write_sorted(sm, k, n, out);
 }
 
+// ------------------------------------------------------------------ list mode
+// One block per row (kTopkThreads threads). The score kernel left, for each
+// wave w of the row, the LT largest composites of the wave's entries, largest
+// first (0 past the visible entries). Let C be the k-th largest composite of
+// the union of the lists (exact: composites are distinct). If no wave's LT-th
+// composite reaches C, then every entry >= C is listed (an unlisted entry of
+// wave w is below w's LT-th composite, hence below C), so the listed
+// composites >= C are exactly the row's top-k. Otherwise the waves whose
+// LT-th composite is >= C ("full" waves) may hold more entries >= C: their
+// unlisted entries >= C are read from the stored scores, and the top-k is
+// selected exactly among the listed composites >= C and those entries (all
+// entries >= C are among them, and there are at least k). Rows whose lists
+// do not fit the kernel's bounds take the full-row path.
+//
+// C comes from a linear 4096-bin histogram of the composites' keys over
+// [min, max] (a monotone map): composites in bins above the bin b of the k-th
+// largest are chosen; those of bin b are compacted and each is ranked among
+// them by one thread. The chosen entries are marked in a bitmap of the row
+// (rows of at most 32 * 8192 entries) and written in ascending order after
+// one block scan. Each phase costs a few barriers and at most one LDS round
+// trip per wave (per-lane counts go through a wave prefix sum and one
+// atomic per wave), because a block per row is latency-bound.
+constexpr int kListPerThread = 16;
+constexpr int kListCap = kListPerThread * kTopkThreads;   // composites per row
+constexpr int kListFullWaves = 64;                        // full waves read back at most
+constexpr int64_t kListMaxN = (int64_t)32 * kHistBins;    // entries covered by the bitmap
+
+template <int LT, typename SC>
+__global__ __launch_bounds__(kTopkThreads) void k_topk_lists(const SC* __restrict__ sbase, int64_t srow0,
+                                                             const unsigned long long* __restrict__ lbase,
+                                                             int64_t lrow0, int64_t X, int64_t row0,
+                                                             const int32_t* __restrict__ q_pos, int64_t N, int ratio,
+                                                             int k, int32_t* __restrict__ idx_out) {
+  __shared__ TopkSmem sm;
+  static_assert(kTopkThreads % LT == 0, "a wave's last slot sits in a fixed thread residue");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t r = row0 + blockIdx.x;
+  const int64_t n = visible(q_pos[r], ratio, N);
+  int32_t* out = idx_out + r * (int64_t)k;
+  if (n <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const SC* srow = sbase + (r - srow0) * N;
+  auto full_row = [&]() {   // uniform call sites, after a barrier
+    select_full_row(sm, srow, n, k);
+    __syncthreads();
+    write_sorted(sm, k, n, out);
+  };
+  // lists of the score blocks that saw visible entries (block x's first
+  // entry is 256 x)
+  const int64_t xv = (n + 255) / 256 < X ? (n + 255) / 256 : X;
+  const int64_t nl = xv * 4 * LT;
+  if (nl > kListCap || n > kListMaxN) {   // uniform
+    full_row();
+    return;
+  }
+  const unsigned long long* lrow = lbase + (r - lrow0) * (4 * X * LT);
+  // 1. composites: slot j * kTopkThreads + tid (coalesced loads). Slot sl is
+  //    the (sl % LT)-th of wave sl / LT; this thread's slots all share the
+  //    residue tid % LT.
+  unsigned long long cv[kListPerThread];
+#pragma unroll
+  for (int j = 0; j < kListPerThread; ++j) {
+    const int64_t sl = (int64_t)j * kTopkThreads + tid;
+    cv[j] = sl < nl ? lrow[sl] : 0ull;
+  }
+  const bool last_slot = (tid % LT) == LT - 1;
+  // 2. clear the histogram and the bitmap; key range and count of the nonzero
+  //    composites (wave reductions, one LDS word each per wave)
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(sm.cand);   // kHistBins words, cand[0 .. kMaxCand)
+  unsigned long long* blist = sm.cand + kMaxCand;             // composites of bin b
+  for (int i = tid; i < kGBins; i += kTopkThreads) sm.hist[i] = 0u;
+  for (int i = tid; i < kHistBins; i += kTopkThreads) bitmap[i] = 0u;
+  if (tid == 0) { sm.nsel = 0; sm.ngrp = 0; sm.ncand = 0; sm.thresh = 1ull; }
+  uint32_t kmin = 0xffffffffu, kmax = 0u, nzw = 0u;
+#pragma unroll
+  for (int j = 0; j < kListPerThread; ++j) {
+    const uint32_t key = (uint32_t)(cv[j] >> 32);
+    const bool nz = cv[j] != 0ull;
+    if (nz) { kmin = min(kmin, key); kmax = max(kmax, key); }
+    nzw += (uint32_t)__popcll(__ballot(nz));
+  }
+  kmax = wave_max_u32(kmax);
+  kmin = ~wave_max_u32(~kmin);
+  uint32_t* rmax = reinterpret_cast<uint32_t*>(sm.redg);
+  uint32_t* rmin = reinterpret_cast<uint32_t*>(sm.redf);
+  if (lane == 0) { rmax[wv] = kmax; rmin[wv] = kmin; sm.wsum[wv] = nzw; }
+  __syncthreads();
+  uint32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    kmax = max(kmax, rmax[w]);
+    kmin = min(kmin, rmin[w]);
+    total += sm.wsum[w];
+  }
+  const float inv = (float)kGBins / ((float)(kmax - kmin) + 1.f);
+  auto bin_of = [&](uint32_t key) -> int {   // monotone in key
+    const int t = (int)((float)(key - kmin) * inv);
+    return t > kGBins - 1 ? kGBins - 1 : t;
+  };
+  // 3. histogram of the nonzero composites
+  int bn[kListPerThread];
+#pragma unroll
+  for (int j = 0; j < kListPerThread; ++j) {
+    bn[j] = cv[j] != 0ull ? bin_of((uint32_t)(cv[j] >> 32)) : -1;
+    if (bn[j] >= 0) atomicAdd(&sm.hist[bn[j]], 1u);
+  }
+  __syncthreads();
+  // With fewer than k listed composites, C stays 1: every listed one qualifies.
+  if (total >= (uint32_t)k) {   // uniform
+    // 4. bin b of the k-th largest composite
+    find_bin4096(sm, sm.hist, (uint32_t)k);
+    const int b = (int)sm.bin;
+    const uint32_t need = sm.need;
+    const uint32_t nb = sm.hist[b];
+    if (nb > (uint32_t)(kCandCap - kMaxCand)) {   // uniform: a huge tie on one key range
+      __syncthreads();
+      full_row();
+      return;
+    }
+    // 5. composites above bin b are chosen (marked now); those of bin b are
+    //    compacted (a wave prefix sum of per-lane counts, one atomic per wave)
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kListPerThread; ++j) {
+      cnt += bn[j] == b;
+      if (bn[j] > b) {
+        const int e = composite_index(cv[j]);
+        atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+      }
+    }
+    const uint32_t incl = wave_incl_sum(cnt);
+    const uint32_t wtot = __builtin_amdgcn_readlane(incl, 63);
+    uint32_t base = 0;
+    if (wtot != 0) {   // uniform
+      if (lane == 0) base = atomicAdd(reinterpret_cast<uint32_t*>(&sm.nsel), wtot);
+      base = __builtin_amdgcn_readfirstlane(base);
+    }
+    uint32_t pos = base + incl - cnt;
+#pragma unroll
+    for (int j = 0; j < kListPerThread; ++j)
+      if (bn[j] == b) blist[pos++] = cv[j];
+    __syncthreads();
+    // 6. rank of each bin-b composite among them (one thread each): C is the
+    //    need-th largest; the need largest are chosen
+    for (uint32_t e = tid; e < nb; e += kTopkThreads) {
+      const unsigned long long c = blist[e];
+      uint32_t rank = 0;
+#pragma unroll 8
+      for (uint32_t i = 0; i < nb; ++i) rank += blist[i] > c;
+      if (rank == need - 1) sm.thresh = c;   // exactly one composite has this rank
+      if (rank < need) {
+        const int ei = composite_index(c);
+        atomicOr(&bitmap[ei >> 5], 1u << (ei & 31));
+      }
+    }
+    __syncthreads();
+  }
+  // 7. full waves: those whose last slot (LT-th composite) is >= C
+  const unsigned long long C = sm.thresh;
+  {
+    uint32_t nf = 0;
+#pragma unroll
+    for (int j = 0; j < kListPerThread; ++j) nf += (uint32_t)__popcll(__ballot(last_slot && cv[j] != 0ull && cv[j] >= C));
+    if (lane == 0 && nf != 0) atomicAdd(&sm.ngrp, (int)nf);
+  }
+  __syncthreads();
+  const int nfull = sm.ngrp;
+  // (nfull == 0 implies total >= k: with C = 1 a wave without a full list has
+  // every visible entry listed, so no full wave would mean total = n > k)
+  if (nfull == 0 && total >= (uint32_t)k) {   // uniform: exactly k composites are marked
+    // 8. the chosen entries in ascending order: each thread counts the bits of
+    //    its kHistBins / kTopkThreads bitmap words, one block scan places them
+    constexpr int WPT = kHistBins / kTopkThreads;
+    uint32_t wd[WPT], c = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) { wd[j] = bitmap[tid * WPT + j]; c += __popc(wd[j]); }
+    uint32_t tot;
+    uint32_t o = block_scan_excl(c, sm.wsum, tot);
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      uint32_t x = wd[j];
+      while (x) {
+        const int bit = __ffs((int)x) - 1;
+        out[o++] = (tid * WPT + j) * 32 + bit;
+        x &= x - 1u;
+      }
+    }
+    return;
+  }
+  if (nfull > kListFullWaves) {   // uniform: many full waves (ties, ordered scores)
+    full_row();
+    return;
+  }
+  // 9. (rare) the full waves, by their id sl / LT
+  int* full = reinterpret_cast<int*>(sm.sel);
+  __syncthreads();   // every thread has read nfull
+  if (tid == 0) sm.ngrp = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kListPerThread; ++j) {
+    const int64_t sl = (int64_t)j * kTopkThreads + tid;
+    const int slot = wave_append(last_slot && cv[j] != 0ull && cv[j] >= C, &sm.ngrp);
+    if (slot >= 0) full[slot] = (int)(sl / LT);
+  }
+  // 10. candidates: the listed composites >= C, then the unlisted entries >= C
+  //     of the full waves (entries 64 (w' + 4 (x + X i)) + lane, i < 4, of
+  //     wave 4 x + w'); the order of discovery does not matter below
+#pragma unroll
+  for (int j = 0; j < kListPerThread; ++j) {
+    const int slot = wave_append(cv[j] != 0ull && cv[j] >= C, &sm.ncand);
+    if (slot >= 0 && slot < kCandCap) sm.cand[slot] = cv[j];
+  }
+  __syncthreads();
+  for (int f = wv; f < nfull; f += kTopkThreads / 64) {   // one full wave per wave of the block
+    const int wid = full[f];
+    const int64_t x = wid / 4, wq = wid % 4;
+    const unsigned long long floor_c = lrow[(int64_t)wid * LT + LT - 1];   // its LT-th composite
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t e = 64 * (wq + 4 * (x + X * i)) + lane;
+      unsigned long long c = 0ull;
+      if (e < n) c = composite(order_key(ScoreT<SC>::load(srow, e)), e);
+      const int slot = wave_append(c != 0ull && c >= C && c < floor_c, &sm.ncand);
+      if (slot >= 0 && slot < kCandCap) sm.cand[slot] = c;
+    }
+  }
+  __syncthreads();
+  const int ncand = sm.ncand;
+  __syncthreads();
+  if (ncand > kCandCap) {   // uniform
+    full_row();
+    return;
+  }
+  // 11. exact top-k among the candidates (at least k: every entry >= C is one)
+  if (tid == 0) {
+    sm.nsel = 0;
+    sm.prefix = 0ull;
+    sm.mask = 0ull;
+    sm.need = (uint32_t)k;
+    sm.done = 0;
+  }
+  __syncthreads();
+  take_top_candidates(sm, ncand);
+  write_sorted(sm, k, n, out);
+}
+
 // ------------------------------------------------------------------ short rows
 // Rows of n <= kSmallN scores (used for a whole launch when N <= kSmallN, e.g.
 // prefill rows over the compressed entries of a 64k-token sequence): one
@@ -1660,16 +1981,33 @@ __global__ __launch_bounds__(kSmallThreads) void k_topk_small(const SC* __restri
 struct IndexPlan {
   int QB;
   int64_t groups_per_batch, groups, chunk_entries, groups_per_pass, max_rows_per_pass;
+  bool dec;          // one query per block row: k_index_score_dec
+  int lt;            // list mode (k_topk_lists): composites kept per wave, 0 = group maxima
+  int64_t dec_x;     // decode grid width (blocks of 256 * kDecNB entries per row)
 };
 
-static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N, int sbytes) {
+constexpr int kDecNB = 4, kDecDepth = 2;   // decode score kernel: batches per wave, ring depth
+
+static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N, int sbytes, int d_I, csa_dtype fmt, int k) {
   IndexPlan p;
   p.QB = Tq >= 4 ? 4 : 1;
   p.groups_per_batch = cdiv(Tq, p.QB);
   p.groups = B * p.groups_per_batch;
+  p.dec = p.QB == 1 && d_I == 128 && (fmt == CSA_FP8_E4M3 || fmt == CSA_FP4_E2M1);
+  p.dec_x = cdiv(N > 0 ? N : 1, (int64_t)256 * kDecNB);
+  // List mode for long decode rows: each wave of 256 entries keeps its LT
+  // largest composites. About lambda = 256 k / N of a row's top-k fall in one
+  // wave; LT covers lambda with a margin that leaves a wave full (more than
+  // LT of its entries in the top-k, read back from the scores) rarely: LT 8
+  // for lambda <= 1.25, 16 for lambda <= 5.
+  p.lt = 0;
+  if (p.dec && N > kSmallN) {
+    const int lt = (int64_t)1024 * k <= 5 * N ? 8 : ((int64_t)256 * k <= 5 * N ? 16 : 0);
+    if (lt > 0 && 4 * p.dec_x * lt <= kListCap && N <= kListMaxN) p.lt = lt;
+  }
   // Score buffer budget per pass: 1 GiB.
   const int64_t budget = (int64_t)1 << 30;
-  const int64_t row_bytes = (N > 0 ? N : 1) * sbytes + ((N + kGroup - 1) / kGroup) * 4;
+  const int64_t row_bytes = (N > 0 ? N : 1) * sbytes + ((N + kGroup - 1) / kGroup) * 4 + 4 * p.dec_x * p.lt * 8;
   int64_t gpp = budget / (row_bytes * p.QB);
   if (gpp < 1) gpp = 1;
   if (gpp > 65535) gpp = 65535;
@@ -1691,14 +2029,18 @@ static IndexPlan make_plan(int64_t B, int64_t Tq, int64_t N, int sbytes) {
 static int64_t groups_of(int64_t N) { return (N + kGroup - 1) / kGroup; }
 
 // Workspace: per pass, the scores [rows, N] (sbytes each: 4 for float32, 2 for
-// bf16) and, from the next 256-byte boundary, the group maxima [rows, G].
+// bf16); from the next 256-byte boundary the group maxima [rows, G]; then,
+// from the next 256-byte boundary, the list-mode composites [rows, 4 X LT].
 static size_t score_area(const IndexPlan& p, int64_t N, int sbytes) {
   return ((size_t)p.max_rows_per_pass * (size_t)N * (size_t)sbytes + 255) / 256 * 256;
 }
-size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes) {
-  const IndexPlan p = make_plan(B, Tq, N, sbytes);
-  const size_t rows = (size_t)p.max_rows_per_pass;
-  return score_area(p, N, sbytes) + rows * (size_t)groups_of(N) * 4 + 256;
+static size_t group_area(const IndexPlan& p, int64_t N) {
+  return ((size_t)p.max_rows_per_pass * (size_t)groups_of(N) * 4 + 255) / 256 * 256;
+}
+size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes, int d_I, csa_dtype fmt, int k) {
+  const IndexPlan p = make_plan(B, Tq, N, sbytes, d_I, fmt, k);
+  const size_t lists = (size_t)p.max_rows_per_pass * (size_t)(4 * p.dec_x * p.lt) * 8;
+  return score_area(p, N, sbytes) + group_area(p, N) + lists + 256;
 }
 
 // Batch shape of the key stream per format and queries per block (from
@@ -1710,20 +2052,31 @@ template <int FMT, int QB> struct ScoreCfg {
   static constexpr bool DBUF = false;
 };
 
-// Decode score kernel shape: 4 batches of 64 entries per wave, 2-deep ring
-// (sweep at the 1M-context fp4 and 262k-context fp8 decode shapes).
-constexpr int kDecNB = 4, kDecDepth = 2;
+// Decode score kernel shape (kDecNB, kDecDepth above): 4 batches of 64
+// entries per wave, 2-deep ring (sweep at the 1M-context fp4 and 262k-context
+// fp8 decode shapes).
+
+template <int FMT, int LT, typename SC>
+static void launch_score_dec_lt(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
+                                const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
+                                int ratio, int64_t r0, SC* sb, int64_t sr0, float* gb, int64_t gr0,
+                                unsigned long long* lb, int64_t lr0) {
+  switch (HB) {
+    case 1: k_index_score_dec<FMT, 1, kDecNB, kDecDepth, LT, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0, lb, lr0); break;
+    case 2: k_index_score_dec<FMT, 2, kDecNB, kDecDepth, LT, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0, lb, lr0); break;
+    case 3: k_index_score_dec<FMT, 3, kDecNB, kDecDepth, LT, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0, lb, lr0); break;
+    default: k_index_score_dec<FMT, 4, kDecNB, kDecDepth, LT, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0, lb, lr0); break;
+  }
+}
 
 template <int FMT, typename SC>
-static void launch_score_dec(int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
+static void launch_score_dec(int LT, int HB, dim3 grid, hipStream_t s, const void* q, const void* qs, const float* w,
                              const void* kk, const void* ks, const int32_t* qp, int64_t Tq, int64_t N, int H_I,
-                             int ratio, int64_t r0, SC* sb, int64_t sr0, float* gb, int64_t gr0) {
-  switch (HB) {
-    case 1: k_index_score_dec<FMT, 1, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
-    case 2: k_index_score_dec<FMT, 2, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
-    case 3: k_index_score_dec<FMT, 3, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
-    default: k_index_score_dec<FMT, 4, kDecNB, kDecDepth, SC><<<grid, 256, 0, s>>>(q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0); break;
-  }
+                             int ratio, int64_t r0, SC* sb, int64_t sr0, float* gb, int64_t gr0,
+                             unsigned long long* lb, int64_t lr0) {
+  if (LT == 8) launch_score_dec_lt<FMT, 8, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0, lb, lr0);
+  else if (LT == 16) launch_score_dec_lt<FMT, 16, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0, lb, lr0);
+  else launch_score_dec_lt<FMT, 0, SC>(HB, grid, s, q, qs, w, kk, ks, qp, Tq, N, H_I, ratio, r0, sb, sr0, gb, gr0, lb, lr0);
 }
 
 template <int FMT, int DI, int HB, int QB, typename SC>
@@ -1785,10 +2138,12 @@ static hipError_t run_indexer(const void* q_idx, const void* q_scale, const floa
                               int64_t N, int H_I, int d_I, int ratio, int k, int32_t* idx_out, SC* score_out,
                               void* ws, hipStream_t s) {
   constexpr int SB = (int)sizeof(SC);
-  const IndexPlan p = make_plan(B, Tq, N, SB);
+  const IndexPlan p = make_plan(B, Tq, N, SB, d_I, fmt, k);
   const int HB = (H_I + 15) / 16;
-  // group maxima follow the pass's score rows in the workspace
-  float* gb = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + score_area(p, N, SB));
+  // group maxima and list composites follow the pass's score rows in the workspace
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  float* gb = reinterpret_cast<float*>(wsb + score_area(p, N, SB));
+  unsigned long long* lb = reinterpret_cast<unsigned long long*>(wsb + score_area(p, N, SB) + group_area(p, N));
   for (int64_t g0 = 0; g0 < p.groups; g0 += p.groups_per_pass) {
     const int64_t g1 = (g0 + p.groups_per_pass) < p.groups ? (g0 + p.groups_per_pass) : p.groups;
     const int64_t rlo = (g0 / p.groups_per_batch) * Tq + (g0 % p.groups_per_batch) * p.QB;
@@ -1799,15 +2154,14 @@ static hipError_t run_indexer(const void* q_idx, const void* q_scale, const floa
     SC* sb = score_out ? score_out : reinterpret_cast<SC*>(ws);
     const int64_t sr0 = score_out ? 0 : rlo;
     const int64_t gr0 = rlo;
-    const bool dec = p.QB == 1 && d_I == 128 && (fmt == CSA_FP8_E4M3 || fmt == CSA_FP4_E2M1);
-    if (N > 0 && dec) {
+    if (N > 0 && p.dec) {
       // one query per block row: rows rlo .. rlo + (g1 - g0)
-      const dim3 grid((unsigned)cdiv(N, (int64_t)256 * kDecNB), (unsigned)(g1 - g0));
+      const dim3 grid((unsigned)p.dec_x, (unsigned)(g1 - g0));
       timer_before(CSA_KID_INDEX_SCORE, s);
       if (fmt == CSA_FP8_E4M3)
-        launch_score_dec<CSA_FP8_E4M3, SC>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
+        launch_score_dec<CSA_FP8_E4M3, SC>(p.lt, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0, lb, rlo);
       else
-        launch_score_dec<CSA_FP4_E2M1, SC>(HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0);
+        launch_score_dec<CSA_FP4_E2M1, SC>(p.lt, HB, grid, s, q_idx, q_scale, w, k_idx, k_scale, q_pos, Tq, N, H_I, ratio, rlo, sb, sr0, gb, gr0, lb, rlo);
       hipError_t e = hipGetLastError();
       timer_after(CSA_KID_INDEX_SCORE, s);
       if (e != hipSuccess) return e;
@@ -1824,12 +2178,16 @@ static hipError_t run_indexer(const void* q_idx, const void* q_scale, const floa
       timer_after(CSA_KID_INDEX_SCORE, s);
       if (e != hipSuccess) return e;
     }
+    const dim3 tgrid((unsigned)(rhi - rlo));
     timer_before(CSA_KID_TOPK, s);
     if (N <= kSmallN)   // every row is short: one 256-thread block per row
-      k_topk_small<SC><<<dim3((unsigned)(rhi - rlo)), kSmallThreads, 0, s>>>(sb, sr0, rlo, q_pos, N, ratio, k, idx_out);
+      k_topk_small<SC><<<tgrid, kSmallThreads, 0, s>>>(sb, sr0, rlo, q_pos, N, ratio, k, idx_out);
+    else if (p.lt == 8)
+      k_topk_lists<8, SC><<<tgrid, kTopkThreads, 0, s>>>(sb, sr0, lb, rlo, p.dec_x, rlo, q_pos, N, ratio, k, idx_out);
+    else if (p.lt == 16)
+      k_topk_lists<16, SC><<<tgrid, kTopkThreads, 0, s>>>(sb, sr0, lb, rlo, p.dec_x, rlo, q_pos, N, ratio, k, idx_out);
     else
-      k_topk_select<SC><<<dim3((unsigned)(rhi - rlo)), kTopkThreads, 0, s>>>(sb, sr0, gb, gr0, rlo, q_pos, N, ratio,
-                                                                            k, idx_out);
+      k_topk_select<SC><<<tgrid, kTopkThreads, 0, s>>>(sb, sr0, gb, gr0, rlo, q_pos, N, ratio, k, idx_out);
     hipError_t e = hipGetLastError();
     timer_after(CSA_KID_TOPK, s);
     if (e != hipSuccess) return e;
