@@ -285,6 +285,26 @@ csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, co
                            hipStream_t stream);
 
 /*
+ * sparse_attn_fwd_noalloc — sparse_attn_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, formula, layouts, flags, limits and
+ * results as sparse_attn_fwd, without ws / ws_bytes: the split partial results
+ * go to a scratch array of sparse_attn_noalloc_scratch_bytes() bytes (32 MiB)
+ * that the library holds on each GPU it runs on, from the library's load until
+ * the process ends. Shapes whose sparse_attn_workspace_size() exceeds it are
+ * rejected with CSA_ERR_WORKSPACE before anything is launched. The call makes
+ * no allocation (no hipMalloc, hipFree or allocating library routine). Every
+ * call on one GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ */
+size_t sparse_attn_noalloc_scratch_bytes(void);
+csa_status sparse_attn_fwd_noalloc(const void* q, const void* kv, const int32_t* idx, const void* x_win,
+                                   const int32_t* win_start, const float* sink, const int32_t* q_pos,
+                                   csa_dtype t, int64_t B, int64_t Tq, int64_t N, int64_t T_win,
+                                   int32_t H, int32_t d, int32_t k, int32_t window, float scale,
+                                   void* out, float* lse, uint32_t flags, hipStream_t stream);
+
+/*
  * dense_compressed_attn_fwd — HCA core attention: every visible compressed
  * entry (j < n(p), dense, no selection), plus the window and the sink
  * (cf-1.com write-up §3.2, §3.3). Same formula, layouts, flags and limits as

@@ -368,6 +368,68 @@ csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* 
                     "dense_compressed_attn_fwd");
 }
 
+// ------------------------------------------------------------------ allocation-free variant
+// Scratch for sparse_attn_fwd_noalloc: a file-scope device array that each GPU
+// holds from module load until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in): the device
+// address is looked up once per device with hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+static csa_status scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  CSA_REQUIRE(dev >= 0 && dev < kMaxDevices, CSA_ERR_UNSUPPORTED, "%s: device %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
+size_t sparse_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+csa_status sparse_attn_fwd_noalloc(const void* q, const void* kv, const int32_t* idx, const void* x_win,
+                                   const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t,
+                                   int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t k,
+                                   int32_t window, float scale, void* out, float* lse, uint32_t flags,
+                                   hipStream_t stream) {
+  g_last_error.clear();
+  csa_status st = check_attn_common("sparse_attn_fwd_noalloc", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win,
+                                    H, d, window, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_SHAPE, "sparse_attn_fwd_noalloc: k %d (1..4096)", k);
+  CSA_REQUIRE((flags & ~kAttnFlags) == 0, CSA_ERR_SHAPE, "sparse_attn_fwd_noalloc: unknown flags 0x%x", flags);
+  if (B * Tq == 0) return CSA_OK;
+  CSA_REQUIRE(idx, CSA_ERR_NULL, "sparse_attn_fwd_noalloc: idx is NULL");
+  const bool binv = (flags & CSA_ATTN_BATCH_INVARIANT) != 0;
+  const size_t need = attn_ws_bytes(B, Tq, H, (int64_t)k + window, binv);
+  CSA_REQUIRE(need <= kNoAllocScratchBytes, CSA_ERR_WORKSPACE,
+              "sparse_attn_fwd_noalloc: these shapes need %zu bytes of scratch, more than the %zu bytes the "
+              "library holds per device (use sparse_attn_fwd with a workspace)",
+              need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address("sparse_attn_fwd_noalloc", &ws);
+    if (st != CSA_OK) return st;
+  }
+  return hip_status(launch_attention(true, t, q, kv, idx, x_win, win_start, sink, q_pos, B, Tq, N, T_win,
+                                     (flags & CSA_ATTN_WIN_RING) ? 1 : 0, H, k, window, 1, scale, out, lse, ws,
+                                     (int64_t)k + window, binv, stream),
+                    "sparse_attn_fwd_noalloc");
+}
+
 csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t d, const int32_t* pos, void* ring,
                              int64_t R, hipStream_t stream) {
   g_last_error.clear();

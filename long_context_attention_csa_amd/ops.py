@@ -200,6 +200,27 @@ def sparse_attn_fwd(q, kv, idx, x_win, win_start, sink, q_pos, window: int = 128
     return (out, lse) if want_lse else out
 
 
+def sparse_attn_noalloc_scratch_bytes() -> int:
+    return int(lib().sparse_attn_noalloc_scratch_bytes())
+
+
+def sparse_attn_fwd_noalloc(q, kv, idx, x_win, win_start, sink, q_pos, window: int = 128, scale: float = 1.0,
+                            out=None, lse=None, win_ring: bool = False, batch_invariant: bool = False):
+    """sparse_attn_fwd without a workspace: the library's per-device scratch holds
+    the split results. The caller passes the outputs (out [B, Tq, H, d], lse
+    float32 [B, Tq, H] or None) to allocate nothing in the call."""
+    _contig(q, kv, idx, x_win, win_start, sink, q_pos, out, lse)
+    t = _float_dtype(q)
+    B, Tq, H, d = q.shape
+    N, T_win, k = kv.shape[1], x_win.shape[1], idx.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    check("sparse_attn_fwd_noalloc", lib().sparse_attn_fwd_noalloc(
+        _ptr(q), _ptr(kv), _ptr(idx), _ptr(x_win), _ptr(win_start), _ptr(sink), _ptr(q_pos), t, B, Tq, N, T_win, H,
+        d, k, window, scale, _ptr(out), _ptr(lse), _attn_flags(win_ring, batch_invariant), _stream()))
+    return out
+
+
 def dense_attn_workspace_size(B, Tq, N, H, d, window, batch_invariant: bool = False) -> int:
     return int(lib().dense_attn_workspace_size(B, Tq, N, H, d, window, _attn_flags(False, batch_invariant)))
 
