@@ -205,6 +205,19 @@ csa_status indexer_topk(const void* q_idx, const void* q_scale, const float* w,
                         hipStream_t stream);
 
 /*
+ * indexer_scores — the score stage of indexer_topk on its own (cf-1.com
+ * write-up §3.1, §3.4): I(p,s) for every visible entry s < n(p), exactly as
+ * indexer_topk computes them (same kernels, same bits), written to
+ * score_out float32 [B, Tq, N] (entries >= n(p) untouched); no selection and
+ * no workspace. Arguments, layouts, limits and errors are those of
+ * indexer_topk without k, idx_out and the workspace.
+ */
+csa_status indexer_scores(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
+                          const void* k_scale, csa_dtype qk_t, const int32_t* q_pos, int64_t B, int64_t Tq,
+                          int64_t N, int32_t H_I, int32_t d_I, int32_t ratio, float* score_out,
+                          hipStream_t stream);
+
+/*
  * indexer_topk_bf16_scores — indexer_topk with bfloat16 index scores
  * (cf-1.com write-up §4.4: quantising the index scores from FP32 to BF16
  * halves the selector's score traffic at a small recall cost).

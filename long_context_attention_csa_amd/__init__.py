@@ -6,7 +6,7 @@ thin binding that marshals torch tensors into it.
 from .ops import (csa_append_state, csa_compress, csa_compress_append,  # noqa: F401
                   csa_quantize_rows, dense_attn_bwd_workspace_size, dense_attn_workspace_size,
                   dense_compressed_attn_bwd, dense_compressed_attn_fwd, hca_append_state,
-                  hca_compress, hca_compress_append, indexer_topk, indexer_topk_workspace_size,
+                  hca_compress, hca_compress_append, indexer_scores, indexer_topk, indexer_topk_workspace_size,
                   kernel_timer_read, kernel_timer_start, sparse_attn_bwd,
                   sparse_attn_bwd_workspace_size, sparse_attn_fwd, sparse_attn_fwd_noalloc,
                   sparse_attn_noalloc_scratch_bytes, sparse_attn_workspace_size,

@@ -26,6 +26,8 @@ size_t indexer_ws_bytes(int64_t B, int64_t Tq, int64_t N, int sbytes, int d_I, c
 hipError_t launch_indexer_topk(const void*, const void*, const float*, const void*, const void*, csa_dtype,
                                const int32_t*, int64_t, int64_t, int64_t, int, int, int, int, int32_t*, void*, bool,
                                void*, hipStream_t);
+hipError_t launch_indexer_scores(const void*, const void*, const float*, const void*, const void*, csa_dtype,
+                                 const int32_t*, int64_t, int64_t, int64_t, int, int, int, float*, hipStream_t);
 size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max, bool batch_inv);
 size_t attn_bwd_ws_bytes(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window);
 hipError_t launch_attn_bwd(bool sparse, const void* q, const void* kv, const int32_t* idx, const void* x_win,
@@ -264,6 +266,30 @@ static csa_status indexer_common(const char* fn, const void* q_idx, const void* 
   CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   return hip_status(launch_indexer_topk(q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio, k,
                                         idx_out, score_out, bf16, ws, stream),
+                    fn);
+}
+
+csa_status indexer_scores(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
+                          const void* k_scale, csa_dtype qk_t, const int32_t* q_pos, int64_t B, int64_t Tq, int64_t N,
+                          int32_t H_I, int32_t d_I, int32_t ratio, float* score_out, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "indexer_scores";
+  CSA_REQUIRE(is_dtype(qk_t), CSA_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)qk_t);
+  CSA_REQUIRE(B >= 0 && Tq >= 0 && N >= 0 && N < (int64_t(1) << 30) && B * Tq < (int64_t(1) << 31), CSA_ERR_SHAPE,
+              "%s: B=%lld Tq=%lld N=%lld", fn, (long long)B, (long long)Tq, (long long)N);
+  CSA_REQUIRE(H_I >= 1 && H_I <= 64, CSA_ERR_UNSUPPORTED, "%s: H_I %d (1..64)", fn, H_I);
+  CSA_REQUIRE(d_I == 64 || d_I == 128, CSA_ERR_UNSUPPORTED, "%s: d_I %d (64 or 128)", fn, d_I);
+  CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "%s: ratio %d", fn, ratio);
+  const bool quant = qk_t == CSA_FP8_E4M3 || qk_t == CSA_FP4_E2M1;
+  CSA_REQUIRE(quant || (q_scale == nullptr && k_scale == nullptr), CSA_ERR_SHAPE,
+              "%s: q_scale/k_scale must be NULL for float operands", fn);
+  if (B * Tq == 0 || N == 0) return CSA_OK;
+  CSA_REQUIRE(q_idx && w && q_pos && k_idx && score_out, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  CSA_REQUIRE(!quant || (q_scale && k_scale), CSA_ERR_NULL, "%s: scales required", fn);
+  CSA_REQUIRE(((uintptr_t)q_idx & 15) == 0 && ((uintptr_t)k_idx & 15) == 0 && ((uintptr_t)k_scale & 3) == 0,
+              CSA_ERR_SHAPE, "%s: q_idx and k_idx must be 16-byte aligned, k_scale 4-byte aligned", fn);
+  return hip_status(launch_indexer_scores(q_idx, q_scale, w, k_idx, k_scale, qk_t, q_pos, B, Tq, N, H_I, d_I, ratio,
+                                          score_out, stream),
                     fn);
 }
 

@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void k_index_score(
         const float gm = max_row16(ok ? part : -INFINITY);
         const int64_t r = b * Tq + t0 + qi;
         if (g == 0 && ok) ScoreT<SC>::store(sbase, (r - srow0) * N + e, part);
-        if (lane == 0 && e0 < nvis[qi]) gbase[(r - grow0) * G + e0 / kGroup] = gm;
+        if (gbase && lane == 0 && e0 < nvis[qi]) gbase[(r - grow0) * G + e0 / kGroup] = gm;
       }
     }
   };
@@ -575,6 +575,7 @@ __global__ __launch_bounds__(256) void k_index_score_dec(
     if (e0 + lane < nvis) ScoreT<SC>::store(srow, e0 + lane, out_s[i]);
   }
   if constexpr (LT == 0) {
+    if (gbase == nullptr) return;   // scores only (indexer_scores)
     const int64_t G = (N + kGroup - 1) / kGroup;
     float* grow = gbase + (r - grow0) * G;
 #pragma unroll
@@ -775,7 +776,7 @@ __global__ __launch_bounds__(256) void k_index_score_pf(
   auto store_prev = [&]() {
     if (live_q && prev_e >= 0) {
       if (prev_e + lane < nvw) ScoreT<SC>::store(srow, prev_e + lane, prev_s);
-      if (col == 0 && prev_e + 16 * g < nvw) grow[(prev_e + 16 * g) / kGroup] = prev_g;
+      if (gbase && col == 0 && prev_e + 16 * g < nvw) grow[(prev_e + 16 * g) / kGroup] = prev_g;
     }
   };
   for (int st = 0; st < S; ++st) {
@@ -2138,12 +2139,15 @@ static hipError_t run_indexer(const void* q_idx, const void* q_scale, const floa
                               int64_t N, int H_I, int d_I, int ratio, int k, int32_t* idx_out, SC* score_out,
                               void* ws, hipStream_t s) {
   constexpr int SB = (int)sizeof(SC);
-  const IndexPlan p = make_plan(B, Tq, N, SB, d_I, fmt, k);
+  const bool scores_only = idx_out == nullptr;   // the score stage alone, into score_out
+  IndexPlan p = make_plan(B, Tq, N, SB, d_I, fmt, k);
+  if (scores_only) p.lt = 0;
   const int HB = (H_I + 15) / 16;
   // group maxima and list composites follow the pass's score rows in the workspace
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-  float* gb = reinterpret_cast<float*>(wsb + score_area(p, N, SB));
-  unsigned long long* lb = reinterpret_cast<unsigned long long*>(wsb + score_area(p, N, SB) + group_area(p, N));
+  float* gb = scores_only ? nullptr : reinterpret_cast<float*>(wsb + score_area(p, N, SB));
+  unsigned long long* lb =
+      scores_only ? nullptr : reinterpret_cast<unsigned long long*>(wsb + score_area(p, N, SB) + group_area(p, N));
   for (int64_t g0 = 0; g0 < p.groups; g0 += p.groups_per_pass) {
     const int64_t g1 = (g0 + p.groups_per_pass) < p.groups ? (g0 + p.groups_per_pass) : p.groups;
     const int64_t rlo = (g0 / p.groups_per_batch) * Tq + (g0 % p.groups_per_batch) * p.QB;
@@ -2178,6 +2182,7 @@ static hipError_t run_indexer(const void* q_idx, const void* q_scale, const floa
       timer_after(CSA_KID_INDEX_SCORE, s);
       if (e != hipSuccess) return e;
     }
+    if (scores_only) continue;
     const dim3 tgrid((unsigned)(rhi - rlo));
     timer_before(CSA_KID_TOPK, s);
     if (N <= kSmallN)   // every row is short: one 256-thread block per row
@@ -2193,6 +2198,14 @@ static hipError_t run_indexer(const void* q_idx, const void* q_scale, const floa
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_indexer_scores(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,
+                                 const void* k_scale, csa_dtype fmt, const int32_t* q_pos, int64_t B, int64_t Tq,
+                                 int64_t N, int H_I, int d_I, int ratio, float* score_out, hipStream_t s) {
+  if (B * Tq == 0 || N == 0) return hipSuccess;
+  return run_indexer<float>(q_idx, q_scale, w, k_idx, k_scale, fmt, q_pos, B, Tq, N, H_I, d_I, ratio, 1, nullptr,
+                            score_out, nullptr, s);
 }
 
 hipError_t launch_indexer_topk(const void* q_idx, const void* q_scale, const float* w, const void* k_idx,

@@ -173,6 +173,20 @@ def _attn_flags(win_ring: bool, batch_invariant: bool) -> int:
     return (ATTN_WIN_RING if win_ring else 0) | (ATTN_BATCH_INVARIANT if batch_invariant else 0)
 
 
+def indexer_scores(q_idx, q_scale, w, k_idx, k_scale, fmt: str, q_pos, ratio: int, d_I: int, out=None):
+    """The indexer's score stage alone: float32 scores [B, Tq, N] for the visible
+    entries (the rest of `out` is left as it was)."""
+    _contig(q_idx, q_scale, w, k_idx, k_scale, q_pos, out)
+    B, Tq, H_I = q_idx.shape[:3]
+    N = k_idx.shape[1]
+    if out is None:
+        out = torch.zeros(B, Tq, N, dtype=torch.float32, device=q_idx.device)
+    check("indexer_scores", lib().indexer_scores(_ptr(q_idx), _ptr(q_scale), _ptr(w), _ptr(k_idx), _ptr(k_scale),
+                                                 FMT[fmt], _ptr(q_pos), B, Tq, N, H_I, d_I, ratio, _ptr(out),
+                                                 _stream()))
+    return out
+
+
 def sparse_attn_workspace_size(B, Tq, H, d, k, window, batch_invariant: bool = False) -> int:
     return int(lib().sparse_attn_workspace_size(B, Tq, H, d, k, window, _attn_flags(False, batch_invariant)))
 

@@ -162,3 +162,30 @@ def test_benchmarked_decode_step_graph_replay():
             assert torch.equal(st[n], ref[n]), f"replay {rep}: {n}"
         st["step"](0)          # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("fmt,Tq,N,d_I,H_I", [("fp4", 1, 262144, 128, 64), ("fp8", 2, 40000, 128, 64),
+                                              ("fp8", 300, 5000, 128, 64), ("f32", 40, 3000, 64, 4)])
+def test_score_stage_alone_equals_topk_scores(fmt, Tq, N, d_I, H_I):
+    """indexer_scores writes the bits indexer_topk writes as its scores, and
+    leaves the entries past n(p) untouched."""
+    B = 2
+    qi32 = dev(syn.normal(840, (B, Tq, H_I, d_I)))
+    ki32 = dev(syn.normal(841, (B, N, d_I)))
+    if fmt == "f32":
+        qc, qs, kc, ks = qi32, None, ki32, None
+    else:
+        qc, qs = C.csa_quantize_rows(qi32, fmt)
+        kc, ks = C.csa_quantize_rows(ki32, fmt)
+    w = dev(syn.uniform(842, (B, Tq, H_I)))
+    q_pos = dev(np.stack([np.linspace(N, 4 * N + 9, Tq).astype(np.int32) - 5 * b for b in range(B)]), torch.int32)
+    _, sc = C.indexer_topk(qc, qs, w, kc, ks, fmt, q_pos, 4, 64, d_I, want_scores=True)
+    out = torch.full((B, Tq, N), -7.0, dtype=torch.float32, device="cuda")
+    C.indexer_scores(qc, qs, w, kc, ks, fmt, q_pos, 4, d_I, out=out)
+    n_vis = np.minimum(N, (host(q_pos).astype(np.int64) + 1) // 4)
+    got, ref = host(out), host(sc)
+    for b in range(B):
+        for t in range(Tq):
+            n = n_vis[b, t]
+            assert np.array_equal(got[b, t, :n].view(np.uint32), ref[b, t, :n].view(np.uint32)), (b, t)
+            assert np.all(got[b, t, n:] == -7.0)
