@@ -340,7 +340,7 @@ csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* 
  * their KV forms the window branch): ring[b, pos[b] mod R] = x_new[b].
  *   x_new  [B, d] of t (CSA_F32 or CSA_BF16): the new token's window row
  *          (the raw KV vector that the attention reads as a window key)
- *   pos    int32 [B] >= 0: the token's position
+ *   pos    int32 [B]: the token's position; a negative position skips the sequence
  *   ring   [B, R, d] of t, caller-owned, R >= 1
  * d == 128; x_new and ring 16-byte aligned. After appending position p with
  * R >= window, pass x_win = ring, T_win = R, the CSA_ATTN_WIN_RING flag and
@@ -348,6 +348,50 @@ csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* 
  */
 csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t d,
                              const int32_t* pos, void* ring, int64_t R, hipStream_t stream);
+
+/*
+ * State cache for resuming at a prefix (cf-1.com write-up §4.4: the KV cache
+ * is split into a state cache and a classical KV cache, with three trade-offs
+ * for the recent uncompressed tokens: full SWA caching, periodic
+ * checkpointing every 1024 tokens, zero SWA caching). A sequence's state
+ * cache is its decode-time rings: the window ring [B, R, d]
+ * (csa_window_append), the CSA compressor ring [B, 2*ratio, 4, width] and the
+ * HCA compressor ring [B, ratio, 2, width] (csa_compress_append,
+ * hca_compress_append); the compressed entries are the classical cache. Each
+ * call below treats one ring tensor, seq_bytes (or row_bytes) per sequence,
+ * as bytes: a multiple of 16, 16-byte aligned; B <= 65535.
+ *
+ * csa_state_checkpoint — periodic checkpointing. After the token at position
+ * pos[b] has been appended, a sequence with pos[b] >= 0 and
+ * (pos[b] + 1) % period == 0 copies its ring, state[b] (seq_bytes), to
+ * ckpt[b, (pos[b] + 1) / period - 1] (skipped past n_slots); other sequences
+ * are untouched. ckpt: [B, n_slots, seq_bytes] bytes, caller-owned.
+ */
+csa_status csa_state_checkpoint(const void* state, int64_t B, int64_t seq_bytes, const int32_t* pos,
+                                int32_t period, void* ckpt, int64_t n_slots, hipStream_t stream);
+
+/*
+ * csa_state_restore — state[b] = ckpt[b, slot[b]] for 0 <= slot[b] < n_slots
+ * (other sequences untouched). To resume at position P from checkpoint
+ * c = P / period - 1 (>= 0), restore slot c and append tokens
+ * period * (c + 1) .. P - 1 again: the rings then hold exactly what an
+ * uninterrupted run holds after appending position P - 1.
+ */
+csa_status csa_state_restore(const void* ckpt, int64_t B, int64_t seq_bytes, int64_t n_slots,
+                             const int32_t* slot, void* state, hipStream_t stream);
+
+/*
+ * csa_ring_fill — full SWA caching: a ring rebuilt from a full-length
+ * history of its rows. hist [B, T_hist, row_bytes] holds the row of every
+ * position (the window row, or a compressor ring slot's stream rows
+ * interleaved as in the ring); ring [B, R, row_bytes]. For each sequence,
+ * ring[b, t % R] = hist[b, t] for max(0, pos[b] - R) <= t < pos[b] and
+ * t < T_hist (other rows untouched): the ring as an uninterrupted run leaves
+ * it after appending position pos[b] - 1. Zero SWA caching needs no call:
+ * appending the last max(R) positions again rebuilds every ring.
+ */
+csa_status csa_ring_fill(const void* hist, int64_t B, int64_t T_hist, int64_t row_bytes,
+                         const int32_t* pos, int64_t R, void* ring, hipStream_t stream);
 
 /*
  * sparse_attn_bwd — gradients of sparse_attn_fwd (cf-1.com write-up §4.3:

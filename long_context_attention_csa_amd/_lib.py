@@ -51,6 +51,9 @@ SIGNATURES = {
     "sparse_attn_noalloc_scratch_bytes": (_SZ, []),
     "sparse_attn_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64,
                                                _I32, _I32, _I32, _I32, _F, _P, _P, _U32, _P]),
+    "csa_state_checkpoint": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _I64, _P]),
+    "csa_state_restore": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "csa_ring_fill": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
     "sparse_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
                                        _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -28,6 +28,12 @@ hipError_t launch_indexer_topk(const void*, const void*, const float*, const voi
                                void*, hipStream_t);
 hipError_t launch_indexer_scores(const void*, const void*, const float*, const void*, const void*, csa_dtype,
                                  const int32_t*, int64_t, int64_t, int64_t, int, int, int, float*, hipStream_t);
+hipError_t launch_state_checkpoint(const void* state, int64_t B, int64_t seq_bytes, const int32_t* pos, int period,
+                                   void* ckpt, int64_t n_slots, hipStream_t s);
+hipError_t launch_state_restore(const void* ckpt, int64_t B, int64_t seq_bytes, int64_t n_slots, const int32_t* slot,
+                                void* state, hipStream_t s);
+hipError_t launch_ring_fill(const void* hist, int64_t B, int64_t T_hist, int64_t row_bytes, const int32_t* pos,
+                            int64_t R, void* ring, hipStream_t s);
 size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max, bool batch_inv);
 size_t attn_bwd_ws_bytes(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window);
 hipError_t launch_attn_bwd(bool sparse, const void* q, const void* kv, const int32_t* idx, const void* x_win,
@@ -468,6 +474,48 @@ csa_status csa_window_append(const void* x_new, csa_dtype t, int64_t B, int32_t 
   CSA_REQUIRE(((uintptr_t)x_new & 15) == 0 && ((uintptr_t)ring & 15) == 0, CSA_ERR_SHAPE,
               "csa_window_append: x_new and ring must be 16-byte aligned");
   return hip_status(launch_window_append(x_new, t, B, pos, ring, R, stream), "csa_window_append");
+}
+
+csa_status csa_state_checkpoint(const void* state, int64_t B, int64_t seq_bytes, const int32_t* pos, int32_t period,
+                                void* ckpt, int64_t n_slots, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "csa_state_checkpoint";
+  CSA_REQUIRE(B >= 0 && B <= 65535 && seq_bytes > 0 && seq_bytes % 16 == 0 && period >= 1 && n_slots >= 1,
+              CSA_ERR_SHAPE, "%s: B=%lld seq_bytes=%lld period=%d n_slots=%lld", fn, (long long)B,
+              (long long)seq_bytes, period, (long long)n_slots);
+  if (B == 0) return CSA_OK;
+  CSA_REQUIRE(state && pos && ckpt, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  CSA_REQUIRE(((uintptr_t)state & 15) == 0 && ((uintptr_t)ckpt & 15) == 0, CSA_ERR_SHAPE,
+              "%s: state and ckpt must be 16-byte aligned", fn);
+  return hip_status(launch_state_checkpoint(state, B, seq_bytes, pos, period, ckpt, n_slots, stream), fn);
+}
+
+csa_status csa_state_restore(const void* ckpt, int64_t B, int64_t seq_bytes, int64_t n_slots, const int32_t* slot,
+                             void* state, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "csa_state_restore";
+  CSA_REQUIRE(B >= 0 && B <= 65535 && seq_bytes > 0 && seq_bytes % 16 == 0 && n_slots >= 1, CSA_ERR_SHAPE,
+              "%s: B=%lld seq_bytes=%lld n_slots=%lld", fn, (long long)B, (long long)seq_bytes, (long long)n_slots);
+  if (B == 0) return CSA_OK;
+  CSA_REQUIRE(ckpt && slot && state, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  CSA_REQUIRE(((uintptr_t)state & 15) == 0 && ((uintptr_t)ckpt & 15) == 0, CSA_ERR_SHAPE,
+              "%s: state and ckpt must be 16-byte aligned", fn);
+  return hip_status(launch_state_restore(ckpt, B, seq_bytes, n_slots, slot, state, stream), fn);
+}
+
+csa_status csa_ring_fill(const void* hist, int64_t B, int64_t T_hist, int64_t row_bytes, const int32_t* pos,
+                         int64_t R, void* ring, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "csa_ring_fill";
+  CSA_REQUIRE(B >= 0 && B <= 65535 && T_hist >= 0 && row_bytes > 0 && row_bytes % 16 == 0 && R >= 1 &&
+                  R <= ((int64_t)1 << 31) - 1,
+              CSA_ERR_SHAPE, "%s: B=%lld T_hist=%lld row_bytes=%lld R=%lld", fn, (long long)B, (long long)T_hist,
+              (long long)row_bytes, (long long)R);
+  if (B == 0 || T_hist == 0) return CSA_OK;
+  CSA_REQUIRE(hist && pos && ring, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  CSA_REQUIRE(((uintptr_t)hist & 15) == 0 && ((uintptr_t)ring & 15) == 0, CSA_ERR_SHAPE,
+              "%s: hist and ring must be 16-byte aligned", fn);
+  return hip_status(launch_ring_fill(hist, B, T_hist, row_bytes, pos, R, ring, stream), fn);
 }
 
 static csa_status check_attn_bwd(const char* fn, const void* q, const void* kv, const void* x_win,

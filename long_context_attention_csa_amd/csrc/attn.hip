@@ -901,6 +901,7 @@ __global__ __launch_bounds__(256) void k_window_append(const T* __restrict__ x_n
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= B * CPR) return;
   const int64_t b = i / CPR, c = i % CPR;
+  if (pos[b] < 0) return;   // a negative position skips the sequence
   const int64_t row = (int64_t)((uint32_t)pos[b] % (uint64_t)R);
   *reinterpret_cast<i32x4*>(ring + (b * R + row) * kD + c * C) =
       *reinterpret_cast<const i32x4*>(x_new + b * kD + c * C);

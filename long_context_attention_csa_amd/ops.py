@@ -329,3 +329,34 @@ def kernel_timer_read(capacity: int = 4096) -> list[float]:
     if n < 0:
         raise RuntimeError("csa_kernel_timer_read failed")
     return [buf[i] for i in range(min(n, capacity))]
+
+
+def state_checkpoint(state, pos, period: int, ckpt):
+    """Periodic checkpoint of one ring tensor state [B, ...]: sequences whose
+    appended position pos[b] ends a period copy state[b] into ckpt[b, slot]
+    (ckpt [B, n_slots, ...] of the same dtype)."""
+    _contig(state, pos, ckpt)
+    B = state.shape[0]
+    seq = state[0].numel() * state.element_size() if B else 0
+    n_slots = ckpt.shape[1]
+    check("csa_state_checkpoint", lib().csa_state_checkpoint(_ptr(state), B, seq, _ptr(pos), period, _ptr(ckpt),
+                                                             n_slots, _stream()))
+
+
+def state_restore(ckpt, slot, state):
+    """state[b] = ckpt[b, slot[b]] for slot[b] >= 0."""
+    _contig(ckpt, slot, state)
+    B = state.shape[0]
+    seq = state[0].numel() * state.element_size() if B else 0
+    check("csa_state_restore", lib().csa_state_restore(_ptr(ckpt), B, seq, ckpt.shape[1], _ptr(slot), _ptr(state),
+                                                       _stream()))
+
+
+def ring_fill(hist, pos, ring):
+    """ring[b, t % R] = hist[b, t] for the R positions before pos[b]
+    (hist [B, T_hist, ...] and ring [B, R, ...] with the same row shape)."""
+    _contig(hist, pos, ring)
+    B, T_hist = hist.shape[:2]
+    R = ring.shape[1]
+    row = hist[0, 0].numel() * hist.element_size() if B and T_hist else 16
+    check("csa_ring_fill", lib().csa_ring_fill(_ptr(hist), B, T_hist, row, _ptr(pos), R, _ptr(ring), _stream()))

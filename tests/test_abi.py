@@ -225,3 +225,20 @@ def test_headers_compile_as_c(tmp_path):
                         "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-c", str(src),
                         "-o", str(tmp_path / "abi.o")], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_state_cache_validation():
+    lib = _lib.lib()
+    Q = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    assert lib.csa_state_checkpoint(P, 2, 100, P, 1024, P, 4, None) == SHAPE      # bytes not a multiple of 16
+    assert lib.csa_state_checkpoint(P, 2, 128, P, 0, P, 4, None) == SHAPE        # period 0
+    assert lib.csa_state_checkpoint(P, 2, 128, P, 1024, P, 0, None) == SHAPE     # no slot
+    assert lib.csa_state_checkpoint(None, 2, 128, P, 1024, P, 4, None) == NULL
+    assert lib.csa_state_checkpoint(Q, 2, 128, P, 1024, P, 4, None) == SHAPE     # misaligned
+    assert lib.csa_state_checkpoint(None, 0, 128, None, 1024, None, 4, None) == OK
+    assert lib.csa_state_restore(P, 70000, 128, 4, P, P, None) == SHAPE         # B > 65535
+    assert lib.csa_state_restore(P, 2, 128, 4, None, P, None) == NULL
+    assert lib.csa_ring_fill(P, 2, 10, 24, P, 8, P, None) == SHAPE               # row bytes
+    assert lib.csa_ring_fill(P, 2, 10, 32, P, 0, P, None) == SHAPE               # R = 0
+    assert lib.csa_ring_fill(P, 2, 10, 32, None, 8, P, None) == NULL
+    assert lib.csa_ring_fill(None, 2, 0, 32, None, 8, None, None) == OK          # empty history
