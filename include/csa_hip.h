@@ -394,6 +394,54 @@ csa_status csa_ring_fill(const void* hist, int64_t B, int64_t T_hist, int64_t ro
                          const int32_t* pos, int64_t R, void* ring, hipStream_t stream);
 
 /*
+ * Projections around the attention core (cf-1.com write-up §3.4: the
+ * lightning indexer shares projection parameters with the main attention;
+ * the grouped output projection splits the many query heads (128 in V4-Pro)
+ * into groups, reduces each group's dimension, concatenates the groups and
+ * projects, cutting the output projection's parameters and FLOPs). The pages
+ * give no group count, rank or model width: all are arguments.
+ *
+ * csa_linear_bf16 — C[g] = A[g] * W[g]^T for g < G: A[g] [M, K] (row stride
+ * lda), W[g] [N, K] (a linear layer's [out, in] weight, row stride ldw),
+ * C[g] [M, N] (row stride ldc) of out_t (CSA_BF16, rounded to nearest even,
+ * or CSA_F32); group g's A, W and C start sA, sW, sC elements after group
+ * 0's. bf16 inputs, float32 accumulation. K a multiple of 64; A and W rows
+ * 16-byte aligned (bases 16-byte aligned, lda, ldw, sA, sW multiples of 8
+ * elements); C aligned to its element size; M, N < 2^31, G <= 65535.
+ */
+csa_status csa_linear_bf16(const void* A, int64_t lda, int64_t sA, const void* W, int64_t ldw, int64_t sW,
+                           void* C, csa_dtype out_t, int64_t ldc, int64_t sC, int64_t M, int64_t N,
+                           int64_t K, int64_t G, hipStream_t stream);
+
+/*
+ * csa_grouped_out_proj — grouped output projection. The H heads of o
+ * [T, H, d] (bf16) form G groups of H/G consecutive heads; group g's
+ * concatenated heads [T, (H/G)*d] are projected to rank r by w_group[g]
+ * [r, (H/G)*d], the G results concatenated to y [T, G*r] (bf16, in ws) and
+ * projected by w_out [D, G*r]:  out [T, D] (bf16) = y * w_out^T.
+ * (H/G)*d and G*r multiples of 64. ws: at least
+ * csa_grouped_out_proj_workspace_size() bytes, 16-byte aligned.
+ */
+size_t csa_grouped_out_proj_workspace_size(int64_t T, int32_t G, int32_t r);
+csa_status csa_grouped_out_proj(const void* o, const void* w_group, const void* w_out, int64_t T, int32_t H,
+                                int32_t d, int32_t G, int32_t r, int32_t D, void* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/*
+ * csa_query_proj_shared — query projections of the main attention and the
+ * lightning indexer from one shared low-rank latent (the indexer shares the
+ * main attention's projection): latent [T, r_q] (bf16, in ws) = x [T, D] *
+ * w_dq^T (w_dq [r_q, D]); q [T, n_q] = latent * w_uq^T (w_uq [n_q, r_q]);
+ * q_idx [T, n_i] = latent * w_iq^T (w_iq [n_i, r_q]); all bf16 (q_idx is
+ * quantised for the indexer by csa_quantize_rows). D and r_q multiples of
+ * 64. ws: csa_query_proj_shared_workspace_size() bytes.
+ */
+size_t csa_query_proj_shared_workspace_size(int64_t T, int32_t r_q);
+csa_status csa_query_proj_shared(const void* x, const void* w_dq, const void* w_uq, const void* w_iq,
+                                 int64_t T, int32_t D, int32_t r_q, int32_t n_q, int32_t n_i, void* q,
+                                 void* q_idx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * sparse_attn_bwd — gradients of sparse_attn_fwd (cf-1.com write-up §4.3:
  * training runs a deterministic attention backward; the formulas are the
  * derivatives of the forward's definition above). With P_i = e^{l_i - lse_h},

@@ -34,7 +34,8 @@ typedef enum {
   CSA_KID_SPARSE_ATTN = 6,
   CSA_KID_DENSE_ATTN = 7,
   CSA_KID_ATTN_MERGE = 8,
-  CSA_KID_ATTN_BWD = 9
+  CSA_KID_ATTN_BWD = 9,
+  CSA_KID_GEMM = 10
 } csa_kernel_id;
 
 csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches);

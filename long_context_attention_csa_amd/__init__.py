@@ -10,4 +10,5 @@ from .ops import (csa_append_state, csa_compress, csa_compress_append,  # noqa: 
                   kernel_timer_read, kernel_timer_start, sparse_attn_bwd,
                   sparse_attn_bwd_workspace_size, sparse_attn_fwd, sparse_attn_fwd_noalloc,
                   sparse_attn_noalloc_scratch_bytes, sparse_attn_workspace_size,
-                  window_append, state_checkpoint, state_restore, ring_fill)
+                  window_append, state_checkpoint, state_restore, ring_fill,
+                  linear_bf16, grouped_out_proj, query_proj_shared)

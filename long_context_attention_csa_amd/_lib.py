@@ -16,7 +16,7 @@ STATUS = {0: "CSA_OK", 1: "CSA_ERR_NULL", 2: "CSA_ERR_SHAPE", 3: "CSA_ERR_UNSUPP
           4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_HIP"}
 ATTN_WIN_RING, ATTN_BATCH_INVARIANT = 1, 2
 KID = {"compress": 1, "hca_compress": 2, "quantize": 3, "index_score": 4, "topk": 5,
-       "sparse_attn": 6, "dense_attn": 7, "attn_merge": 8, "attn_bwd": 9}
+       "sparse_attn": 6, "dense_attn": 7, "attn_merge": 8, "attn_bwd": 9, "gemm": 10}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -54,6 +54,12 @@ SIGNATURES = {
     "csa_state_checkpoint": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _I64, _P]),
     "csa_state_restore": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "csa_ring_fill": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
+    "csa_linear_bf16": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _I64, _P, ctypes.c_int, _I64, _I64, _I64, _I64,
+                                       _I64, _I64, _P]),
+    "csa_grouped_out_proj_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "csa_grouped_out_proj": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "csa_query_proj_shared_workspace_size": (_SZ, [_I64, _I32]),
+    "csa_query_proj_shared": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "sparse_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
                                        _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -34,6 +34,9 @@ hipError_t launch_state_restore(const void* ckpt, int64_t B, int64_t seq_bytes, 
                                 void* state, hipStream_t s);
 hipError_t launch_ring_fill(const void* hist, int64_t B, int64_t T_hist, int64_t row_bytes, const int32_t* pos,
                             int64_t R, void* ring, hipStream_t s);
+hipError_t launch_gemm_bf16(const void* A, int64_t lda, int64_t sA, const void* W, int64_t ldw, int64_t sW, void* C,
+                            int64_t ldc, int64_t sC, int64_t M, int64_t N, int64_t K, int64_t G, bool out_bf16,
+                            hipStream_t s);
 size_t attn_ws_bytes(int64_t B, int64_t Tq, int H, int64_t nk_max, bool batch_inv);
 size_t attn_bwd_ws_bytes(bool sparse, int64_t B, int64_t Tq, int64_t N, int64_t T_win, int H, int k, int window);
 hipError_t launch_attn_bwd(bool sparse, const void* q, const void* kv, const int32_t* idx, const void* x_win,
@@ -518,6 +521,84 @@ csa_status csa_ring_fill(const void* hist, int64_t B, int64_t T_hist, int64_t ro
   return hip_status(launch_ring_fill(hist, B, T_hist, row_bytes, pos, R, ring, stream), fn);
 }
 
+// ------------------------------------------------------------------ projections
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+csa_status csa_linear_bf16(const void* A, int64_t lda, int64_t sA, const void* W, int64_t ldw, int64_t sW, void* C,
+                           csa_dtype out_t, int64_t ldc, int64_t sC, int64_t M, int64_t N, int64_t K, int64_t G,
+                           hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "csa_linear_bf16";
+  CSA_REQUIRE(out_t == CSA_BF16 || out_t == CSA_F32, CSA_ERR_UNSUPPORTED, "%s: output must be CSA_BF16 or CSA_F32",
+              fn);
+  CSA_REQUIRE(M >= 0 && N >= 0 && K >= 0 && G >= 0 && M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && G <= 65535,
+              CSA_ERR_SHAPE, "%s: M=%lld N=%lld K=%lld G=%lld", fn, (long long)M, (long long)N, (long long)K,
+              (long long)G);
+  CSA_REQUIRE(K % 64 == 0, CSA_ERR_SHAPE, "%s: K=%lld must be a multiple of 64", fn, (long long)K);
+  if (M * N * G == 0) return CSA_OK;
+  CSA_REQUIRE(K > 0, CSA_ERR_SHAPE, "%s: K must be positive", fn);
+  CSA_REQUIRE(A && W && C, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  CSA_REQUIRE(lda >= K && ldw >= K && ldc >= N, CSA_ERR_SHAPE, "%s: lda=%lld ldw=%lld ldc=%lld", fn, (long long)lda,
+              (long long)ldw, (long long)ldc);
+  CSA_REQUIRE(lda % 8 == 0 && ldw % 8 == 0 && sA % 8 == 0 && sW % 8 == 0 && aligned16(A) && aligned16(W) &&
+                  ((uintptr_t)C & (out_t == CSA_BF16 ? 1 : 3)) == 0,
+              CSA_ERR_SHAPE, "%s: A and W need 16-byte aligned rows (base 16-byte aligned, strides multiples of 8 "
+              "elements); C must be aligned to its element size", fn);
+  return hip_status(launch_gemm_bf16(A, lda, sA, W, ldw, sW, C, ldc, sC, M, N, K, G, out_t == CSA_BF16, stream), fn);
+}
+
+size_t csa_grouped_out_proj_workspace_size(int64_t T, int32_t G, int32_t r) {
+  if (T <= 0 || G <= 0 || r <= 0) return 0;
+  return ((size_t)T * G * r * 2 + 255) / 256 * 256;
+}
+
+csa_status csa_grouped_out_proj(const void* o, const void* w_group, const void* w_out, int64_t T, int32_t H, int32_t d,
+                                int32_t G, int32_t r, int32_t D, void* out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "csa_grouped_out_proj";
+  CSA_REQUIRE(T >= 0 && H >= 1 && d >= 1 && G >= 1 && r >= 1 && D >= 1 && H % G == 0, CSA_ERR_SHAPE,
+              "%s: T=%lld H=%d d=%d G=%d r=%d D=%d (G must divide H)", fn, (long long)T, H, d, G, r, D);
+  const int64_t Kg = (int64_t)(H / G) * d;
+  CSA_REQUIRE(Kg % 64 == 0 && ((int64_t)G * r) % 64 == 0, CSA_ERR_SHAPE,
+              "%s: (H/G)*d and G*r must be multiples of 64", fn);
+  if (T == 0) return CSA_OK;
+  CSA_REQUIRE(o && w_group && w_out && out, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  const size_t need = csa_grouped_out_proj_workspace_size(T, G, r);
+  CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  // y[:, g*r : (g+1)*r] = o[:, g*Kg : (g+1)*Kg] * w_group[g]^T   (bf16 group results)
+  csa_status st = csa_linear_bf16(o, (int64_t)H * d, Kg, w_group, Kg, (int64_t)r * Kg, ws, CSA_BF16, (int64_t)G * r,
+                                  r, T, r, Kg, G, stream);
+  if (st != CSA_OK) return st;
+  // out = y * w_out^T
+  return csa_linear_bf16(ws, (int64_t)G * r, 0, w_out, (int64_t)G * r, 0, out, CSA_BF16, D, 0, T, D, (int64_t)G * r,
+                         1, stream);
+}
+
+size_t csa_query_proj_shared_workspace_size(int64_t T, int32_t r_q) {
+  if (T <= 0 || r_q <= 0) return 0;
+  return ((size_t)T * r_q * 2 + 255) / 256 * 256;
+}
+
+csa_status csa_query_proj_shared(const void* x, const void* w_dq, const void* w_uq, const void* w_iq, int64_t T,
+                                 int32_t D, int32_t r_q, int32_t n_q, int32_t n_i, void* q, void* q_idx, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "csa_query_proj_shared";
+  CSA_REQUIRE(T >= 0 && D >= 1 && r_q >= 1 && n_q >= 1 && n_i >= 1, CSA_ERR_SHAPE,
+              "%s: T=%lld D=%d r_q=%d n_q=%d n_i=%d", fn, (long long)T, D, r_q, n_q, n_i);
+  CSA_REQUIRE(D % 64 == 0 && r_q % 64 == 0, CSA_ERR_SHAPE, "%s: D and r_q must be multiples of 64", fn);
+  if (T == 0) return CSA_OK;
+  CSA_REQUIRE(x && w_dq && w_uq && w_iq && q && q_idx, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  const size_t need = csa_query_proj_shared_workspace_size(T, r_q);
+  CSA_REQUIRE(ws && ws_bytes >= need, CSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  csa_status st = csa_linear_bf16(x, D, 0, w_dq, D, 0, ws, CSA_BF16, r_q, 0, T, r_q, D, 1, stream);   // shared latent
+  if (st != CSA_OK) return st;
+  st = csa_linear_bf16(ws, r_q, 0, w_uq, r_q, 0, q, CSA_BF16, n_q, 0, T, n_q, r_q, 1, stream);       // attention queries
+  if (st != CSA_OK) return st;
+  return csa_linear_bf16(ws, r_q, 0, w_iq, r_q, 0, q_idx, CSA_BF16, n_i, 0, T, n_i, r_q, 1, stream); // indexer queries
+}
+
 static csa_status check_attn_bwd(const char* fn, const void* q, const void* kv, const void* x_win,
                                  const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t,
                                  int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d,
@@ -594,7 +675,7 @@ csa_status dense_compressed_attn_bwd(const void* q, const void* kv, const void* 
 
 csa_status csa_kernel_timer_start(int32_t kernel_id, int32_t max_launches) {
   g_last_error.clear();
-  CSA_REQUIRE(kernel_id >= CSA_KID_COMPRESS && kernel_id <= CSA_KID_ATTN_BWD, CSA_ERR_SHAPE,
+  CSA_REQUIRE(kernel_id >= CSA_KID_COMPRESS && kernel_id <= CSA_KID_GEMM, CSA_ERR_SHAPE,
               "csa_kernel_timer_start: kernel id %d", kernel_id);
   CSA_REQUIRE(max_launches >= 1 && max_launches <= kMaxTimed, CSA_ERR_SHAPE,
               "csa_kernel_timer_start: max_launches %d (1..%d)", max_launches, kMaxTimed);

@@ -360,3 +360,43 @@ def ring_fill(hist, pos, ring):
     R = ring.shape[1]
     row = hist[0, 0].numel() * hist.element_size() if B and T_hist else 16
     check("csa_ring_fill", lib().csa_ring_fill(_ptr(hist), B, T_hist, row, _ptr(pos), R, _ptr(ring), _stream()))
+
+
+def linear_bf16(a, w, out_dtype=torch.bfloat16, out=None):
+    """a [M, K] bf16 times w [N, K]^T (a linear layer's weight) -> [M, N]."""
+    _contig(a, w, out)
+    M, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    check("csa_linear_bf16", lib().csa_linear_bf16(_ptr(a), K, 0, _ptr(w), K, 0, _ptr(out), _float_dtype(out), N, 0,
+                                                   M, N, K, 1, _stream()))
+    return out
+
+
+def grouped_out_proj(o, w_group, w_out, out=None, ws=None):
+    """Grouped output projection: o [T, H, d] bf16, w_group [G, r, (H/G)*d], w_out [D, G*r] -> [T, D] bf16."""
+    _contig(o, w_group, w_out, out)
+    T, H, d = o.shape
+    G, r = w_group.shape[:2]
+    D = w_out.shape[0]
+    if out is None:
+        out = torch.empty(T, D, dtype=torch.bfloat16, device=o.device)
+    ws, nbytes = _workspace(int(lib().csa_grouped_out_proj_workspace_size(T, G, r)), o.device, ws)
+    check("csa_grouped_out_proj", lib().csa_grouped_out_proj(_ptr(o), _ptr(w_group), _ptr(w_out), T, H, d, G, r, D,
+                                                             _ptr(out), _ptr(ws), nbytes, _stream()))
+    return out
+
+
+def query_proj_shared(x, w_dq, w_uq, w_iq, ws=None):
+    """Shared-latent query projections: x [T, D] -> (q [T, n_q], q_idx [T, n_i]), all bf16."""
+    _contig(x, w_dq, w_uq, w_iq)
+    T, D = x.shape
+    r_q, n_q, n_i = w_dq.shape[0], w_uq.shape[0], w_iq.shape[0]
+    q = torch.empty(T, n_q, dtype=torch.bfloat16, device=x.device)
+    qi = torch.empty(T, n_i, dtype=torch.bfloat16, device=x.device)
+    ws, nbytes = _workspace(int(lib().csa_query_proj_shared_workspace_size(T, r_q)), x.device, ws)
+    check("csa_query_proj_shared", lib().csa_query_proj_shared(_ptr(x), _ptr(w_dq), _ptr(w_uq), _ptr(w_iq), T, D,
+                                                               r_q, n_q, n_i, _ptr(q), _ptr(qi), _ptr(ws), nbytes,
+                                                               _stream()))
+    return q, qi

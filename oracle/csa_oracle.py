@@ -563,3 +563,39 @@ def hca_layer(inp: dict, ratio: int = 128, window: int = 128):
     q_pos = np.arange(T)
     o, lse = dense_attn(inp["q"], kv, inp["c"], 0, inp["sink"], q_pos, ratio, window)
     return {"kv": kv, "o": o, "lse": lse}
+
+
+# ---------------------------------------------------------------------------
+# Projections around the attention core ([cf-1 §3.4]: the lightning indexer
+# shares projection parameters with the main attention; the grouped output
+# projection reduces each group of heads before the final projection). The
+# pages give no group count, rank or width: all are arguments here.
+# ---------------------------------------------------------------------------
+
+
+def grouped_output_projection(o, w_group, w_out):
+    """Grouped output projection.
+
+    The H heads of o [T, H, d] form G groups of H/G consecutive heads; group
+    g's heads, concatenated in head order, are reduced to rank r by w_group[g]
+    ([r, (H/G)*d], a linear layer's [out, in] weight); the G group results are
+    concatenated in group order and projected by w_out [D, G*r].
+    Returns float64 [T, D].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    w_group = np.asarray(w_group, dtype=np.float64)
+    w_out = np.asarray(w_out, dtype=np.float64)
+    T, H, d = o.shape
+    G, r, _ = w_group.shape
+    og = o.reshape(T, G, (H // G) * d)
+    y = np.einsum("tgk,grk->tgr", og, w_group)
+    return y.reshape(T, G * r) @ w_out.T
+
+
+def shared_query_projection(x, w_dq, w_uq, w_iq):
+    """Query projections sharing one low-rank latent: latent = x w_dq^T, then
+    the attention queries latent w_uq^T and the indexer queries latent w_iq^T.
+    Returns float64 (q, q_idx)."""
+    x = np.asarray(x, dtype=np.float64)
+    latent = x @ np.asarray(w_dq, dtype=np.float64).T
+    return latent @ np.asarray(w_uq, dtype=np.float64).T, latent @ np.asarray(w_iq, dtype=np.float64).T

@@ -675,3 +675,59 @@ def test_attn_bwd_zero_cotangent_and_no_keys():
     assert all(np.all(a == 0) for a in z)
     dq, dk, ds = O.attend_bwd(q, np.zeros((0, d)), sink, g.standard_normal((H, d)))
     assert dk.shape == (0, d) and np.all(dq == 0) and np.all(ds == 0)
+
+
+# ---------------------------------------------------------------- projections
+
+
+@pytest.mark.parametrize("T,H,d,G,r,D", [(5, 8, 4, 2, 3, 6), (3, 6, 2, 3, 4, 5), (4, 4, 3, 1, 2, 7), (2, 4, 2, 4, 1, 3)])
+def test_grouped_projection_is_block_diagonal(T, H, d, G, r, D):
+    """The grouped output projection equals one projection by the
+    block-diagonal matrix whose g-th block is w_group[g] (over head columns
+    g*(H/G)*d ...), built entry by entry, followed by w_out."""
+    g = np.random.default_rng(T * 100 + G)
+    o = g.standard_normal((T, H, d))
+    wg = g.standard_normal((G, r, (H // G) * d))
+    wo = g.standard_normal((D, G * r))
+    bd = np.zeros((G * r, H * d))
+    for gi in range(G):
+        for i in range(r):
+            for k in range((H // G) * d):
+                bd[gi * r + i, gi * (H // G) * d + k] = wg[gi, i, k]
+    want = np.zeros((T, D))
+    for t in range(T):
+        y = [sum(bd[j, c] * o[t].reshape(-1)[c] for c in range(H * d)) for j in range(G * r)]
+        want[t] = [sum(wo[n, j] * y[j] for j in range(G * r)) for n in range(D)]
+    np.testing.assert_allclose(O.grouped_output_projection(o, wg, wo), want, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_projection_identity_and_single_group():
+    """Identity group weights (r = (H/G) d) and an identity output give back the
+    heads concatenated in order; with one group the projection is the dense
+    chain o w_group[0]^T w_out^T."""
+    g = np.random.default_rng(7)
+    T, H, d, G = 3, 6, 4, 3
+    o = g.standard_normal((T, H, d))
+    k = (H // G) * d
+    eye = np.stack([np.eye(k)] * G)
+    np.testing.assert_allclose(O.grouped_output_projection(o, eye, np.eye(G * k)), o.reshape(T, H * d), rtol=0,
+                               atol=1e-15)
+    wg = g.standard_normal((1, 5, H * d))
+    wo = g.standard_normal((4, 5))
+    np.testing.assert_allclose(O.grouped_output_projection(o, wg, wo), (o.reshape(T, -1) @ wg[0].T) @ wo.T,
+                               rtol=1e-13)
+
+
+def test_shared_query_projection_associativity():
+    """Both query sets equal the input times the product of the up and down
+    projections (one matrix each), and the latent is shared: scaling w_dq
+    scales both outputs."""
+    g = np.random.default_rng(8)
+    x = g.standard_normal((4, 16))
+    wdq, wuq, wiq = g.standard_normal((6, 16)), g.standard_normal((10, 6)), g.standard_normal((3, 6))
+    q, qi = O.shared_query_projection(x, wdq, wuq, wiq)
+    np.testing.assert_allclose(q, x @ (wuq @ wdq).T, rtol=1e-12)
+    np.testing.assert_allclose(qi, x @ (wiq @ wdq).T, rtol=1e-12)
+    q2, qi2 = O.shared_query_projection(x, 2.5 * wdq, wuq, wiq)
+    np.testing.assert_allclose(q2, 2.5 * q, rtol=1e-13)
+    np.testing.assert_allclose(qi2, 2.5 * qi, rtol=1e-13)
