@@ -13,12 +13,14 @@ copies of the caches are rotated so the 256 MB Infinity Cache cannot serve a
 step from the previous one. ``value`` = queries/s = B / step time.
 
 Also reported: the step's algorithmic HBM bytes / step time, the dominant
-kernel's roofline fraction (timed with HIP events on its own stream by the
-library's kernel timer), the CPU oracle timed on a bounded sample, and extra
-workloads (CSA decode at 262k context; prefill TFLOP/s) under "extras".
+kernel's roofline fraction (the indexer's score stage: back-to-back launches
+in one HIP graph timed with HIP events on the stream they run on), the
+selection recall of the fp4 keys against float32, the CPU oracle timed on a
+bounded sample, and extra workloads (CSA decode at 262k context, cache
+appends, prefill and backward TFLOP/s, projections) under "extras".
 
 Usage: python bench.py [--steps K] [--warmup W]
-                       [--extras decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca|none]
+                       [--extras decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca,proj|none]
 """
 from __future__ import annotations
 
@@ -625,6 +627,43 @@ def bwd_hca(torch, C, syn, iters):
             "workspace_gb": round(ws.numel() / 1e9, 2)}
 
 
+def proj(torch, C, syn, iters):
+    """Projections around the attention core for one 8,192-token prefill
+    chunk, bf16 MFMA GEMMs: the grouped output projection (128 heads x 128 in
+    8 groups, rank 1024 per group, model width 7168) and the shared-latent
+    query projections (7168 -> 1536 latent -> 128 x 128 attention queries and
+    64 x 128 indexer queries). The sizes are a reading: the pages give the
+    structure, not these widths."""
+    dev, bf = "cuda", torch.bfloat16
+    T, H, d, G, r, D, r_q, H_I = 8192, 128, 128, 8, 1024, 7168, 1536, 64
+    s = 8000
+    o = syn.normal_device(s, (T, H, d), dev, bf)
+    wg = syn.normal_device(s + 1, (G, r, H // G * d), dev, bf, scale=1 / np.sqrt(H // G * d))
+    wo = syn.normal_device(s + 2, (D, G * r), dev, bf, scale=1 / np.sqrt(G * r))
+    x = syn.normal_device(s + 3, (T, D), dev, bf)
+    wdq = syn.normal_device(s + 4, (r_q, D), dev, bf, scale=1 / np.sqrt(D))
+    wuq = syn.normal_device(s + 5, (H * d, r_q), dev, bf, scale=1 / np.sqrt(r_q))
+    wiq = syn.normal_device(s + 6, (H_I * d, r_q), dev, bf, scale=1 / np.sqrt(r_q))
+    out = torch.empty(T, D, dtype=bf, device=dev)
+    ws_o = torch.empty(C.grouped_out_proj_workspace_size(T, G, r), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(C.query_proj_shared_workspace_size(T, r_q), dtype=torch.uint8, device=dev)
+    ops = [("grouped_out_proj", lambda: C.grouped_out_proj(o, wg, wo, out=out, ws=ws_o)),
+           ("query_proj_shared", lambda: C.query_proj_shared(x, wdq, wuq, wiq, ws=ws_q))]
+    t = time_ops(torch, ops, iters)
+    fl_o = 2.0 * T * H * d * r + 2.0 * T * G * r * D
+    fl_q = 2.0 * T * D * r_q + 2.0 * T * r_q * (H + H_I) * d
+    res = {"workload": "projections_bf16_T8192", "tokens": T, "ms": {k: round(v, 4) for k, v in t.items()},
+           "grouped_out_proj": {"heads": H, "groups": G, "rank": r, "width": D, "tflop": round(fl_o / 1e12, 4),
+                                "tflop_s": round(fl_o / (t["grouped_out_proj"] * 1e-3) / 1e12, 1),
+                                "frac_bf16_peak": round(fl_o / (t["grouped_out_proj"] * 1e-3) / 1e12
+                                                        / BF16_PEAK_TFLOPS, 4)},
+           "query_proj_shared": {"latent": r_q, "tflop": round(fl_q / 1e12, 4),
+                                 "tflop_s": round(fl_q / (t["query_proj_shared"] * 1e-3) / 1e12, 1),
+                                 "frac_bf16_peak": round(fl_q / (t["query_proj_shared"] * 1e-3) / 1e12
+                                                         / BF16_PEAK_TFLOPS, 4)}}
+    return res
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -633,7 +672,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
-    ap.add_argument("--extras", default="decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca",
+    ap.add_argument("--extras", default="decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca,"
+                                        "proj",
                     help="comma list of decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk or 'none'")
     ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -662,7 +702,10 @@ def main():
     B = st["B"]
     qps = B / (ms * 1e-3)
     dom_us = st["score_us"]
-    achieved = st["bytes_index_score"] / (dom_us * 1e-6) / 1e9
+    # a score-stage launch reads the keys, queries and weights and writes one
+    # float32 score per (sequence, entry)
+    dom_bytes = st["bytes_index_score"] + B * st["N"] * 4
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     step_gbs = st["bytes"] / (ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -692,7 +735,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic("k_index_score",
                                                  "long_context_attention_csa_amd/csrc/indexer.hip"),
-                     "bytes_per_launch": st["bytes_index_score"], "us_per_launch": round(dom_us, 2),
+                     "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 2),
                      "timing": "48 back-to-back score-stage launches over the rotated cache copies in one HIP "
                                "graph, HIP events on its stream"},
         "step_roofline": {"bound": "hbm", "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -724,14 +767,15 @@ def main():
         extras["csa_decode_262k_ctx"] = {
             "batch": st4["B"], "queries_per_s": round(st4["B"] / (ms4 * 1e-3), 1), "ms_per_step": round(ms4, 5),
             "hbm_tb_s": round(st4["bytes"] / (ms4 * 1e-3) / 1e12, 3),
-            "index_score_gb_s": round(st4["bytes_index_score"] / (st4["score_us"] * 1e-6) / 1e9, 1),
+            "index_score_gb_s": round((st4["bytes_index_score"] + st4["B"] * st4["N"] * 4) / (st4["score_us"] * 1e-6)
+                                      / 1e9, 1),
             "index_score_us": round(st4["score_us"], 2),
             "index_recall_vs_float32": {"format": st4["fmt"], "rows": st4["recall"]},
             "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in kt4.items()}}
         del st4
         torch.cuda.empty_cache()
     for key, fn in (("decode_append", decode_append), ("prefill_csa", prefill_csa), ("prefill_hca", prefill_hca),
-                    ("prefill_chunk", prefill_chunk), ("bwd_csa", bwd_csa), ("bwd_hca", bwd_hca)):
+                    ("prefill_chunk", prefill_chunk), ("bwd_csa", bwd_csa), ("bwd_hca", bwd_hca), ("proj", proj)):
         if key in wanted:
             r = fn(torch, C, syn, args.prefill_iters)
             log(f"[bench] {r['workload']}: {r}")

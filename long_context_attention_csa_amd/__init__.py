@@ -11,4 +11,5 @@ from .ops import (csa_append_state, csa_compress, csa_compress_append,  # noqa: 
                   sparse_attn_bwd_workspace_size, sparse_attn_fwd, sparse_attn_fwd_noalloc,
                   sparse_attn_noalloc_scratch_bytes, sparse_attn_workspace_size,
                   window_append, state_checkpoint, state_restore, ring_fill,
-                  linear_bf16, grouped_out_proj, query_proj_shared)
+                  linear_bf16, grouped_out_proj, query_proj_shared,
+                  grouped_out_proj_workspace_size, query_proj_shared_workspace_size)

@@ -374,6 +374,14 @@ def linear_bf16(a, w, out_dtype=torch.bfloat16, out=None):
     return out
 
 
+def grouped_out_proj_workspace_size(T, G, r) -> int:
+    return int(lib().csa_grouped_out_proj_workspace_size(T, G, r))
+
+
+def query_proj_shared_workspace_size(T, r_q) -> int:
+    return int(lib().csa_query_proj_shared_workspace_size(T, r_q))
+
+
 def grouped_out_proj(o, w_group, w_out, out=None, ws=None):
     """Grouped output projection: o [T, H, d] bf16, w_group [G, r, (H/G)*d], w_out [D, G*r] -> [T, D] bf16."""
     _contig(o, w_group, w_out, out)
@@ -382,7 +390,7 @@ def grouped_out_proj(o, w_group, w_out, out=None, ws=None):
     D = w_out.shape[0]
     if out is None:
         out = torch.empty(T, D, dtype=torch.bfloat16, device=o.device)
-    ws, nbytes = _workspace(int(lib().csa_grouped_out_proj_workspace_size(T, G, r)), o.device, ws)
+    ws, nbytes = _workspace(grouped_out_proj_workspace_size(T, G, r), o.device, ws)
     check("csa_grouped_out_proj", lib().csa_grouped_out_proj(_ptr(o), _ptr(w_group), _ptr(w_out), T, H, d, G, r, D,
                                                              _ptr(out), _ptr(ws), nbytes, _stream()))
     return out
@@ -395,7 +403,7 @@ def query_proj_shared(x, w_dq, w_uq, w_iq, ws=None):
     r_q, n_q, n_i = w_dq.shape[0], w_uq.shape[0], w_iq.shape[0]
     q = torch.empty(T, n_q, dtype=torch.bfloat16, device=x.device)
     qi = torch.empty(T, n_i, dtype=torch.bfloat16, device=x.device)
-    ws, nbytes = _workspace(int(lib().csa_query_proj_shared_workspace_size(T, r_q)), x.device, ws)
+    ws, nbytes = _workspace(query_proj_shared_workspace_size(T, r_q), x.device, ws)
     check("csa_query_proj_shared", lib().csa_query_proj_shared(_ptr(x), _ptr(w_dq), _ptr(w_uq), _ptr(w_iq), T, D,
                                                                r_q, n_q, n_i, _ptr(q), _ptr(qi), _ptr(ws), nbytes,
                                                                _stream()))

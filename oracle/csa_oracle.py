@@ -574,7 +574,8 @@ def hca_layer(inp: dict, ratio: int = 128, window: int = 128):
 
 
 def grouped_output_projection(o, w_group, w_out):
-    """Grouped output projection.
+    """Grouped output projection (cf-1.com write-up §3.4: heads are grouped
+    and each group's output reduced before the output projection).
 
     The H heads of o [T, H, d] form G groups of H/G consecutive heads; group
     g's heads, concatenated in head order, are reduced to rank r by w_group[g]
@@ -593,9 +594,10 @@ def grouped_output_projection(o, w_group, w_out):
 
 
 def shared_query_projection(x, w_dq, w_uq, w_iq):
-    """Query projections sharing one low-rank latent: latent = x w_dq^T, then
-    the attention queries latent w_uq^T and the indexer queries latent w_iq^T.
-    Returns float64 (q, q_idx)."""
+    """Query projections sharing one low-rank latent (cf-1.com write-up §3.4:
+    the indexer's query projection is shared with the main attention's):
+    latent = x w_dq^T, then the attention queries latent w_uq^T and the
+    indexer queries latent w_iq^T. Returns float64 (q, q_idx)."""
     x = np.asarray(x, dtype=np.float64)
     latent = x @ np.asarray(w_dq, dtype=np.float64).T
     return latent @ np.asarray(w_uq, dtype=np.float64).T, latent @ np.asarray(w_iq, dtype=np.float64).T
