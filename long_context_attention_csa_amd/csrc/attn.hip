@@ -292,10 +292,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn(
 // at sixteen different positions, so the K fragment reads (16 rows, one chunk
 // each) and the transposed V reads (4 rows x 32 bytes per 16 lanes) spread
 // over all LDS banks. A lane of a gather instruction fetches exactly the
-// chunk its LDS slot must hold; blocks of fewer than 4 waves use SWM = 7
-// (rows 8 apart share positions, a 2-way conflict on the K reads), which
-// keeps a lane's source chunk the same for all its gathers of a tile and so
-// saves the registers those kernels are short of.
+// chunk its LDS slot must hold.
 constexpr int kSelChunk = 1024;     // selected indices staged in LDS at a time
 
 // One 64-key tile (row-major in LDS, swizzled chunks) for the HPW 16-head
@@ -356,7 +353,12 @@ __device__ __forceinline__ void attn_tile16(uint32_t tb, const TileLanes& tl, bo
   // P, O and l grow by at most 2^kLazy (exact in float32, and bf16 keeps
   // its relative precision); only a larger logit raises m (the column max
   // over the 4 lane rows, by permlane swaps) and rescales O and l. The
-  // result O / l and the log-sum m + log2(l) do not depend on m.
+  // result O / l and the log-sum m + log2(l) do not depend on m. One branch
+  // (rarely taken) covers every head block, so the exponentials of all head
+  // blocks and the P V products that follow form one straight-line block the
+  // compiler can interleave.
+  float lm2[HPW];
+  bool need = false;
 #pragma unroll
   for (int hb = 0; hb < HPW; ++hb) {
     float lmax = s[hb][0][0];
@@ -364,19 +366,28 @@ __device__ __forceinline__ void attn_tile16(uint32_t tb, const TileLanes& tl, bo
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) lmax = fmaxf(lmax, s[hb][kb][rr]);
-    const float lm2 = lmax * scale2;
-    if (__ballot(lm2 > m[hb] + kLazy)) {   // wave-uniform
-      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm2), __float_as_uint(lm2), false, false);
-      const float c1 = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
-      const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(c1), __float_as_uint(c1), false, false);
-      const float cmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
-      const float mnew = fmaxf(m[hb], cmax);
-      const float alpha = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mnew);
-      lsum[hb] *= alpha;
+    lm2[hb] = lmax * scale2;
+    need |= lm2[hb] > m[hb] + kLazy;
+  }
+  if (__ballot(need)) {   // wave-uniform, rare: one branch for all head blocks
 #pragma unroll
-      for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
-      m[hb] = mnew;
+    for (int hb = 0; hb < HPW; ++hb) {
+      if (__ballot(lm2[hb] > m[hb] + kLazy)) {
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(lm2[hb]), __float_as_uint(lm2[hb]), false, false);
+        const float c1 = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+        const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(c1), __float_as_uint(c1), false, false);
+        const float cmax = fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+        const float mnew = fmaxf(m[hb], cmax);
+        const float alpha = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mnew);
+        lsum[hb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < kD / 16; ++db) O[hb][db] *= alpha;
+        m[hb] = mnew;
+      }
     }
+  }
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) {
     const float negm = m[hb] == -INFINITY ? 0.f : -m[hb];
     float ps[2] = {0.f, 0.f};
 #pragma unroll
@@ -446,7 +457,7 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0 .. NWT-1: gathers
   const int hw = wv % NW, ts = wv / NW;                      // head wave, tile stream
   const int g = lane >> 4, col = lane & 15;
-  constexpr int SWM = NWT >= 4 ? 15 : 7;          // chunk swizzle mask of the tiles
+  constexpr int SWM = 15;                         // chunk swizzle mask of the tiles
   const TileLanes tl(lane, SWM);
   // rows < 2^31: 32-bit row arithmetic, so that both scalar loads below are
   // issued together (a 64-bit division would put a branch between them)
@@ -551,14 +562,15 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
       if (c0 == kbeg) load_q();
     }
     const int ntiles = (clen + kKT - 1) / kKT;
-    // Gather instruction j of this lane: tile row grow[j] (4 rows per wave
-    // instruction), 16-byte chunk gcol[j] of it (swizzled position lane & 15).
-    int grow[LPT], gcol[LPT];
-#pragma unroll
-    for (int j = 0; j < LPT; ++j) {
-      grow[j] = (j * NWT + wv) * 4 + (lane >> 4);
-      gcol[j] = ((lane & 15) ^ (grow[j] & SWM)) << 3;
-    }
+    // Gather instruction j of this lane: tile row grow(j) (4 rows per wave
+    // instruction), 16-byte chunk gcol(j) of it (swizzled position lane & 15):
+    // grow(j) mod 16 = 4 ((j NWT + wv) mod 4) + lane / 16, and (j NWT + wv)
+    // mod 4 = (j NWT mod 4) ^ (wv mod 4) for the wave counts used, so the
+    // chunk is one per-lane value xor a constant of j (no per-j registers).
+    static_assert(NWT == 1 || NWT == 2 || NWT % 4 == 0, "gather row pattern");
+    const int gc0 = ((lane & 15) ^ (((wv & 3) << 2) | (lane >> 4))) << 3;
+    auto grow = [&](int j) { return (j * NWT + wv) * 4 + (lane >> 4); };
+    auto gcol = [&](int j) { return gc0 ^ (((j * NWT) & 3) << 5); };
     // key kk of the section: its row, or null when the slot holds no key
     auto key_src = [&](int kk) -> const uint16_t* {
       if (kk >= clen) return nullptr;
@@ -585,24 +597,24 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
         const uint16_t* tb = t0k >= n_sel ? xwb + wt * kD : kvb + t0k * kD;
 #pragma unroll
         for (int j = 0; j < LPT; ++j)
-          gather_lds16(tb + grow[j] * kD + gcol[j], (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
+          gather_lds16(tb + grow(j) * kD + gcol(j), (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
       } else if (SPARSE && offs32 && kk0 + kKT <= clen && t0k + kKT <= n_sel) {
         // 64 selected entries: byte offsets from the batch's first entry (an
         // entry outside [0, N) reads entry 0 and is marked)
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
-          const int32_t e = sidx[kk0 + grow[j]];
+          const int32_t e = sidx[kk0 + grow(j)];
           const bool ok = (uint32_t)e < (uint32_t)N;
           bad |= !ok;
-          gather_lds16_s(kvb, (ok ? (uint32_t)e * (uint32_t)(kD * 2) : 0u) + (uint32_t)gcol[j] * 2u,
+          gather_lds16_s(kvb, (ok ? (uint32_t)e * (uint32_t)(kD * 2) : 0u) + (uint32_t)gcol(j) * 2u,
                          (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
         }
       } else {
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
-          const uint16_t* src = key_src(kk0 + grow[j]);
+          const uint16_t* src = key_src(kk0 + grow(j));
           bad |= src == nullptr;
-          gather_lds16((src ? src : dummy) + gcol[j], (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
+          gather_lds16((src ? src : dummy) + gcol(j), (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
         }
       }
       const bool wbad = __ballot(bad) != 0ull;
