@@ -600,10 +600,15 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
           gather_lds16(tb + grow(j) * kD + gcol(j), (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
       } else if (SPARSE && offs32 && kk0 + kKT <= clen && t0k + kKT <= n_sel) {
         // 64 selected entries: byte offsets from the batch's first entry (an
-        // entry outside [0, N) reads entry 0 and is marked)
+        // entry outside [0, N) reads entry 0 and is marked). All index reads
+        // go first: a gather statement orders memory accesses around it, so
+        // a read placed between gathers would be waited for one at a time.
+        int32_t ent[LPT];
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) ent[j] = sidx[kk0 + grow(j)];
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
-          const int32_t e = sidx[kk0 + grow(j)];
+          const int32_t e = ent[j];
           const bool ok = (uint32_t)e < (uint32_t)N;
           bad |= !ok;
           gather_lds16_s(kvb, (ok ? (uint32_t)e * (uint32_t)(kD * 2) : 0u) + (uint32_t)gcol(j) * 2u,
