@@ -1,10 +1,11 @@
 """Projections around the attention core on the GPU (bf16 MFMA GEMM) against
 the oracle: the general grouped GEMM (ragged M and N, several groups with
-strides, bf16 and float32 outputs), the grouped output projection and the
-shared-latent query projections. Tolerance: inputs are bf16 values (exact in
-both), products accumulate in float32, and each bf16 output (and the bf16
-intermediate of the two-stage projections) is rounded once (2^-9 relative):
-max-abs 2e-2 of the largest output magnitude and relative L2 1e-2."""
+strides, bf16 and float32 outputs, shapes for both tile sizes), the grouped
+output projection and the shared-latent query projections. Tolerance: inputs
+are bf16 values (exact in both), products accumulate in float32, and each
+bf16 output (and the bf16 intermediate of the two-stage projections) is
+rounded once (2^-9 relative): max-abs 2e-2 of the largest output magnitude
+and relative L2 1e-2."""
 import numpy as np
 import pytest
 import torch
@@ -31,7 +32,7 @@ def _w(seed, shape, fan_in):
     return syn.normal(seed, shape, scale=1.0 / np.sqrt(fan_in), bf16=True)
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (300, 517, 192), (1, 64, 128), (1000, 100, 1024)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (300, 517, 192), (1, 64, 128), (1000, 100, 1024), (4100, 4000, 128)])
 @pytest.mark.parametrize("out_dtype", [BF, torch.float32])
 def test_linear(M, N, K, out_dtype):
     a = syn.normal(1100, (M, K), bf16=True)
@@ -61,7 +62,7 @@ def test_linear_groups_with_strides():
 
 
 @pytest.mark.parametrize("T,H,G,r,D", [(300, 128, 8, 512, 1024), (77, 64, 4, 64, 256), (5, 16, 1, 128, 64),
-                                       (33, 32, 32, 2, 100)])
+                                       (33, 32, 32, 2, 100), (2100, 128, 8, 1024, 1000)])
 def test_grouped_out_proj(T, H, G, r, D):
     d = 128
     o = syn.normal(1104, (T, H, d), bf16=True)
