@@ -17,8 +17,9 @@
 // Kernel: a block computes a 128 x 128 tile of C with 4 waves (2 x 2, 64 x 64
 // each, 4 x 4 tiles of v_mfma_f32_16x16x32_bf16), stepping K by 64 through a
 // 2-slot LDS ring filled by global_load_lds_dwordx4 (each lane's 16 bytes
-// straight to LDS). A tile row is 128 bytes, 8 chunks of 16. The MFMA's A operand is W (rows n) and its B operand is A (rows m):
-// the accumulator then holds C^T, and a lane's 4 values are 4 consecutive
+// straight to LDS). A tile row is 128 bytes, 8 chunks of 16. The MFMA's A
+// operand is W (rows n) and its B operand is A (rows m): the accumulator
+// then holds C^T, and a lane's 4 values are 4 consecutive
 // columns of one row of C (one 8- or 16-byte store when C's rows are 16-byte
 // aligned, else 4 element stores). Rows past M or N read the last valid row
 // and are not stored; K is a multiple of 64. Problems with at least 256
