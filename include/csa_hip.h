@@ -407,7 +407,8 @@ csa_status csa_ring_fill(const void* hist, int64_t B, int64_t T_hist, int64_t ro
  * or CSA_F32); group g's A, W and C start sA, sW, sC elements after group
  * 0's. bf16 inputs, float32 accumulation. K a multiple of 64; A and W rows
  * 16-byte aligned (bases 16-byte aligned, lda, ldw, sA, sW multiples of 8
- * elements); C aligned to its element size; M, N < 2^31, G <= 65535.
+ * elements); C aligned to its element size; M, N < 2^31 with fewer than
+ * 2^24 tiles of 128 x 128 in C, G <= 65535.
  */
 csa_status csa_linear_bf16(const void* A, int64_t lda, int64_t sA, const void* W, int64_t ldw, int64_t sW,
                            void* C, csa_dtype out_t, int64_t ldc, int64_t sC, int64_t M, int64_t N,

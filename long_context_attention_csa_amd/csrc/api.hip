@@ -536,6 +536,10 @@ csa_status csa_linear_bf16(const void* A, int64_t lda, int64_t sA, const void* W
               (long long)G);
   CSA_REQUIRE(K % 64 == 0, CSA_ERR_SHAPE, "%s: K=%lld must be a multiple of 64", fn, (long long)K);
   if (M * N * G == 0) return CSA_OK;
+  // one block per 128 x 128 tile of C: the launch's work-item count must fit 32 bits
+  CSA_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 24), CSA_ERR_SHAPE,
+              "%s: M=%lld x N=%lld has too many 128 x 128 tiles for one launch (at most 2^24 - 1)", fn,
+              (long long)M, (long long)N);
   CSA_REQUIRE(K > 0, CSA_ERR_SHAPE, "%s: K must be positive", fn);
   CSA_REQUIRE(A && W && C, CSA_ERR_NULL, "%s: NULL tensor", fn);
   CSA_REQUIRE(lda >= K && ldw >= K && ldc >= N, CSA_ERR_SHAPE, "%s: lda=%lld ldw=%lld ldc=%lld", fn, (long long)lda,

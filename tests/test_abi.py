@@ -242,3 +242,37 @@ def test_state_cache_validation():
     assert lib.csa_ring_fill(P, 2, 10, 32, P, 0, P, None) == SHAPE               # R = 0
     assert lib.csa_ring_fill(P, 2, 10, 32, None, 8, P, None) == NULL
     assert lib.csa_ring_fill(None, 2, 0, 32, None, 8, None, None) == OK          # empty history
+
+
+def test_projection_validation():
+    lib = _lib.lib()
+    BF16, F32, FP8 = 1, 0, 2
+    Q = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    lin = lib.csa_linear_bf16
+    # A, lda, sA, W, ldw, sW, C, out_t, ldc, sC, M, N, K, G, stream
+    assert lin(P, 64, 0, P, 64, 0, P, FP8, 64, 0, 10, 10, 64, 1, None) == UNSUP     # output type
+    assert lin(P, 96, 0, P, 96, 0, P, BF16, 64, 0, 10, 10, 96, 1, None) == SHAPE    # K not a multiple of 64
+    assert lin(P, 64, 0, P, 64, 0, P, BF16, 64, 0, 10, 10, 64, 70000, None) == SHAPE  # G > 65535
+    assert lin(P, 60, 0, P, 64, 0, P, BF16, 64, 0, 10, 10, 64, 1, None) == SHAPE    # lda < K
+    assert lin(P, 68, 0, P, 68, 0, P, BF16, 64, 0, 10, 10, 64, 1, None) == SHAPE    # lda = 68: rows not 16-byte aligned
+    assert lin(Q, 64, 0, P, 64, 0, P, BF16, 64, 0, 10, 10, 64, 1, None) == SHAPE    # A base misaligned
+    assert lin(None, 64, 0, P, 64, 0, P, BF16, 64, 0, 10, 10, 64, 1, None) == NULL
+    assert lin(P, 64, 0, P, 64, 0, P, BF16, 1 << 30, 0, 1 << 30, 1 << 30, 64, 1, None) == SHAPE  # tile count
+    assert lin(None, 64, 0, None, 64, 0, None, BF16, 64, 0, 0, 10, 64, 1, None) == OK  # empty
+    gop = lib.csa_grouped_out_proj
+    # o, w_group, w_out, T, H, d, G, r, D, out, ws, ws_bytes, stream
+    need = lib.csa_grouped_out_proj_workspace_size(8, 4, 64)
+    assert need >= 8 * 4 * 64 * 2
+    assert gop(P, P, P, 8, 64, 128, 5, 64, 256, P, P, need, None) == SHAPE          # H not a multiple of G
+    assert gop(P, P, P, 8, 64, 12, 8, 64, 256, P, P, need, None) == SHAPE           # (H/G) d = 96: not a multiple of 64
+    assert gop(P, P, P, 8, 64, 128, 4, 8, 256, P, P, need, None) == SHAPE           # G r not a multiple of 64
+    assert gop(None, P, P, 8, 64, 128, 4, 64, 256, P, P, need, None) == NULL
+    assert gop(P, P, P, 8, 64, 128, 4, 64, 256, P, P, need - 1, None) == WS
+    qps = lib.csa_query_proj_shared
+    # x, w_dq, w_uq, w_iq, T, D, r_q, n_q, n_i, q, q_idx, ws, ws_bytes, stream
+    need = lib.csa_query_proj_shared_workspace_size(8, 128)
+    assert need >= 8 * 128 * 2
+    assert qps(P, P, P, P, 8, 100, 128, 256, 256, P, P, P, need, None) == SHAPE     # D not a multiple of 64
+    assert qps(P, P, P, P, 8, 128, 96, 256, 256, P, P, P, need, None) == SHAPE      # r_q not a multiple of 64
+    assert qps(P, P, P, P, 8, 128, 128, 256, 256, P, None, P, need, None) == NULL
+    assert qps(P, P, P, P, 8, 128, 128, 256, 256, P, P, P, need - 1, None) == WS
