@@ -630,9 +630,10 @@ def bwd_hca(torch, C, syn, iters):
 def proj(torch, C, syn, iters):
     """Projections around the attention core for one 8,192-token prefill
     chunk, bf16 MFMA GEMMs: the grouped output projection (128 heads x 128 in
-    8 groups, rank 1024 per group, model width 7168) and the shared-latent
+    8 groups, rank 1024 per group, model width 7168), the shared-latent
     query projections (7168 -> 1536 latent -> 128 x 128 attention queries and
-    64 x 128 indexer queries). The sizes are a reading: the pages give the
+    64 x 128 indexer queries) and the compressor's input streams (KV and gate
+    streams of the KV and index-key compressors, 8 x 128, from 7168). The sizes are a reading: the pages give the
     structure, not these widths."""
     dev, bf = "cuda", torch.bfloat16
     T, H, d, G, r, D, r_q, H_I = 8192, 128, 128, 8, 1024, 7168, 1536, 64
@@ -647,11 +648,16 @@ def proj(torch, C, syn, iters):
     out = torch.empty(T, D, dtype=bf, device=dev)
     ws_o = torch.empty(C.grouped_out_proj_workspace_size(T, G, r), dtype=torch.uint8, device=dev)
     ws_q = torch.empty(C.query_proj_shared_workspace_size(T, r_q), dtype=torch.uint8, device=dev)
+    # the compressor's KV and gate streams and the indexer's key streams: 8 x 128
+    wkv = syn.normal_device(s + 7, (8, d, D), dev, bf, scale=1 / np.sqrt(D))
+    streams = torch.empty(8, T, d, dtype=bf, device=dev)
     ops = [("grouped_out_proj", lambda: C.grouped_out_proj(o, wg, wo, out=out, ws=ws_o)),
-           ("query_proj_shared", lambda: C.query_proj_shared(x, wdq, wuq, wiq, ws=ws_q))]
+           ("query_proj_shared", lambda: C.query_proj_shared(x, wdq, wuq, wiq, ws=ws_q)),
+           ("kv_proj", lambda: C.kv_proj(x, wkv, out=streams))]
     t = time_ops(torch, ops, iters)
     fl_o = 2.0 * T * H * d * r + 2.0 * T * G * r * D
     fl_q = 2.0 * T * D * r_q + 2.0 * T * r_q * (H + H_I) * d
+    fl_kv = 2.0 * T * D * 8 * d
     res = {"workload": "projections_bf16_T8192", "tokens": T, "ms": {k: round(v, 4) for k, v in t.items()},
            "grouped_out_proj": {"heads": H, "groups": G, "rank": r, "width": D, "tflop": round(fl_o / 1e12, 4),
                                 "tflop_s": round(fl_o / (t["grouped_out_proj"] * 1e-3) / 1e12, 1),
@@ -660,7 +666,10 @@ def proj(torch, C, syn, iters):
            "query_proj_shared": {"latent": r_q, "tflop": round(fl_q / 1e12, 4),
                                  "tflop_s": round(fl_q / (t["query_proj_shared"] * 1e-3) / 1e12, 1),
                                  "frac_bf16_peak": round(fl_q / (t["query_proj_shared"] * 1e-3) / 1e12
-                                                         / BF16_PEAK_TFLOPS, 4)}}
+                                                         / BF16_PEAK_TFLOPS, 4)},
+           "kv_proj": {"streams": 8, "width": d, "tflop": round(fl_kv / 1e12, 4),
+                       "tflop_s": round(fl_kv / (t["kv_proj"] * 1e-3) / 1e12, 1),
+                       "frac_bf16_peak": round(fl_kv / (t["kv_proj"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
     return res
 
 

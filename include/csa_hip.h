@@ -443,6 +443,22 @@ csa_status csa_query_proj_shared(const void* x, const void* w_dq, const void* w_
                                  void* q_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * csa_kv_proj — the compressor's input streams from the hidden state (the
+ * KV and gate projections in front of the compressor; cf-1.com write-up
+ * §3.1 builds the compressed entries from per-token KV vectors and gate
+ * logits of the two overlapped streams, §3.4 has the indexer's keys built
+ * the same way): streams[s] [T, width] = x [T, D] * w[s]^T for s <
+ * n_streams, w [n_streams, width, D] (bf16, one linear layer's weight per
+ * stream), streams [n_streams, T, width] of out_t (CSA_BF16 or CSA_F32),
+ * stream s starting s * T * width elements in. For csa_compress the four
+ * streams are C_a, C_b, Z_a, Z_b (n_streams 4, width 128 or the indexer's
+ * d_I); rows of several sequences [B, T] are T = B * T rows. D a multiple of
+ * 64; x and w 16-byte aligned. No workspace.
+ */
+csa_status csa_kv_proj(const void* x, const void* w, int64_t T, int32_t D, int32_t n_streams, int32_t width,
+                       void* streams, csa_dtype out_t, hipStream_t stream);
+
+/*
  * sparse_attn_bwd — gradients of sparse_attn_fwd (cf-1.com write-up §4.3:
  * training runs a deterministic attention backward; the formulas are the
  * derivatives of the forward's definition above). With P_i = e^{l_i - lse_h},

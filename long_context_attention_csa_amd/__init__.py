@@ -12,4 +12,4 @@ from .ops import (csa_append_state, csa_compress, csa_compress_append,  # noqa: 
                   sparse_attn_noalloc_scratch_bytes, sparse_attn_workspace_size,
                   window_append, state_checkpoint, state_restore, ring_fill,
                   linear_bf16, grouped_out_proj, query_proj_shared,
-                  grouped_out_proj_workspace_size, query_proj_shared_workspace_size)
+                  grouped_out_proj_workspace_size, query_proj_shared_workspace_size, kv_proj)

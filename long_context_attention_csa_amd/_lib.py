@@ -60,6 +60,7 @@ SIGNATURES = {
     "csa_grouped_out_proj": (ctypes.c_int, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "csa_query_proj_shared_workspace_size": (_SZ, [_I64, _I32]),
     "csa_query_proj_shared": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "csa_kv_proj": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _P, _I32, _P]),
     "sparse_attn_bwd_workspace_size": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
     "sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _I64, _I32, _I32,
                                        _I32, _I32, _F, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),

@@ -603,6 +603,22 @@ csa_status csa_query_proj_shared(const void* x, const void* w_dq, const void* w_
   return csa_linear_bf16(ws, r_q, 0, w_iq, r_q, 0, q_idx, CSA_BF16, n_i, 0, T, n_i, r_q, 1, stream); // indexer queries
 }
 
+csa_status csa_kv_proj(const void* x, const void* w, int64_t T, int32_t D, int32_t n_streams, int32_t width,
+                       void* streams, csa_dtype out_t, hipStream_t stream) {
+  g_last_error.clear();
+  const char* fn = "csa_kv_proj";
+  CSA_REQUIRE(out_t == CSA_BF16 || out_t == CSA_F32, CSA_ERR_UNSUPPORTED, "%s: output must be CSA_BF16 or CSA_F32",
+              fn);
+  CSA_REQUIRE(T >= 0 && D >= 1 && n_streams >= 1 && n_streams <= 65535 && width >= 1, CSA_ERR_SHAPE,
+              "%s: T=%lld D=%d n_streams=%d width=%d", fn, (long long)T, D, n_streams, width);
+  CSA_REQUIRE(D % 64 == 0, CSA_ERR_SHAPE, "%s: D=%d must be a multiple of 64", fn, D);
+  if (T == 0) return CSA_OK;
+  CSA_REQUIRE(x && w && streams, CSA_ERR_NULL, "%s: NULL tensor", fn);
+  // stream s = x * w[s]^T: one group per stream, every group reading the same x
+  return csa_linear_bf16(x, D, 0, w, D, (int64_t)width * D, streams, out_t, width, T * width, T, width, D,
+                         n_streams, stream);
+}
+
 static csa_status check_attn_bwd(const char* fn, const void* q, const void* kv, const void* x_win,
                                  const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t,
                                  int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d,

@@ -23,7 +23,7 @@
 // columns of one row of C (one 8- or 16-byte store when C's rows are 16-byte
 // aligned, else 4 element stores). Rows past M or N read the last valid row
 // and are not stored; K is a multiple of 64. Problems with at least 256
-// tiles of 256 x 256 use the large-tile kernel below instead (8 waves,
+// tiles of 256 x 256 (and M, N >= 256) use the large-tile kernel below (8 waves,
 // 128 x 64 each); the chunk swizzle of both is c ^ ((r / 2) mod 8), which
 // puts the 16 rows of a fragment read (two 128-byte rows per 256-byte bank
 // line) on 16 different bank groups.
@@ -289,7 +289,8 @@ hipError_t launch_gemm_bf16(const void* A, int64_t lda, int64_t sA, const void* 
   // 4-element vector stores when every row of C starts 16-byte aligned
   const int vec_c = (ldc % 4 == 0 && sC % 4 == 0 && ((uintptr_t)C & 15) == 0) ? 1 : 0;
   const int bm = (int)cdiv(M, kBM), bn = (int)cdiv(N, kBN);
-  if ((int64_t)bm * bn * G >= 256) {   // enough large tiles to fill the chip
+  // large tiles when they fill the chip and are not mostly padding
+  if ((int64_t)bm * bn * G >= 256 && M >= kBM && N >= kBN) {
     const dim3 grid((unsigned)(bm * bn), (unsigned)G);
     timer_before(CSA_KID_GEMM, s);
     if (out_bf16)

@@ -8,6 +8,7 @@ HIP kernels of libcsa_hip.so; nothing here computes.
 from __future__ import annotations
 
 import ctypes
+import math
 
 import torch
 
@@ -408,3 +409,19 @@ def query_proj_shared(x, w_dq, w_uq, w_iq, ws=None):
                                                                r_q, n_q, n_i, _ptr(q), _ptr(qi), _ptr(ws), nbytes,
                                                                _stream()))
     return q, qi
+
+
+def kv_proj(x, w, out_dtype=torch.bfloat16, out=None):
+    """Compressor input streams from the hidden state: x [..., D] bf16 (rows of
+    any leading shape), w [S, width, D] bf16 -> [S, ..., width] (stream s =
+    x w[s]^T; for csa_compress the streams C_a, C_b, Z_a, Z_b)."""
+    _contig(x, w, out)
+    lead = x.shape[:-1]
+    D = x.shape[-1]
+    T = math.prod(lead)
+    S, width = w.shape[:2]
+    if out is None:
+        out = torch.empty(S, *lead, width, dtype=out_dtype, device=x.device)
+    check("csa_kv_proj", lib().csa_kv_proj(_ptr(x), _ptr(w), T, D, S, width, _ptr(out), _float_dtype(out),
+                                           _stream()))
+    return out

@@ -601,3 +601,14 @@ def shared_query_projection(x, w_dq, w_uq, w_iq):
     x = np.asarray(x, dtype=np.float64)
     latent = x @ np.asarray(w_dq, dtype=np.float64).T
     return latent @ np.asarray(w_uq, dtype=np.float64).T, latent @ np.asarray(w_iq, dtype=np.float64).T
+
+
+def kv_projection(x, w):
+    """The compressor's input streams from the hidden state (cf-1.com write-up
+    §3.1: the compressed entries are built from per-token KV vectors and gate
+    logits; §3.4: the indexer's keys are built the same way): stream s is
+    x w[s]^T for x [T, D] and w [S, width, D] (one linear layer's weight per
+    stream). Returns float64 [S, T, width]."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    return np.stack([x @ w[s].T for s in range(w.shape[0])])

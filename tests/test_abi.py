@@ -276,3 +276,10 @@ def test_projection_validation():
     assert qps(P, P, P, P, 8, 128, 96, 256, 256, P, P, P, need, None) == SHAPE      # r_q not a multiple of 64
     assert qps(P, P, P, P, 8, 128, 128, 256, 256, P, None, P, need, None) == NULL
     assert qps(P, P, P, P, 8, 128, 128, 256, 256, P, P, P, need - 1, None) == WS
+    kvp = lib.csa_kv_proj
+    # x, w, T, D, n_streams, width, streams, out_t, stream
+    assert kvp(P, P, 8, 100, 4, 128, P, BF16, None) == SHAPE      # D not a multiple of 64
+    assert kvp(P, P, 8, 128, 0, 128, P, BF16, None) == SHAPE      # no stream
+    assert kvp(P, P, 8, 128, 4, 128, P, FP8, None) == UNSUP       # output type
+    assert kvp(P, None, 8, 128, 4, 128, P, BF16, None) == NULL
+    assert kvp(None, None, 0, 128, 4, 128, None, BF16, None) == OK   # no rows

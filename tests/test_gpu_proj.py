@@ -82,3 +82,20 @@ def test_query_proj_shared():
     wq, wqi = O.shared_query_projection(x, wdq, wuq, wiq)
     _close(host(q), wq, "attention queries")
     _close(host(qi), wqi, "indexer queries")
+
+
+@pytest.mark.parametrize("B,T,D,S,width,out_dtype", [(1, 300, 512, 4, 128, BF), (2, 77, 256, 8, 64, torch.float32),
+                                                     (1, 2048, 1024, 8, 128, BF)])
+def test_kv_proj(B, T, D, S, width, out_dtype):
+    """The compressor's input streams from the hidden state, then the CSA
+    compressor on the projected streams, against the oracle."""
+    x = syn.normal(1111, (B, T, D), bf16=True)
+    w = _w(1112, (S, width, D), D)
+    got = C.kv_proj(dev(x, BF), dev(w, BF), out_dtype)
+    assert tuple(got.shape) == (S, B, T, width)
+    want = O.kv_projection(x.reshape(B * T, D), w).reshape(S, B, T, width)
+    _close(host(got), want, f"kv_proj B={B} T={T} D={D} S={S}")
+    if S >= 4 and out_dtype == torch.float32:
+        e = C.csa_compress(got[0], got[1], got[2], got[3], 4)
+        for b in range(B):
+            _close(host(e)[b], O.csa_compress(*(want[s, b] for s in range(4)), ratio=4), f"compress b={b}")

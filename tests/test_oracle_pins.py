@@ -731,3 +731,30 @@ def test_shared_query_projection_associativity():
     q2, qi2 = O.shared_query_projection(x, 2.5 * wdq, wuq, wiq)
     np.testing.assert_allclose(q2, 2.5 * q, rtol=1e-13)
     np.testing.assert_allclose(qi2, 2.5 * qi, rtol=1e-13)
+
+
+def test_kv_projection_brute_force_and_compression():
+    """Each stream entry is the explicit sum over the hidden dimension; and a
+    projection whose weights pick hidden channels (one-hot rows) turns the
+    projected streams into those channels, so compressing them equals
+    compressing the picked channels directly."""
+    g = np.random.default_rng(11)
+    T, D, S, W = 6, 8, 3, 4
+    x = g.standard_normal((T, D))
+    w = g.standard_normal((S, W, D))
+    got = O.kv_projection(x, w)
+    for s in range(S):
+        for t in range(T):
+            for c in range(W):
+                assert abs(got[s, t, c] - sum(x[t, i] * w[s, c, i] for i in range(D))) < 1e-12
+    # one-hot selection rows: stream s, channel c reads hidden channel (s W + c) mod D2
+    T2, D2, W2 = 16, 32, 8
+    x2 = g.standard_normal((T2, D2))
+    sel = np.zeros((4, W2, D2))
+    for s in range(4):
+        for c in range(W2):
+            sel[s, c, (s * W2 + c) % D2] = 1.0
+    st = O.kv_projection(x2, sel)
+    picked = [x2[:, [(s * W2 + c) % D2 for c in range(W2)]] for s in range(4)]
+    np.testing.assert_array_equal(st, np.stack(picked))
+    np.testing.assert_allclose(O.csa_compress(*st, ratio=4), O.csa_compress(*picked, ratio=4), rtol=1e-14, atol=1e-15)
