@@ -140,3 +140,27 @@ def test_lists_normal_operands(fmt):
         scores = O.indexer_scores(qd, d["w"][b][None], kd, q_pos[b], 4)
         want = O.topk_select(scores, n_vis, k)
         assert certified_index_mismatches(got[b], want, scores, n_vis, k) <= 1
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "fp4"])
+def test_lists_stale_slots_masked(fmt):
+    """One workspace for two calls: the first fills every list slot (whole
+    rows visible), the second sees shorter rows, so the slots of score blocks
+    past a row's visible entries still hold the first call's composites; the
+    selection must ignore them. The second call also has a row with n <= k
+    (the short-row exit, whose list loads are already in flight)."""
+    B, N, H_I, k = 3, 40000, 64, 128
+    q_i = _grid(fmt, 71, (B, 1, H_I, 128))
+    k_i = _grid(fmt, 72, (B, N, 128))
+    w = syn.grid_weights(73, (B, 1, H_I))
+    qc, qs = _codes(fmt, q_i)
+    kc, ks = _codes(fmt, k_i)
+    ws = torch.empty(C.indexer_topk_workspace_size(B, 1, N, H_I, 128, k, fmt), dtype=torch.uint8, device="cuda")
+    _print("lists stale slots", fmt)
+    for q_pos in (np.full((B, 1), 4 * N, np.int32), np.array([[4 * 3001 + 2], [4 * 100], [4 * 20000]], np.int32)):
+        idx = C.indexer_topk(qc, qs, dev(w), kc, ks, fmt, dev(q_pos, torch.int32), 4, k, 128, ws=ws)
+        got = host(idx)
+        for b in range(B):
+            n_vis = O.visible_entries(q_pos[b], 4, N)
+            scores = O.indexer_scores(q_i[b], w[b], k_i[b], q_pos[b], 4)
+            assert np.array_equal(got[b], O.topk_select(scores, n_vis, k)), f"q_pos={q_pos[b]} b={b}"
