@@ -66,7 +66,32 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_native_demo(verbose)
     return LIB
+
+
+# A plain C program that drives the library through its C ABI alone (no
+# Python), used by the tests: tests/native/layer_demo.c -> tests/native/layer_demo.
+DEMO_SRC = os.path.join(os.path.dirname(HERE), "tests", "native", "layer_demo.c")
+DEMO = os.path.join(os.path.dirname(HERE), "tests", "native", "layer_demo")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_native_demo(verbose: bool = True) -> str | None:
+    if not os.path.exists(DEMO_SRC):
+        return None
+    cc = os.environ.get("CC", "gcc")
+    inc = os.path.join(os.path.dirname(HERE), "include")
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{inc}",
+           f"-I{ROCM}/include", DEMO_SRC, f"-L{HERE}", "-lcsa_hip", f"-L{ROCM}/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../long_context_attention_csa_amd", f"-Wl,-rpath,{ROCM}/lib", "-o", DEMO + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building {DEMO_SRC} failed:\n{r.stdout}{r.stderr}")
+    os.replace(DEMO + ".tmp", DEMO)
+    if verbose:
+        print(f"built {DEMO}")
+    return DEMO
 
 
 if __name__ == "__main__":
