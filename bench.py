@@ -16,11 +16,13 @@ Also reported: the step's algorithmic HBM bytes / step time, the dominant
 kernel's roofline fraction (the indexer's score stage: back-to-back launches
 in one HIP graph timed with HIP events on the stream they run on), the
 selection recall of the fp4 keys against float32, the CPU oracle timed on a
-bounded sample, and extra workloads (CSA decode at 262k context, cache
-appends, prefill and backward TFLOP/s, projections) under "extras".
+bounded sample, and extra workloads (the same decode pair at batches 16, 32
+and 64, CSA decode at 262k context, cache appends, prefill and backward
+TFLOP/s, projections) under "extras".
 
 Usage: python bench.py [--steps K] [--warmup W]
-                       [--extras decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca,proj|none]
+                       [--extras decode_batches,decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,
+                                 prefill_chunk,bwd_csa,bwd_hca,proj|none]
 """
 from __future__ import annotations
 
@@ -140,6 +142,28 @@ def decode_workload(torch, C, syn, name, B, L, H, H_I, d_I, k, fmt, hca, copies,
     st["name"] = name
     st["hca"] = hca
     return st
+
+
+def decode_batches(torch, C, syn, steps, warmup):
+    """The 1M-context decode pair (the headline step) at larger batches, two
+    rotated cache copies (every copy's step reads more than the 256 MB
+    Infinity Cache holds): the step's fixed per-kernel latencies amortise over
+    more sequences, and its HBM rate approaches the score stage's."""
+    rows = []
+    for B in (16, 32, 64):
+        st = decode_workload(torch, C, syn, f"csa_hca_decode_pair_1m_ctx_b{B}", B=B, L=1 << 20, H=128, H_I=64,
+                             d_I=128, k=1024, fmt="fp4", hca=True, copies=2, wid=7, host_sample=False)
+        del st["ki32_rows"]
+        torch.cuda.synchronize()
+        ms, _ = time_graphs(torch, st, 2, steps, warmup)
+        gbs = st["bytes"] / (ms * 1e-3) / 1e9
+        rows.append({"batch": B, "us_per_step": round(ms * 1e3, 1), "queries_per_s": round(B / (ms * 1e-3), 1),
+                     "step_bytes": st["bytes"], "hbm_gb_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+        log(f"[bench] decode pair 1M, batch {B}: {rows[-1]}")
+        del st
+        torch.cuda.empty_cache()
+    return {"workload": "csa_hca_decode_pair_1m_ctx_batches", "rows": rows, "cache_copies": 2,
+            "timing": "hip graph replay"}
 
 
 def time_graphs(torch, st, copies, steps, warmup, use_graph=True):
@@ -681,9 +705,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=4, help="rotated cache copies (defeats the Infinity Cache)")
-    ap.add_argument("--extras", default="decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,prefill_chunk,bwd_csa,bwd_hca,"
+    ap.add_argument("--extras", default="decode_batches,decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,"
+                                        "prefill_chunk,bwd_csa,bwd_hca,"
                                         "proj",
-                    help="comma list of decode4,decode_append,prefill_csa,prefill_hca,prefill_chunk or 'none'")
+                    help="comma list of decode_batches,decode4,decode_bf16,decode_append,prefill_csa,prefill_hca,"
+                         "prefill_chunk,bwd_csa,bwd_hca,proj or 'none'")
     ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -771,6 +797,9 @@ def main():
             "kernel_us": {k_: (None if v is None else round(v * 1e3, 2)) for k_, v in ktb.items()}}
         del stb
         torch.cuda.empty_cache()
+    if "decode_batches" in wanted:
+        r = decode_batches(torch, C, syn, args.steps, args.warmup)
+        extras[r["workload"]] = r
     if "decode4" in wanted:
         st4, ms4, wall4, kt4 = run_decode(torch, C, syn, O, args, "decode4")
         extras["csa_decode_262k_ctx"] = {
