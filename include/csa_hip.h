@@ -284,6 +284,7 @@ enum { CSA_ATTN_WIN_RING = 1, CSA_ATTN_BATCH_INVARIANT = 2 };
  *   ws     the workspace sparse_attn_workspace_size() returns for the same
  *          shapes and flags (NULL allowed when it returns 0)
  *   flags  CSA_ATTN_* options
+ *   scale  the softmax scale (e.g. 1/sqrt(d)): finite and > 0, else CSA_ERR_SHAPE
  *   d == 128; H a multiple of 16, <= 256; 1 <= k <= 4096; window >= 0; B*Tq < 2^31.
  * Accumulation is float32; a query with no keys and no sink gives o = 0 and
  * lse = -inf.
@@ -474,8 +475,8 @@ csa_status csa_kv_proj(const void* x, const void* w, int64_t T, int32_t D, int32
  *   dq         [B, Tq, H, d] of t
  *   dkv        float32 [B, N, d];  dx_win float32 [B, T_win, d]
  *   dsink      float32 [H] (summed over B and Tq), or NULL when sink is NULL
- * Limits: t == CSA_BF16, H 64 or 128, d == 128, 1 <= k <= 4096,
- * B*Tq < 2^31, B*(N + T_win) < 2^31; idx rows as indexer_topk writes them
+ * Limits: t == CSA_BF16, H 64 or 128, d == 128, 1 <= k <= 4096, scale as in
+ * the forward, B*Tq < 2^31, B*(N + T_win) < 2^31; idx rows as indexer_topk writes them
  * (an entry repeated within a row is counted once per occurrence).
  * Deterministic: every sum runs in a fixed order that depends only on the
  * shapes (no floating-point atomics), so repeated calls give identical bits.

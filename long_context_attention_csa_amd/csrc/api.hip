@@ -324,8 +324,12 @@ csa_status indexer_topk_bf16_scores(const void* q_idx, const void* q_scale, cons
 static csa_status check_attn_common(const char* fn, const void* q, const void* kv, const void* x_win,
                                     const int32_t* win_start, const int32_t* q_pos, csa_dtype t, int64_t B,
                                     int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d, int32_t window,
-                                    void* out) {
+                                    float scale, void* out) {
   CSA_REQUIRE(is_dtype(t), CSA_ERR_UNSUPPORTED, "%s: unknown dtype", fn);
+  // the kernels mask keys with a logit of -inf and take the running maximum
+  // of unscaled logits: both rely on a positive scale
+  CSA_REQUIRE(scale > 0.f && scale <= 3.402823466e38f, CSA_ERR_SHAPE, "%s: scale %g (finite and > 0)", fn,
+              (double)scale);
   CSA_REQUIRE(is_float(t), CSA_ERR_UNSUPPORTED, "%s: dtype must be CSA_F32 or CSA_BF16", fn);
   CSA_REQUIRE(B >= 0 && Tq >= 0 && N >= 0 && T_win >= 0 && window >= 0, CSA_ERR_SHAPE,
               "%s: B=%lld Tq=%lld N=%lld T_win=%lld window=%d", fn, (long long)B, (long long)Tq, (long long)N,
@@ -357,7 +361,7 @@ csa_status sparse_attn_fwd(const void* q, const void* kv, const int32_t* idx, co
                            hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_common("sparse_attn_fwd", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win, H, d,
-                                    window, out);
+                                    window, scale, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_SHAPE, "sparse_attn_fwd: k %d (1..4096)", k);
   CSA_REQUIRE((flags & ~kAttnFlags) == 0, CSA_ERR_SHAPE, "sparse_attn_fwd: unknown flags 0x%x", flags);
@@ -388,7 +392,7 @@ csa_status dense_compressed_attn_fwd(const void* q, const void* kv, const void* 
                                      hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_common("dense_compressed_attn_fwd", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win,
-                                    H, d, window, out);
+                                    H, d, window, scale, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "dense_compressed_attn_fwd: ratio %d", ratio);
   CSA_REQUIRE((flags & ~kAttnFlags) == 0, CSA_ERR_SHAPE, "dense_compressed_attn_fwd: unknown flags 0x%x", flags);
@@ -442,7 +446,7 @@ csa_status sparse_attn_fwd_noalloc(const void* q, const void* kv, const int32_t*
                                    hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_common("sparse_attn_fwd_noalloc", q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win,
-                                    H, d, window, out);
+                                    H, d, window, scale, out);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_SHAPE, "sparse_attn_fwd_noalloc: k %d (1..4096)", k);
   CSA_REQUIRE((flags & ~kAttnFlags) == 0, CSA_ERR_SHAPE, "sparse_attn_fwd_noalloc: unknown flags 0x%x", flags);
@@ -622,9 +626,9 @@ csa_status csa_kv_proj(const void* x, const void* w, int64_t T, int32_t D, int32
 static csa_status check_attn_bwd(const char* fn, const void* q, const void* kv, const void* x_win,
                                  const int32_t* win_start, const float* sink, const int32_t* q_pos, csa_dtype t,
                                  int64_t B, int64_t Tq, int64_t N, int64_t T_win, int32_t H, int32_t d,
-                                 int32_t window, const void* out, const float* lse, const void* dout, void* dq,
-                                 float* dkv, float* dx_win, float* dsink) {
-  csa_status st = check_attn_common(fn, q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win, H, d, window,
+                                 int32_t window, float scale, const void* out, const float* lse, const void* dout,
+                                 void* dq, float* dkv, float* dx_win, float* dsink) {
+  csa_status st = check_attn_common(fn, q, kv, x_win, win_start, q_pos, t, B, Tq, N, T_win, H, d, window, scale,
                                     const_cast<void*>(out));
   if (st != CSA_OK) return st;
   CSA_REQUIRE(t == CSA_BF16, CSA_ERR_UNSUPPORTED, "%s: dtype must be CSA_BF16", fn);
@@ -652,7 +656,7 @@ csa_status sparse_attn_bwd(const void* q, const void* kv, const int32_t* idx, co
                            float* dx_win, float* dsink, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_bwd("sparse_attn_bwd", q, kv, x_win, win_start, sink, q_pos, t, B, Tq, N, T_win, H, d,
-                                 window, out, lse, dout, dq, dkv, dx_win, dsink);
+                                 window, scale, out, lse, dout, dq, dkv, dx_win, dsink);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(k >= 1 && k <= 4096, CSA_ERR_SHAPE, "sparse_attn_bwd: k %d (1..4096)", k);
   if (B * Tq == 0) return CSA_OK;
@@ -680,7 +684,7 @@ csa_status dense_compressed_attn_bwd(const void* q, const void* kv, const void* 
                                      hipStream_t stream) {
   g_last_error.clear();
   csa_status st = check_attn_bwd("dense_compressed_attn_bwd", q, kv, x_win, win_start, sink, q_pos, t, B, Tq, N,
-                                 T_win, H, d, window, out, lse, dout, dq, dkv, dx_win, dsink);
+                                 T_win, H, d, window, scale, out, lse, dout, dq, dkv, dx_win, dsink);
   if (st != CSA_OK) return st;
   CSA_REQUIRE(ratio >= 1, CSA_ERR_SHAPE, "dense_compressed_attn_bwd: ratio %d", ratio);
   if (B * Tq == 0) return CSA_OK;

@@ -562,6 +562,12 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
       if (c0 == kbeg) load_q();
     }
     const int ntiles = (clen + kKT - 1) / kKT;
+    // Keys [0, sel_end) of the section are entries (selected or dense), the
+    // rest window rows; window row of key kk >= sel_end: wbase + kk, less
+    // T_win once past the end of a ring.
+    const int64_t se = n_sel - c0;
+    const int sel_end = se <= 0 ? 0 : (se < (int64_t)clen ? (int)se : clen);
+    const int64_t wbase = wrow0 - se;
     // Gather instruction j of this lane: tile row grow(j) (4 rows per wave
     // instruction), 16-byte chunk gcol(j) of it (swizzled position lane & 15):
     // grow(j) mod 16 = 4 ((j NWT + wv) mod 4) + lane / 16, and (j NWT + wv)
@@ -571,34 +577,34 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
     const int gc0 = ((lane & 15) ^ (((wv & 3) << 2) | (lane >> 4))) << 3;
     auto grow = [&](int j) { return (j * NWT + wv) * 4 + (lane >> 4); };
     auto gcol = [&](int j) { return gc0 ^ (((j * NWT) & 3) << 5); };
-    // key kk of the section: its row, or null when the slot holds no key
-    auto key_src = [&](int kk) -> const uint16_t* {
-      if (kk >= clen) return nullptr;
-      const int64_t ki = c0 + kk;
-      if (ki < n_sel) {
-        const int64_t e = SPARSE ? (int64_t)sidx[kk] : ki;
-        return (e >= 0 && e < N) ? kvb + e * kD : nullptr;
-      }
-      int64_t wr = wrow0 + (ki - n_sel);
-      if (wr >= T_win) wr -= T_win;
-      return xwb + wr * kD;
+    // whether key kk of the section holds a key: inside the section and, for a
+    // selected entry, an index in [0, N)
+    const uint32_t n32 = N < ((int64_t)1 << 31) ? (uint32_t)N : 0x80000000u;
+    auto key_ok = [&](int kk) {
+      if constexpr (SPARSE) return kk < clen && (kk >= sel_end || (uint32_t)sidx[kk] < n32);
+      else return kk < clen;
     };
     auto issue = [&](int t) {
       const int slot = t % NBUF;
       uint16_t* base = ring[slot];
       const int kk0 = t * kKT;
-      const int64_t t0k = c0 + kk0;
+      const int nt = (clen - kk0) < kKT ? (clen - kk0) : kKT;   // keys of the tile
       bool bad = false;
-      int64_t wt = wrow0 + (t0k - n_sel);   // window row of the tile's first key (window tiles)
+      int64_t wt = wbase + kk0;   // window row of the tile's first key (window tiles)
       if (wt >= T_win) wt -= T_win;
-      if (kk0 + kKT <= clen && ((t0k >= n_sel && wt + kKT <= T_win) || (!SPARSE && t0k + kKT <= n_sel))) {
+      const bool win_run = kk0 >= sel_end && wt + nt <= T_win;
+      if (win_run || (!SPARSE && kk0 + nt <= sel_end)) {
         // the tile's keys are consecutive rows: window rows (not wrapping
-        // around a ring), or entries
-        const uint16_t* tb = t0k >= n_sel ? xwb + wt * kD : kvb + t0k * kD;
+        // around a ring), or dense entries; the rows of a partial tile past
+        // its last key repeat that key (masked)
+        const uint16_t* tb = win_run ? xwb + wt * kD : kvb + (c0 + kk0) * kD;
 #pragma unroll
-        for (int j = 0; j < LPT; ++j)
-          gather_lds16(tb + grow(j) * kD + gcol(j), (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
-      } else if (SPARSE && offs32 && kk0 + kKT <= clen && t0k + kKT <= n_sel) {
+        for (int j = 0; j < LPT; ++j) {
+          const int row = grow(j) < nt ? grow(j) : nt - 1;
+          gather_lds16_s(tb, (uint32_t)row * (uint32_t)(kD * 2) + (uint32_t)gcol(j) * 2u,
+                         (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
+        }
+      } else if (SPARSE && offs32 && kk0 + kKT <= sel_end) {
         // 64 selected entries: byte offsets from the batch's first entry (an
         // entry outside [0, N) reads entry 0 and is marked). All index reads
         // go first: a gather statement orders memory accesses around it, so
@@ -609,17 +615,31 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
           const int32_t e = ent[j];
-          const bool ok = (uint32_t)e < (uint32_t)N;
+          const bool ok = (uint32_t)e < n32;
           bad |= !ok;
           gather_lds16_s(kvb, (ok ? (uint32_t)e * (uint32_t)(kD * 2) : 0u) + (uint32_t)gcol(j) * 2u,
                          (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
         }
       } else {
+        // entries and window rows mixed, a window run that wraps, or entries
+        // past 2^24: one address per gather; rows past the section's end
+        // repeat its last key and an entry outside [0, N) reads a finite row
+        // (both masked)
 #pragma unroll
         for (int j = 0; j < LPT; ++j) {
-          const uint16_t* src = key_src(kk0 + grow(j));
-          bad |= src == nullptr;
-          gather_lds16((src ? src : dummy) + gcol(j), (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
+          const int kk = (kk0 + grow(j)) < clen ? kk0 + grow(j) : clen - 1;
+          const uint16_t* src;
+          if (kk < sel_end) {
+            const int64_t e = SPARSE ? (int64_t)sidx[kk] : c0 + kk;
+            const bool ok = e >= 0 && e < N;
+            bad |= !ok;
+            src = ok ? kvb + e * kD : dummy;
+          } else {
+            int64_t wr = wbase + kk;
+            if (wr >= T_win) wr -= T_win;
+            src = xwb + wr * kD;
+          }
+          gather_lds16(src + gcol(j), (uint32_t)(uintptr_t)(base + (j * NWT + wv) * 4 * kD));
         }
       }
       const bool wbad = __ballot(bad) != 0ull;
@@ -655,8 +675,8 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
 #pragma unroll
       for (int w = 0; w < NWT; ++w) holed |= tbadw[slot][w] != 0;
       // slots without a key hold a finite row (the query's) and get probability 0
-      attn_tile16<HPW>(tb, tl, nt < kKT || holed, [&](int key) { return key_src(t * kKT + key) != nullptr; },
-                       qf, scale2, m, lsum, O);
+      attn_tile16<HPW>(tb, tl, nt < kKT || holed, [&](int key) { return key_ok(t * kKT + key); }, qf, scale2,
+                       m, lsum, O);
       }   // t < ntiles
       __syncthreads();   // the slots are refilled by later issue() calls
     }
@@ -698,6 +718,10 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
     }
   }
 
+  // O's factor at the output (the sink's rescale of O is folded into it)
+  float osc[HPW];
+#pragma unroll
+  for (int hb = 0; hb < HPW; ++hb) osc[hb] = 1.f;
   if (sink != nullptr && sp == 0) {
     // The sink is one more logit (value 0) of split 0: it joins the
     // denominator, with the running max raised to it when larger.
@@ -708,8 +732,7 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
       const float a0 = m[hb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[hb] - mm);
       lsum[hb] = lsum[hb] * a0 + (g == 0 ? __builtin_amdgcn_exp2f(ms - mm) : 0.f);
       m[hb] = mm;
-#pragma unroll
-      for (int db = 0; db < kD / 16; ++db) O[hb][db] *= a0;
+      osc[hb] = a0;
     }
   }
 
@@ -720,7 +743,7 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
     l += __shfl_xor(l, 32);
     const int head = h0 + 16 * hb + col;
     if (S == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float inv = l > 0.f ? osc[hb] / l : 0.f;
       uint16_t* orow = out + (r * H + head) * kD;
 #pragma unroll
       for (int db = 0; db < kD / 16; ++db)   // round to nearest even (v_cvt_pk_bf16_f32)
@@ -734,7 +757,7 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
       // their rounding stays within that of the bf16 output) and (m, l).
       const int64_t pi = (r * H + head) * S + sp;
       uint16_t* po = reinterpret_cast<uint16_t*>(part_o) + pi * kD;
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const float inv = l > 0.f ? osc[hb] / l : 0.f;
 #pragma unroll
       for (int db = 0; db < kD / 16; ++db)
         *reinterpret_cast<uint2*>(po + 16 * db + 4 * g) =

@@ -117,7 +117,8 @@ def test_attention_validation():
     base = [P, P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 64, 128, 1.0, P, None, P, 1 << 40, 0, None]
     def call(**kw):
         a = list(base)
-        pos = {"t": 7, "H": 12, "d": 13, "k": 14, "window": 15, "q": 0, "ws": 19, "wsb": 20, "flags": 21, "idx": 2}
+        pos = {"t": 7, "H": 12, "d": 13, "k": 14, "window": 15, "scale": 16, "q": 0, "ws": 19, "wsb": 20,
+               "flags": 21, "idx": 2}
         for k_, v in kw.items():
             a[pos[k_]] = v
         return f(*a)
@@ -130,6 +131,15 @@ def test_attention_validation():
     assert "flags" in _err(lib)
     assert call(q=None) == NULL
     assert call(idx=None) == NULL
+    # the softmax scale must be finite and positive (keys are masked with a -inf logit)
+    for bad in (0.0, -0.5, float("nan"), float("inf")):
+        assert call(scale=bad) == SHAPE, bad
+        assert "scale" in _err(lib)
+    h = lib.sparse_attn_bwd
+    #       q  kv idx xw ws0 sink pos t  B  Tq N   T_win H   d    k   win  scale out lse dout dq dkv dxw dsink ws wsb stream
+    assert h(P, P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 64, 128, -1.0, P, P, P, P, P, P, None, P, 1 << 40,
+             None) == SHAPE
+    assert "scale" in _err(lib)
     g = lib.dense_compressed_attn_fwd
     #   q  kv xw ws0 sink pos t  B  Tq N   T_win H   d    ratio win scale out lse ws wsb     flags stream
     assert g(P, P, P, P, None, P, 1, 1, 1, 64, 128, 64, 128, 0, 128, 1.0, P, None, P, 1 << 40, 0, None) == SHAPE
