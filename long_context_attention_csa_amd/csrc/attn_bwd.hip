@@ -622,12 +622,16 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd16(
 // (entries past n(p) get P = 0) and adds G^T = Q^T (scale dl) + dO^T P to
 // accumulators that live in registers across the rows. Each block writes its
 // segment's partial once; k_bwd_seg_reduce adds the segments in order. This
-// replaces a 512-byte contribution row per (query, entry).
+// replaces a 512-byte contribution row per (query, entry). Block order:
+// consecutive block numbers go round-robin to the 8 XCDs, and all entry
+// blocks of one segment get numbers of one residue mod 8, so they run on one
+// XCD and each row's Q and dO come from that XCD's L2 after the first read
+// (rather than from HBM once per XCD that holds one of the entry blocks).
 template <int HPW>
 __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd_dense_kv(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ q_pos,
     const float* __restrict__ Dv, const float* __restrict__ lse, const uint16_t* __restrict__ dout, int64_t Tq,
-    int64_t N, int ratio, float scale, int64_t seg, int nseg, float* __restrict__ part) {
+    int64_t N, int ratio, float scale, int64_t seg, int nseg, int64_t nsg, int nkb, float* __restrict__ part) {
   constexpr int H = 64 * HPW;
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ __align__(16) uint16_t kt[kKT * kD];      // the block's 64 entries
@@ -640,8 +644,11 @@ __global__ __launch_bounds__(kBwdThreads, HPW == 1 ? 2 : 1) void k_attn_bwd_dens
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, col = lane & 15;
   const TileLanes tl(lane, 15);
-  const int64_t e0 = (int64_t)blockIdx.x * kKT;
-  const int64_t b = blockIdx.y / nseg, sgi = blockIdx.y % nseg;
+  const int64_t xcd = blockIdx.x % 8, kx = blockIdx.x / 8;
+  const int64_t sg = (kx / nkb) * 8 + xcd;   // segment b * nseg + sgi
+  if (sg >= nsg) return;                      // uniform: the grid is padded to whole groups of 8
+  const int64_t e0 = (kx % nkb) * kKT;
+  const int64_t b = sg / nseg, sgi = sg % nseg;
   const int64_t t0 = sgi * seg, t1 = (t0 + seg) < Tq ? (t0 + seg) : Tq;
   const int h0 = wv * 16 * HPW;
   const float scale2 = scale * kLog2e;
@@ -962,14 +969,15 @@ static hipError_t run_attn_bwd(const uint16_t* q, const uint16_t* kv, const int3
   }
   if (!SPARSE && p.nseg > 0) {   // dense: the entries' gradients, summed over query segments
     float* part = reinterpret_cast<float*>(wb + p.o_part);
-    const dim3 grid((unsigned)p.nkb, (unsigned)(B * p.nseg));
+    const int64_t nsg = B * p.nseg;
+    const unsigned grid = (unsigned)(p.nkb * 8 * cdiv(nsg, 8));
     timer_before(CSA_KID_ATTN_BWD, s);
     if (H == 64)
       k_attn_bwd_dense_kv<1><<<grid, kBwdThreads, 0, s>>>(q, kv, q_pos, delta, lse, dout, Tq, N, ratio, scale, p.seg,
-                                                         (int)p.nseg, part);
+                                                         (int)p.nseg, nsg, (int)p.nkb, part);
     else
       k_attn_bwd_dense_kv<2><<<grid, kBwdThreads, 0, s>>>(q, kv, q_pos, delta, lse, dout, Tq, N, ratio, scale, p.seg,
-                                                         (int)p.nseg, part);
+                                                         (int)p.nseg, nsg, (int)p.nkb, part);
     hipError_t e = hipGetLastError();
     timer_after(CSA_KID_ATTN_BWD, s);
     if (e != hipSuccess) return e;
