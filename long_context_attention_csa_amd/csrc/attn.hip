@@ -755,13 +755,27 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
       // Partial result of this split: its own softmax average O / l in bf16
       // (the merge takes a convex combination of the split averages, so
       // their rounding stays within that of the bf16 output) and (m, l).
+      // The head block's 16 rows go through a wave-private piece of the idle
+      // ring (rows padded to 272 bytes against bank conflicts; with two tile
+      // streams, inside this wave's own block of the exchange area), so that
+      // each head's 256-byte row leaves in one store instruction of 16-byte
+      // pieces (4 stores per lane instead of 8 of 8 bytes, whole lines).
       const int64_t pi = (r * H + head) * S + sp;
-      uint16_t* po = reinterpret_cast<uint16_t*>(part_o) + pi * kD;
       const float inv = l > 0.f ? osc[hb] / l : 0.f;
+      constexpr int kXs = 136;   // staged row stride (elements)
+      static_assert((TS > 1 ? HPW * 4096 : 16 * kXs) * NW <= NBUF * kKT * kD, "staging fits the ring");
+      uint16_t* xs = &ring[0][0] + hw * (TS > 1 ? HPW * 4096 : 16 * kXs);
 #pragma unroll
       for (int db = 0; db < kD / 16; ++db)
-        *reinterpret_cast<uint2*>(po + 16 * db + 4 * g) =
+        *reinterpret_cast<uint2*>(xs + col * kXs + 16 * db + 4 * g) =
             make_uint2(cvt_pk_bf16(O[hb][db][0] * inv, O[hb][db][1] * inv), cvt_pk_bf16(O[hb][db][2] * inv, O[hb][db][3] * inv));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // piece lane & 15 of head row 4 j + lane / 16
+        const int hh = 4 * j + (lane >> 4), c = lane & 15;
+        const uint4 v = *reinterpret_cast<const uint4*>(xs + hh * kXs + 8 * c);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(part_o) +
+                                  ((r * H + h0 + 16 * hb + hh) * S + sp) * kD + 8 * c) = v;
+      }
       if (g == 0) {
         part_ml[2 * pi] = m[hb] * kLn2;   // the merge works in natural-log units
         part_ml[2 * pi + 1] = l;
