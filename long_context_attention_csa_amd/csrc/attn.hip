@@ -742,44 +742,38 @@ __global__ __launch_bounds__(NW * TS * 64, (TS == 1 && NW >= 2) ? 2 : 1) void k_
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     const int head = h0 + 16 * hb + col;
+    // The output (one split) or this split's partial result: the softmax
+    // average O / l in bf16, rounded to nearest even (v_cvt_pk_bf16_f32; a
+    // partial is combined convexly by the merge, so its rounding stays within
+    // that of the bf16 output). The head block's 16 rows go through a
+    // wave-private piece of the idle ring (rows padded to 272 bytes against
+    // bank conflicts; with two tile streams, inside this wave's own block of
+    // the exchange area), so that each head's 256-byte row leaves in one
+    // store instruction of 16-byte pieces (4 stores per lane instead of 8 of
+    // 8 bytes, whole lines).
+    const float inv = l > 0.f ? osc[hb] / l : 0.f;
+    constexpr int kXs = 136;   // staged row stride (elements)
+    static_assert((TS > 1 ? HPW * 4096 : 16 * kXs) * NW <= NBUF * kKT * kD, "staging fits the ring");
+    uint16_t* xs = &ring[0][0] + hw * (TS > 1 ? HPW * 4096 : 16 * kXs);
+#pragma unroll
+    for (int db = 0; db < kD / 16; ++db)
+      *reinterpret_cast<uint2*>(xs + col * kXs + 16 * db + 4 * g) =
+          make_uint2(cvt_pk_bf16(O[hb][db][0] * inv, O[hb][db][1] * inv), cvt_pk_bf16(O[hb][db][2] * inv, O[hb][db][3] * inv));
+    uint16_t* dst = S == 1 ? out + (r * H + h0 + 16 * hb) * kD
+                           : reinterpret_cast<uint16_t*>(part_o) + ((r * H + h0 + 16 * hb) * S + sp) * kD;
+    const int64_t hstride = S == 1 ? kD : (int64_t)S * kD;   // elements between the block's head rows
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {   // piece lane & 15 of head row 4 j + lane / 16
+      const int hh = 4 * j + (lane >> 4), c = lane & 15;
+      const uint4 v = *reinterpret_cast<const uint4*>(xs + hh * kXs + 8 * c);
+      *reinterpret_cast<uint4*>(dst + hh * hstride + 8 * c) = v;
+    }
     if (S == 1) {
-      const float inv = l > 0.f ? osc[hb] / l : 0.f;
-      uint16_t* orow = out + (r * H + head) * kD;
-#pragma unroll
-      for (int db = 0; db < kD / 16; ++db)   // round to nearest even (v_cvt_pk_bf16_f32)
-        *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) =
-            make_uint2(cvt_pk_bf16(O[hb][db][0] * inv, O[hb][db][1] * inv),
-                       cvt_pk_bf16(O[hb][db][2] * inv, O[hb][db][3] * inv));
       if (lse && g == 0) lse[r * H + head] = l > 0.f ? (m[hb] + __log2f(l)) * kLn2 : -INFINITY;
-    } else {
-      // Partial result of this split: its own softmax average O / l in bf16
-      // (the merge takes a convex combination of the split averages, so
-      // their rounding stays within that of the bf16 output) and (m, l).
-      // The head block's 16 rows go through a wave-private piece of the idle
-      // ring (rows padded to 272 bytes against bank conflicts; with two tile
-      // streams, inside this wave's own block of the exchange area), so that
-      // each head's 256-byte row leaves in one store instruction of 16-byte
-      // pieces (4 stores per lane instead of 8 of 8 bytes, whole lines).
+    } else if (g == 0) {
       const int64_t pi = (r * H + head) * S + sp;
-      const float inv = l > 0.f ? osc[hb] / l : 0.f;
-      constexpr int kXs = 136;   // staged row stride (elements)
-      static_assert((TS > 1 ? HPW * 4096 : 16 * kXs) * NW <= NBUF * kKT * kD, "staging fits the ring");
-      uint16_t* xs = &ring[0][0] + hw * (TS > 1 ? HPW * 4096 : 16 * kXs);
-#pragma unroll
-      for (int db = 0; db < kD / 16; ++db)
-        *reinterpret_cast<uint2*>(xs + col * kXs + 16 * db + 4 * g) =
-            make_uint2(cvt_pk_bf16(O[hb][db][0] * inv, O[hb][db][1] * inv), cvt_pk_bf16(O[hb][db][2] * inv, O[hb][db][3] * inv));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {   // piece lane & 15 of head row 4 j + lane / 16
-        const int hh = 4 * j + (lane >> 4), c = lane & 15;
-        const uint4 v = *reinterpret_cast<const uint4*>(xs + hh * kXs + 8 * c);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(part_o) +
-                                  ((r * H + h0 + 16 * hb + hh) * S + sp) * kD + 8 * c) = v;
-      }
-      if (g == 0) {
-        part_ml[2 * pi] = m[hb] * kLn2;   // the merge works in natural-log units
-        part_ml[2 * pi + 1] = l;
-      }
+      part_ml[2 * pi] = m[hb] * kLn2;   // the merge works in natural-log units
+      part_ml[2 * pi + 1] = l;
     }
   }
 }
