@@ -825,7 +825,7 @@ __global__ __launch_bounds__(256) void k_index_score_pf(
       sc = ScoreT<SC>::round(sc);
       const int64_t e0 = e_begin + (int64_t)kPfStage * st;
       prev_s = sc;
-      prev_g = max_row16(e0 + lane < nvw ? sc : -INFINITY);
+      if (gbase) prev_g = max_row16(e0 + lane < nvw ? sc : -INFINITY);   // uniform: only a selection that reads them
       prev_e = e0;
     }
   }
@@ -2143,9 +2143,11 @@ static hipError_t run_indexer(const void* q_idx, const void* q_scale, const floa
   IndexPlan p = make_plan(B, Tq, N, SB, d_I, fmt, k);
   if (scores_only) p.lt = 0;
   const int HB = (H_I + 15) / 16;
-  // group maxima and list composites follow the pass's score rows in the workspace
+  // group maxima and list composites follow the pass's score rows in the
+  // workspace; the group maxima only when the selection reads them (rows
+  // longer than kSmallN entries)
   uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-  float* gb = scores_only ? nullptr : reinterpret_cast<float*>(wsb + score_area(p, N, SB));
+  float* gb = scores_only || N <= kSmallN ? nullptr : reinterpret_cast<float*>(wsb + score_area(p, N, SB));
   unsigned long long* lb =
       scores_only ? nullptr : reinterpret_cast<unsigned long long*>(wsb + score_area(p, N, SB) + group_area(p, N));
   for (int64_t g0 = 0; g0 < p.groups; g0 += p.groups_per_pass) {

@@ -34,6 +34,14 @@ def assert_close(got, want, kind: str, what: str = ""):
     assert err <= mx and rel <= rl2, f"{what}: max-abs {err:.3e} (tol {mx}), rel-L2 {rel:.3e} (tol {rl2})"
 
 
+def visible_scores(s, n_vis) -> np.ndarray:
+    """Score rows [Tq, N] as float64 with the entries past each row's visible
+    count (which the kernels never write) replaced by -inf."""
+    s = np.asarray(s)
+    vis = np.arange(s.shape[-1])[None, :] < np.asarray(n_vis)[:, None]
+    return np.where(vis, s, -np.inf).astype(np.float64)
+
+
 def recall(got_idx: np.ndarray, want_idx: np.ndarray) -> np.ndarray:
     """Per-row |got & want| / |want| over the non-padding entries."""
     out = []

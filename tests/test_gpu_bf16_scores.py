@@ -18,7 +18,7 @@ import torch
 import csa_synth as syn
 import long_context_attention_csa_amd as C
 from oracle import csa_oracle as O
-from tests.gpu_common import dev, host, recall
+from tests.gpu_common import dev, host, recall, visible_scores
 from tests.test_gpu_parity import _grid_operands
 
 pytestmark = pytest.mark.gpu
@@ -109,7 +109,7 @@ def _normal_checks(idx, sc, q_i, w, k_i, q_pos, k):
     for b in range(B):
         n_vis = O.visible_entries(q_pos[b], 4, N)
         # selection on the kernel's own bfloat16 scores is bit-exact
-        assert np.array_equal(got_idx[b], O.topk_select(got_s[b].astype(np.float64), n_vis, k))
+        assert np.array_equal(got_idx[b], O.topk_select(visible_scores(got_s[b], n_vis), n_vis, k))
         for t in range(Tq):
             n = int(n_vis[t])
             g, r = got_s[b, t, :n].astype(np.float64), rounded[b, t, :n]

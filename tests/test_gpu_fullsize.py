@@ -25,7 +25,7 @@ import torch
 import csa_synth as syn
 import long_context_attention_csa_amd as C
 from oracle import csa_oracle as O
-from tests.gpu_common import DEV, assert_close, host, recall
+from tests.gpu_common import DEV, assert_close, host, recall, visible_scores
 
 pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
@@ -45,7 +45,7 @@ def _check_selection_and_scores(fmt, qi, qs, w, kc, ks, q_pos_row, ratio, k, got
     oracle scores on the same quantised operands, recall vs the oracle."""
     N = kc.shape[0]
     n_vis = O.visible_entries([q_pos_row], ratio, N)
-    sel = O.topk_select(got_scores_row[None].astype(np.float64), n_vis, k)[0]
+    sel = O.topk_select(visible_scores(got_scores_row[None], n_vis), n_vis, k)[0]
     assert np.array_equal(sel, got_idx_row), f"{what}: selection differs from the oracle's over the GPU scores"
     qd = _deq(fmt, qi, qs)[None]                                # [1, H_I, d_I]
     kd = _deq(fmt, kc, ks)                                      # [N, d_I]

@@ -7,7 +7,7 @@ import torch
 import csa_synth as syn
 import long_context_attention_csa_amd as C
 from oracle import csa_oracle as O
-from tests.gpu_common import (assert_close, certified_index_mismatches, dev, host, recall)
+from tests.gpu_common import (assert_close, certified_index_mismatches, dev, host, recall, visible_scores)
 
 pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
@@ -194,7 +194,7 @@ def test_indexer_normal_group_path_large_n():
     scores, want = _oracle_topk(d["q_i"][:, None], d["w"][:, None], d["k_i"], q_pos, 4, k)
     for b in range(B):
         n_vis = O.visible_entries(q_pos[b], 4, N)
-        assert np.array_equal(got_idx[b], O.topk_select(got_s[b].astype(np.float64), n_vis, k))
+        assert np.array_equal(got_idx[b], O.topk_select(visible_scores(got_s[b], n_vis), n_vis, k))
         assert certified_index_mismatches(got_idx[b], want[b], scores[b], n_vis, k) <= 1
 
 
@@ -283,7 +283,7 @@ def test_indexer_normal_f32_scores_and_selection():
             n = n_vis[t]
             np.testing.assert_allclose(got_s[b, t, :n], scores[b, t, :n], rtol=2e-5, atol=1e-3)
         # selection on the GPU's own scores is bit-exact
-        assert np.array_equal(got_idx[b], O.topk_select(got_s[b].astype(np.float64), n_vis, k))
+        assert np.array_equal(got_idx[b], O.topk_select(visible_scores(got_s[b], n_vis), n_vis, k))
         nbad = certified_index_mismatches(got_idx[b], want[b], scores[b], n_vis, k)
         assert nbad <= 1
 

@@ -14,7 +14,7 @@ import torch
 import csa_synth as syn
 import long_context_attention_csa_amd as C
 from oracle import csa_oracle as O
-from tests.gpu_common import certified_index_mismatches, dev, host
+from tests.gpu_common import certified_index_mismatches, dev, host, visible_scores
 
 pytestmark = pytest.mark.gpu
 
@@ -134,7 +134,7 @@ def test_lists_normal_operands(fmt):
     deq = O.dequant_fp8_rows if fmt == "fp8" else O.dequant_mxfp4_rows
     for b in range(B):
         n_vis = O.visible_entries(q_pos[b], 4, N)
-        assert np.array_equal(got[b], O.topk_select(got_s[b].astype(np.float64), n_vis, k))
+        assert np.array_equal(got[b], O.topk_select(visible_scores(got_s[b], n_vis), n_vis, k))
         qd = deq(host(qc)[b], host(qs)[b])
         kd = deq(host(kc)[b], host(ks)[b])
         scores = O.indexer_scores(qd, d["w"][b][None], kd, q_pos[b], 4)
