@@ -13,8 +13,10 @@
 //   gather  64 key rows (selected entries via idx, or entries 0..n(p)-1, then
 //           window rows) into LDS, row-major for S and transposed for O,
 //   S^T = K Q^T      MFMA, A = key rows (16 per tile), B = Q^T in registers,
-//   online softmax   per head = per lane column; the sink enters as the
-//                    initial running max/denominator (logit sink_h, value 0),
+//   online softmax   per head = per lane column; the sink is one more logit
+//                    (sink_h, value 0): the float32 kernel starts its running
+//                    max and denominator from it, the bf16 kernel adds it
+//                    after its last tile,
 //   O^T += V^T P^T   MFMA, P^T straight from the S^T accumulators: the 8
 //                    K-slots of a lane are the 2x4 keys it already holds, and
 //                    V^T is read from LDS with the same key permutation.
