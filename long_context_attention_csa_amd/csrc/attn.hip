@@ -861,16 +861,34 @@ static AttnShape pick_shape(int H) {
 // timing), so the workspace query and the launch agree and the merge order is
 // fixed. About one block per compute unit, >= kMinSplitKeys keys per split.
 constexpr int64_t kMinSplitKeys = 128;
-struct AttnPlan { int S; };
-static AttnPlan plan_attention(int64_t rows, int H, int64_t nk_max) {
-  const AttnShape sh = pick_shape(H);
+static int split_count(int64_t rows, int H, AttnShape sh, int64_t nk_max) {
   const int64_t base = rows * (H / (16 * sh.nw * sh.hpw));
-  if (base >= 256) return {1};
+  if (base >= 256) return 1;
   const int64_t fill = cdiv(256, base);
   const int64_t by_keys = nk_max / kMinSplitKeys > 1 ? nk_max / kMinSplitKeys : 1;
   int64_t s = fill < by_keys ? fill : by_keys;
   if (s > 128) s = 128;
-  return {(int)(s < 1 ? 1 : s)};
+  return (int)(s < 1 ? 1 : s);
+}
+
+// Short splits (at most kShortSplitKeys keys, five 64-key tiles: a decode
+// grid split across the keys): one head block per wave instead of two when
+// that doubles the blocks per row, which halves the splits. A block's fixed
+// costs (query load, output staging, partial writes) then weigh on half as
+// many heads and the merge reads half the partials; long splits keep two
+// head blocks per wave, whose shared key fragments save more than the extra
+// blocks gain (measured on 128 heads: sparse decode over 1,152 keys per row
+// is faster at 8 to 64 rows, dense decode over 8,320 keys only at 8).
+constexpr int64_t kShortSplitKeys = 320;
+struct AttnPlan { int S; AttnShape sh; };
+static AttnPlan plan_attention(int64_t rows, int H, int64_t nk_max) {
+  AttnShape sh = pick_shape(H);
+  int S = split_count(rows, H, sh, nk_max);
+  if (S > 1 && sh.hpw == 2 && sh.nw == 4 && nk_max <= kShortSplitKeys * S) {
+    sh.hpw = 1;
+    S = split_count(rows, H, sh, nk_max);
+  }
+  return {S, sh};
 }
 
 // Batch-invariant planning (a per-call option): the split count and the
@@ -978,9 +996,9 @@ hipError_t launch_attention(bool sparse, csa_dtype t, const void* q, const void*
                             hipStream_t st) {
   const int64_t rows = B * Tq;
   if (rows == 0) return hipSuccess;
-  const AttnShape sh = pick_shape(H);
   const int64_t prow = plan_rows(B, Tq, batch_inv);
   const AttnPlan pl = plan_attention(prow, H, nk_max);
+  const AttnShape sh = pl.sh;
   const int S = pl.S;
   // two tile streams when the planned grid is small (few rows: decode)
   const bool two_streams = prow * (H / (16 * sh.nw * sh.hpw)) * S <= 1024;
