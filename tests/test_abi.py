@@ -202,6 +202,32 @@ def test_batch_invariant_flag_workspace():
     assert ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128) == default8
 
 
+
+def test_attention_split_plan():
+    """Host logic of the attention split plan, read back from the workspace
+    query (rows x heads x splits x (128 + 2) float32 values): about 256 blocks,
+    >= 128 keys per split, and at 128 heads, when that leaves at most 320
+    keys per split, one 16-head block per wave (two blocks per row), which
+    halves the splits; long splits, other head counts and unsplit grids keep
+    their plans."""
+    from long_context_attention_csa_amd import ops
+
+    def splits(ws, rows, H):
+        assert ws % (rows * H * 130 * 4) == 0
+        return ws // (rows * H * 130 * 4)
+    # dense decode, 8,192 entries + 128 window rows
+    assert splits(ops.dense_attn_workspace_size(8, 1, 8192, 128, 128, 128), 8, 128) == 16   # short: 32 -> 16
+    assert splits(ops.dense_attn_workspace_size(32, 1, 8192, 128, 128, 128), 32, 128) == 8  # 1,040 keys: kept
+    assert splits(ops.dense_attn_workspace_size(2, 1, 60000, 128, 128, 128), 2, 128) == 128  # ~470 keys: kept
+    assert splits(ops.dense_attn_workspace_size(8, 1, 8192, 64, 128, 128), 8, 64) == 32    # 64 heads: unchanged
+    # sparse decode, 1,024 selected + 128 window rows
+    assert splits(ops.sparse_attn_workspace_size(8, 1, 128, 128, 1024, 128), 8, 128) == 9   # short, key-bound
+    assert splits(ops.sparse_attn_workspace_size(64, 1, 128, 128, 1024, 128), 64, 128) == 2  # short: 4 -> 2
+    assert splits(ops.sparse_attn_workspace_size(128, 1, 128, 128, 1024, 128), 128, 128) == 2  # 576 keys: kept
+    # enough rows for one split: no workspace
+    assert ops.sparse_attn_workspace_size(1, 300, 128, 128, 1024, 128) == 0
+
+
 def test_backward_workspace_passes():
     """The backward's workspace holds at most 4 GiB of per-(query, key)
     gradient rows: it grows with the query rows until that budget, then the

@@ -31,7 +31,11 @@ def _case(seed, B, Tq, N, H, T_win):
 
 @pytest.mark.parametrize("B,Tq,H,N,use_sink,window", [
     (8, 1, 128, 8192, True, 128), (2, 1, 64, 3001, True, 128), (3, 2, 48, 900, False, 5),
-    (1, 1, 16, 5000, True, 0), (5, 1, 128, 40, True, 128)])
+    (1, 1, 16, 5000, True, 0), (5, 1, 128, 40, True, 128),
+    # 128 heads split across the keys: 8,320 keys in splits of at most five
+    # tiles (one head block per wave) above; 60,128 in 128 splits of ~470
+    # keys here (two head blocks per wave)
+    (2, 1, 128, 60000, True, 128)])
 def test_dense_decode(B, Tq, H, N, use_sink, window):
     ratio = 128
     L = ratio * N + 77

@@ -1,6 +1,7 @@
 """Attention at head counts whose 16-head blocks do not split evenly into the
-kernels' usual block shapes — 48 (3 blocks), 80 (5), 144 (9) — and at the
-largest supported count, 256 (16), for sparse and dense attention, bf16 and
+kernels' usual block shapes — 48 (3 blocks), 80 (5), 144 (9) — at 128 (8:
+at decode, whose key splits here are short, one head block per wave) and at
+the largest supported count, 256 (16), for sparse and dense attention, bf16 and
 float32, with many query rows (one split per row) and at decode (one query
 row per sequence, the keys split across blocks and merged). Outputs and
 log-sum-exps against the oracle."""
@@ -37,7 +38,7 @@ def _check(kind, got, got_l, want, want_l, what):
 
 
 @pytest.mark.parametrize("mode", ["prefill", "decode"])
-@pytest.mark.parametrize("H", [48, 80, 144, 256])
+@pytest.mark.parametrize("H", [48, 80, 128, 144, 256])
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 def test_sparse_head_counts(kind, H, mode):
     B, Tq = _shape(mode)
@@ -62,7 +63,7 @@ def test_sparse_head_counts(kind, H, mode):
 
 
 @pytest.mark.parametrize("mode", ["prefill", "decode"])
-@pytest.mark.parametrize("H", [48, 80, 144, 256])
+@pytest.mark.parametrize("H", [48, 80, 128, 144, 256])
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 def test_dense_head_counts(kind, H, mode):
     B, Tq = _shape(mode)
